@@ -1,0 +1,57 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case copies the oracle's C source, plants one mistake (a wrong tie rule,
+an off-by-one exponent, a reversed Kronecker bit order, a transposed operand,
+a lost sign of zero, swapped nibbles, a wrong exponent clamp), builds it into a
+temporary library on the CPU and checks that at least one of the pins in
+test_oracle_pins.py fails against it. The shipped oracle is untouched.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import tests.test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "kq_oracle.c")
+
+MUTANTS = {
+    "tie_to_odd": ("(dd == bestd && (i % 2) == 0)", "(dd == bestd && (i % 2) == 1)",
+                   [pins.test_tie_table_from_golden]),
+    "exponent_off_by_one": ("int e = (ex - 1) - 2;", "int e = (ex - 1) - 1;",
+                            [pins.test_every_level_every_exponent_round_trips]),
+    "clamp_at_minus_126": ("if (e < -127) e = -127;", "if (e < -126) e = -126;",
+                           [pins.test_every_bf16_alone_in_a_block]),
+    "kron_bit_order_reversed": ("int bit = 5 - k;", "int bit = k - 1;",
+                                [pins.test_bit_order_g1_is_stride_16]),
+    "fold_not_transposed": ("(double)w[r] * Ki[col * 32 + r]", "(double)w[r] * Ki[r * 32 + col]",
+                            [lambda o: pins.test_invariance_eq1(o, "lu")]),
+    "transform_transposed": ("a[r] * K[r * 32 + col]", "a[r] * K[col * 32 + r]",
+                             [lambda o: pins.test_invariance_eq1(o, "lu")]),
+    "sign_of_zero_lost": ("if (signbit(y[i])) code |= 8;", "if (y[i] < 0) code |= 8;",
+                          [pins.test_zero_block_and_signed_zero]),
+    "nibbles_swapped": ("(uint8_t)(code << ((i % 2) * 4))", "(uint8_t)(code << ((1 - i % 2) * 4))",
+                        [pins.test_worked_examples_golden]),
+    "inverse_sign_slip": ("Gi[k][0][1] = -G[k][0][1] / det;", "Gi[k][0][1] = G[k][0][1] / det;",
+                          [pins.test_inverse_is_kron_of_inverses]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new, checks = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site not found: " + old
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", *oracle.CFLAGS, str(mpath), "-o", str(so), "-lm"])
+    mutant = oracle.Oracle(oracle.load(str(so)))
+    caught = False
+    for check in checks:
+        try:
+            check(mutant)
+        except AssertionError:
+            caught = True
+    assert caught, "pins did not notice the planted mistake " + name
