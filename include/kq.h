@@ -1,0 +1,142 @@
+/*
+ * kq.h -- C ABI of the KroQuant online activation quantizer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method (KroQuant, arXiv 2607.21446v1):
+ *   - Sec. 1, Eq. 1: an invertible transform T is applied to the activations
+ *     (A -> A T) and its inverse to the weights (W -> W T^{-T}); the product
+ *     A W^T is unchanged.
+ *   - Sec. 3.1, Eq. 4: T is block diagonal, one 32x32 block K^(j) per group of
+ *     32 consecutive channels.
+ *   - Sec. 3.2, Eq. 5: each block is a Kronecker product of five 2x2 factors,
+ *     K = G1 (x) G2 (x) G3 (x) G4 (x) G5; Sec. 3.5.1, Eq. 12: entry-wise,
+ *     K[r][c] = prod_{k=1..5} G_k[bit_{5-k}(r)][bit_{5-k}(c)], so G1 mixes
+ *     channels 16 apart and G5 neighbouring channels.
+ *   - Sec. 3.1 and Sec. 4.1 "Data format" / Appendix D: the result is quantized
+ *     block-wise to MXFP4: 32 E2M1 elements sharing one E8M0 scale (OCP MX).
+ *
+ * Number format (OCP MX v1.0 reading; the paper names the format only):
+ *   shared exponent e = floor(log2(max_i |y_i|)) - 2, clamped to [-127, 127]
+ *   (an all-zero block takes e = -127); scale byte = e + 127 (E8M0). Each
+ *   element v = y / 2^e is rounded to the nearest of {0, 0.5, 1, 1.5, 2, 3, 4, 6}
+ *   with ties to the even code, larger magnitudes saturate to 6. A code is
+ *   sign << 3 | index of that magnitude (0x0 = 0 ... 0x7 = 6); the sign bit
+ *   follows y, also for zeros.
+ *
+ * Layouts (all row-major, no padding in the outputs):
+ *   A        bf16 bit patterns, [m][lda], lda >= d; d % 32 == 0
+ *   codes    uint8 [m][d/2]: element 2k in the low nibble of byte k of its row
+ *   scales   uint8 [m][d/32]: E8M0 byte of block j of row i at [i][j]
+ *   factors  fp32 [d/32][5][2][2]: factors[j][k-1][r][c] = G_k[r][c] of block j,
+ *            so factors[j][0] is G1 (channel bit 4) and factors[j][4] is G5 (bit 0)
+ *
+ * Conventions for every entry point that takes a stream:
+ *   - Pointers named "device" point to GPU memory that the caller allocates,
+ *     owns and keeps alive until the enqueued work has finished. The library
+ *     allocates nothing, keeps no state between calls and never synchronizes.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and runs
+ *     asynchronously; results are valid once the stream has reached it.
+ *   - Arguments are checked on the host before anything is enqueued; on an
+ *     error nothing is launched and the status says why. A launch the HIP
+ *     runtime rejects returns KQ_ERR_HIP; kq_last_hip_error() then gives the
+ *     hipError_t value (per host thread).
+ *   - With m == 0 (or d == 0) nothing is read, written or launched and KQ_OK
+ *     is returned.
+ *   - Inputs must be finite; NaN or Inf inputs give unspecified codes.
+ *   - Outputs must not overlap inputs.
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t *kq_stream_t;
+
+typedef enum {
+    KQ_OK = 0,
+    KQ_ERR_NULL = 1,        /* a required pointer is NULL */
+    KQ_ERR_SHAPE = 2,       /* negative size, d % 32 != 0, lda < d, or size overflow */
+    KQ_ERR_ALIGN = 3,       /* a pointer or leading dimension breaks the stated alignment */
+    KQ_ERR_HIP = 4,         /* the HIP runtime rejected the launch */
+    KQ_ERR_UNSUPPORTED = 5  /* argument combination not supported by this build */
+} kq_status;
+
+/*
+ * Quantize-only (T = I): codes/scales of A itself.
+ * KroQuant Sec. 3.1 blockwise quantizer; Sec. 4.4 / Table 3 "Q4" kernel.
+ *   A       device, bf16 bits [m][lda]; 16-byte aligned, lda % 8 == 0
+ *   codes   device, [m][d/2] bytes, 16-byte aligned
+ *   scales  device, [m][d/32] bytes
+ * Results are bit-exact to the format definition above.
+ */
+kq_status kq_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
+                            uint8_t *codes, uint8_t *scales, kq_stream_t stream);
+
+/*
+ * Fused Kronecker transform + quantize: for every row a of A and block j,
+ * y = a[32j : 32j+32] . K^(j) (Eq. 1's A T with Eq. 4-5 and Eq. 12), computed
+ * in fp32, then quantized from fp32 as above (no rounding to bf16 in between).
+ *   factors  device, fp32 [d/32][5][2][2], 16-byte aligned (layout above)
+ *   y_debug  device or NULL; if given, fp32 [m][d] receives y (check mode),
+ *            16-byte aligned. Codes and scales do not depend on it.
+ * Other arguments as kq_quantize_mxfp4.
+ */
+kq_status kq_transform_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
+                                      const float *factors, uint8_t *codes, uint8_t *scales,
+                                      float *y_debug, kq_stream_t stream);
+
+/*
+ * SmoothQuant baseline (KroQuant Appendix D.2; Sec. 4.4 "Scale" kernel):
+ * T = diag(1 / gamma), i.e. y_c = fl32(a_c * inv_scale[c]) (one fp32 multiply),
+ * then quantize as above.
+ *   inv_scale  device, fp32 [d] = 1 / gamma_c, 16-byte aligned
+ * Other arguments as kq_quantize_mxfp4. Bit-exact.
+ */
+kq_status kq_smoothquant_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
+                                        const float *inv_scale, uint8_t *codes, uint8_t *scales,
+                                        kq_stream_t stream);
+
+/*
+ * Quantize-only on fp32 input (for folded weights before the W4A4 GEMM).
+ *   X  device, fp32 [m][ldx], 16-byte aligned, ldx >= d, ldx % 4 == 0
+ * Other arguments as kq_quantize_mxfp4. Bit-exact.
+ */
+kq_status kq_quantize_mxfp4_f32(const float *X, int64_t m, int64_t d, int64_t ldx,
+                                uint8_t *codes, uint8_t *scales, kq_stream_t stream);
+
+/*
+ * Weight fold W' = W T^{-T} (Eq. 1; Sec. 3.2: the inverse of a Kronecker
+ * product is the Kronecker product of the 2x2 inverses). Per block,
+ * w' = w . (K^(j))^{-T}, applied as five 2x2 stages with (G_k^{-1})^T in fp32.
+ *   W         device, fp32 [o][d], 16-byte aligned
+ *   factors   as kq_transform_quantize_mxfp4; every G_k must be invertible
+ *   W_folded  device, fp32 [o][d], 16-byte aligned
+ */
+kq_status kq_inverse_fold_weights(const float *W, int64_t o, int64_t d, const float *factors,
+                                  float *W_folded, kq_stream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *kq_status_string(kq_status s);
+
+/* hipError_t of the last KQ_ERR_HIP returned on the calling host thread (0 if none). */
+int kq_last_hip_error(void);
+
+/*
+ * Host-only: 2x2 factor entries from the paper's 15 parameters per block
+ * (Sec. 3.2, Eq. 6): G = [[1,0],[c,1]] . [[a,b],[0,-1/a]] = [[a, b],[c a, c b - 1/a]].
+ *   abc      host, fp64 [nblk][5][3] = (a, b, c) per factor; a != 0
+ *   factors  host, fp32 [nblk][5][2][2] (the layout above)
+ * Returns KQ_ERR_NULL for NULL pointers, KQ_ERR_SHAPE for nblk < 0 or a == 0.
+ */
+kq_status kq_factors_from_lu(const double *abc, int64_t nblk, float *factors);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KQ_H */

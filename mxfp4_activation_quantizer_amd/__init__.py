@@ -1,0 +1,213 @@
+"""Python binding of libkq.so, the KroQuant MXFP4 activation quantizer for MI355X.
+
+Argument marshalling only: every computation runs in the HIP kernels of
+libkq.so (include/kq.h documents the C ABI). PyTorch provides device memory
+and streams. There is no CPU fallback: if the library is missing or the
+device is not a GPU, the calls raise.
+
+Method: KroQuant (arXiv 2607.21446v1), Sec. 3.1-3.2 and 3.5 (Eq. 1, 4, 5, 12),
+with the MXFP4 format of Sec. 4.1 / Appendix D.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkq.so")
+
+KQ_OK, KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_HIP, KQ_ERR_UNSUPPORTED = range(6)
+
+# Every symbol include/kq.h declares.
+EXPORTS = (
+    "kq_quantize_mxfp4",
+    "kq_transform_quantize_mxfp4",
+    "kq_smoothquant_quantize_mxfp4",
+    "kq_quantize_mxfp4_f32",
+    "kq_inverse_fold_weights",
+    "kq_status_string",
+    "kq_last_hip_error",
+    "kq_factors_from_lu",
+)
+
+_lib = None
+
+
+class KQError(RuntimeError):
+    def __init__(self, fn, status, lib):
+        msg = lib.kq_status_string(status).decode()
+        if status == KQ_ERR_HIP:
+            msg += " (hipError_t %d)" % lib.kq_last_hip_error()
+        super().__init__("%s: %s" % (fn, msg))
+        self.status = status
+
+
+def lib():
+    """Load libkq.so (built by ``__graft_entry__.build()`` or ``python -m ...build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libkq.so is not built: run `python -m mxfp4_activation_quantizer_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        for name, args in {
+            "kq_quantize_mxfp4": [p, i64, i64, i64, p, p, p],
+            "kq_transform_quantize_mxfp4": [p, i64, i64, i64, p, p, p, p, p],
+            "kq_smoothquant_quantize_mxfp4": [p, i64, i64, i64, p, p, p, p],
+            "kq_quantize_mxfp4_f32": [p, i64, i64, i64, p, p, p],
+            "kq_inverse_fold_weights": [p, i64, i64, p, p, p],
+            "kq_factors_from_lu": [p, i64, p],
+        }.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = st
+        L.kq_status_string.argtypes = [st]
+        L.kq_status_string.restype = ctypes.c_char_p
+        L.kq_last_hip_error.argtypes = []
+        L.kq_last_hip_error.restype = st
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != KQ_OK:
+        raise KQError(fn, status, lib())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name, dtypes):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    return t
+
+
+def _rows(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("%s must be 2-D with unit column stride" % name)
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _outputs(m, d, device, codes, scales):
+    torch = _torch()
+    if codes is None:
+        codes = torch.empty((m, d // 2), dtype=torch.uint8, device=device)
+    if scales is None:
+        scales = torch.empty((m, d // 32), dtype=torch.uint8, device=device)
+    _dev(codes, "codes", (torch.uint8,))
+    _dev(scales, "scales", (torch.uint8,))
+    if tuple(codes.shape) != (m, d // 2) or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous [m][d/2] uint8 tensor")
+    if tuple(scales.shape) != (m, d // 32) or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous [m][d/32] uint8 tensor")
+    return codes, scales
+
+
+def _bf16_input(A):
+    torch = _torch()
+    _dev(A, "A", (torch.bfloat16, torch.int16, torch.uint16))
+    return _rows(A, "A")
+
+
+def quantize_mxfp4(A, codes=None, scales=None, stream=None):
+    """MXFP4 codes [m][d/2] and E8M0 scales [m][d/32] of bf16 A [m][d] (T = I)."""
+    m, d, lda = _bf16_input(A)
+    codes, scales = _outputs(m, d, A.device, codes, scales)
+    _check("kq_quantize_mxfp4",
+           lib().kq_quantize_mxfp4(_p(A), m, d, lda, _p(codes), _p(scales), _stream_ptr(stream)))
+    return codes, scales
+
+
+def transform_quantize_mxfp4(A, factors, codes=None, scales=None, y_debug=None, stream=None):
+    """Fused y = A T (per-block Kronecker factors fp32 [d/32][5][2][2]) then MXFP4.
+
+    ``y_debug``: optional fp32 [m][d] tensor that receives y (check mode).
+    """
+    torch = _torch()
+    m, d, lda = _bf16_input(A)
+    _dev(factors, "factors", (torch.float32,))
+    if factors.numel() != (d // 32) * 20 or not factors.is_contiguous():
+        raise ValueError("factors must be contiguous fp32 [d/32][5][2][2]")
+    if y_debug is not None:
+        _dev(y_debug, "y_debug", (torch.float32,))
+        if tuple(y_debug.shape) != (m, d) or not y_debug.is_contiguous():
+            raise ValueError("y_debug must be a contiguous fp32 [m][d] tensor")
+    codes, scales = _outputs(m, d, A.device, codes, scales)
+    _check("kq_transform_quantize_mxfp4",
+           lib().kq_transform_quantize_mxfp4(_p(A), m, d, lda, _p(factors), _p(codes), _p(scales),
+                                             _p(y_debug), _stream_ptr(stream)))
+    return codes, scales
+
+
+def smoothquant_quantize_mxfp4(A, inv_scale, codes=None, scales=None, stream=None):
+    """SmoothQuant baseline: y_c = fl32(a_c * inv_scale[c]) then MXFP4."""
+    torch = _torch()
+    m, d, lda = _bf16_input(A)
+    _dev(inv_scale, "inv_scale", (torch.float32,))
+    if inv_scale.numel() < d or not inv_scale.is_contiguous():
+        raise ValueError("inv_scale must be a contiguous fp32 vector of length d")
+    codes, scales = _outputs(m, d, A.device, codes, scales)
+    _check("kq_smoothquant_quantize_mxfp4",
+           lib().kq_smoothquant_quantize_mxfp4(_p(A), m, d, lda, _p(inv_scale), _p(codes),
+                                               _p(scales), _stream_ptr(stream)))
+    return codes, scales
+
+
+def quantize_mxfp4_f32(X, codes=None, scales=None, stream=None):
+    """MXFP4 codes and scales of fp32 X [m][d]."""
+    torch = _torch()
+    _dev(X, "X", (torch.float32,))
+    m, d, ldx = _rows(X, "X")
+    codes, scales = _outputs(m, d, X.device, codes, scales)
+    _check("kq_quantize_mxfp4_f32",
+           lib().kq_quantize_mxfp4_f32(_p(X), m, d, ldx, _p(codes), _p(scales), _stream_ptr(stream)))
+    return codes, scales
+
+
+def inverse_fold_weights(W, factors, out=None, stream=None):
+    """W' = W T^{-T} for fp32 W [o][d] (the weight side of Eq. 1)."""
+    torch = _torch()
+    _dev(W, "W", (torch.float32,))
+    _dev(factors, "factors", (torch.float32,))
+    if not W.is_contiguous():
+        raise ValueError("W must be contiguous")
+    o, d = W.shape
+    if factors.numel() != (d // 32) * 20 or not factors.is_contiguous():
+        raise ValueError("factors must be contiguous fp32 [d/32][5][2][2]")
+    if out is None:
+        out = torch.empty_like(W)
+    _dev(out, "out", (torch.float32,))
+    if out.shape != W.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor shaped like W")
+    _check("kq_inverse_fold_weights",
+           lib().kq_inverse_fold_weights(_p(W), o, d, _p(factors), _p(out), _stream_ptr(stream)))
+    return out
+
+
+def factors_from_lu(abc):
+    """Host helper: (a, b, c) per factor, fp64 [nblk][5][3] -> fp32 [nblk][5][2][2] (Eq. 6)."""
+    abc = np.ascontiguousarray(abc, dtype=np.float64)
+    nblk = abc.shape[0]
+    out = np.empty((nblk, 5, 2, 2), dtype=np.float32)
+    _check("kq_factors_from_lu",
+           lib().kq_factors_from_lu(ctypes.c_void_p(abc.ctypes.data), nblk,
+                                    ctypes.c_void_p(out.ctypes.data)))
+    return out

@@ -1,0 +1,84 @@
+"""The C ABI library on the CPU: it loads, exports what include/kq.h declares,
+and rejects bad arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mxfp4_activation_quantizer_amd as kq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "kq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return kq.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    syms = declared_symbols()
+    assert len(syms) >= 8
+    for s in syms:
+        assert hasattr(L, s), s
+    assert sorted(kq.EXPORTS) == syms
+
+
+P = ctypes.c_void_p
+GOOD = P(0x10000)  # never dereferenced: every case below fails before a launch
+
+
+@pytest.mark.parametrize("fn,args,status", [
+    ("kq_quantize_mxfp4", (GOOD, 4, 33, 33, GOOD, GOOD, None), kq.KQ_ERR_SHAPE),
+    ("kq_quantize_mxfp4", (GOOD, 4, 64, 32, GOOD, GOOD, None), kq.KQ_ERR_SHAPE),
+    ("kq_quantize_mxfp4", (GOOD, -1, 64, 64, GOOD, GOOD, None), kq.KQ_ERR_SHAPE),
+    ("kq_quantize_mxfp4", (None, 4, 64, 64, GOOD, GOOD, None), kq.KQ_ERR_NULL),
+    ("kq_quantize_mxfp4", (GOOD, 4, 64, 64, None, GOOD, None), kq.KQ_ERR_NULL),
+    ("kq_quantize_mxfp4", (GOOD, 4, 64, 64, GOOD, None, None), kq.KQ_ERR_NULL),
+    ("kq_quantize_mxfp4", (P(0x10002), 4, 64, 64, GOOD, GOOD, None), kq.KQ_ERR_ALIGN),
+    ("kq_quantize_mxfp4", (GOOD, 4, 64, 68, GOOD, GOOD, None), kq.KQ_ERR_ALIGN),
+    ("kq_quantize_mxfp4", (GOOD, 4, 64, 64, P(0x10004), GOOD, None), kq.KQ_ERR_ALIGN),
+    ("kq_quantize_mxfp4", (None, 0, 64, 64, None, None, None), kq.KQ_OK),
+    ("kq_quantize_mxfp4", (None, 5, 0, 0, None, None, None), kq.KQ_OK),
+    ("kq_transform_quantize_mxfp4", (GOOD, 4, 64, 64, None, GOOD, GOOD, None, None), kq.KQ_ERR_NULL),
+    ("kq_transform_quantize_mxfp4", (GOOD, 4, 64, 64, P(0x10008), GOOD, GOOD, None, None), kq.KQ_ERR_ALIGN),
+    ("kq_transform_quantize_mxfp4", (GOOD, 4, 64, 64, GOOD, GOOD, GOOD, P(0x10004), None), kq.KQ_ERR_ALIGN),
+    ("kq_transform_quantize_mxfp4", (GOOD, 4, 48, 64, GOOD, GOOD, GOOD, None, None), kq.KQ_ERR_SHAPE),
+    ("kq_smoothquant_quantize_mxfp4", (GOOD, 4, 64, 64, None, GOOD, GOOD, None), kq.KQ_ERR_NULL),
+    ("kq_smoothquant_quantize_mxfp4", (GOOD, 4, 64, 64, P(0x10004), GOOD, GOOD, None), kq.KQ_ERR_ALIGN),
+    ("kq_quantize_mxfp4_f32", (GOOD, 4, 64, 66, GOOD, GOOD, None), kq.KQ_ERR_ALIGN),
+    ("kq_quantize_mxfp4_f32", (GOOD, 4, 64, 32, GOOD, GOOD, None), kq.KQ_ERR_SHAPE),
+    ("kq_quantize_mxfp4_f32", (None, 4, 64, 64, GOOD, GOOD, None), kq.KQ_ERR_NULL),
+    ("kq_inverse_fold_weights", (GOOD, 4, 40, GOOD, GOOD, None), kq.KQ_ERR_SHAPE),
+    ("kq_inverse_fold_weights", (GOOD, 4, 64, None, GOOD, None), kq.KQ_ERR_NULL),
+    ("kq_inverse_fold_weights", (GOOD, 4, 64, GOOD, P(0x10004), None), kq.KQ_ERR_ALIGN),
+    ("kq_inverse_fold_weights", (None, 0, 64, None, None, None), kq.KQ_OK),
+])
+def test_host_argument_checks(L, fn, args, status):
+    assert getattr(L, fn)(*args) == status
+
+
+def test_status_strings(L):
+    for s in range(6):
+        assert L.kq_status_string(s).startswith(b"KQ_")
+    assert L.kq_last_hip_error() == 0
+
+
+def test_factors_from_lu_matches_eq6(orc):
+    rng = np.random.default_rng(2)
+    abc = rng.standard_normal((9, 5, 3))
+    abc[..., 0] = np.where(np.abs(abc[..., 0]) < 0.1, 0.5, abc[..., 0])
+    got = kq.factors_from_lu(abc)
+    want = orc.factors_from_lu(abc).astype(np.float32)
+    assert np.array_equal(got, want)
+    bad = abc.copy()
+    bad[3, 2, 0] = 0.0
+    with pytest.raises(kq.KQError):
+        kq.factors_from_lu(bad)

@@ -1,0 +1,305 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Inputs come from the seeded generator (synth); the oracle never sees anything
+the GPU produced except where the rule says so (rule 2 of tests/parity.py
+quantizes the GPU's own fp32 y with the oracle). Full-size workloads run in
+the launch configuration the bench uses; the largest one is checked on
+sampled rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["tiny_64x256", "pixart_attn_4096x1152", "pixart_ffn_8192x4608", "flux_18432x3072"]
+SAMPLED = ["flux_18432x12288"]
+SAMPLE_ROWS = 1536
+
+
+def case(msg):
+    print("[case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch
+
+
+@pytest.fixture(scope="module")
+def kq():
+    import mxfp4_activation_quantizer_amd as kq
+    kq.lib()  # fails loudly when libkq.so is missing
+    return kq
+
+
+_cache = {}
+
+
+def workload(name):
+    if name not in _cache:
+        _cache.clear()  # keep host memory bounded: one full workload at a time
+        _cache[name] = synth.workload(name)
+    return _cache[name]
+
+
+def dev_bf16(torch, A):
+    return torch.from_numpy(A.view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def sample_rows(m, n, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(m, size=min(n, m), replace=False))
+    rows[0], rows[-1] = 0, m - 1  # include the first and the ragged last tile
+    return np.unique(rows)
+
+
+def gather(torch, t, rows):
+    return t.index_select(0, torch.from_numpy(rows).to(t.device)).cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# bit-exact paths
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", FULL + SAMPLED)
+def test_quantize_only_bit_exact(torch_dev, kq, orc, name):
+    torch = torch_dev
+    case("quantize_only " + name)
+    w = workload(name)
+    A = dev_bf16(torch, w.A)
+    codes, scales = kq.quantize_mxfp4(A)
+    torch.cuda.synchronize()
+    rows = np.arange(w.m) if name in FULL else sample_rows(w.m, SAMPLE_ROWS)
+    c_ref, s_ref = orc.quantize_bf16(w.A[rows])
+    assert np.array_equal(gather(torch, scales, rows), s_ref)
+    assert np.array_equal(gather(torch, codes, rows), c_ref)
+
+
+@pytest.mark.parametrize("name", FULL + SAMPLED)
+def test_smoothquant_bit_exact(torch_dev, kq, orc, name):
+    torch = torch_dev
+    case("smoothquant " + name)
+    w = workload(name)
+    A = dev_bf16(torch, w.A)
+    inv = torch.from_numpy(w.inv_scale).cuda()
+    codes, scales = kq.smoothquant_quantize_mxfp4(A, inv)
+    torch.cuda.synchronize()
+    rows = np.arange(w.m) if name in FULL else sample_rows(w.m, SAMPLE_ROWS)
+    c_ref, s_ref = orc.smoothquant_quantize(w.A[rows], w.inv_scale)
+    assert np.array_equal(gather(torch, scales, rows), s_ref)
+    assert np.array_equal(gather(torch, codes, rows), c_ref)
+
+
+# ---------------------------------------------------------------------------
+# fused Kronecker transform + quantize
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", FULL + SAMPLED)
+def test_fused_against_oracle(torch_dev, kq, orc, name):
+    torch = torch_dev
+    case("fused " + name)
+    w = workload(name)
+    A = dev_bf16(torch, w.A)
+    fac = torch.from_numpy(w.factors).cuda()
+    y = torch.empty((w.m, w.d), dtype=torch.float32, device="cuda")
+    codes, scales = kq.transform_quantize_mxfp4(A, fac, y_debug=y)
+    codes_fast, scales_fast = kq.transform_quantize_mxfp4(A, fac)
+    torch.cuda.synchronize()
+    # rule 4: fast mode writes the same bytes as check mode
+    assert torch.equal(codes, codes_fast) and torch.equal(scales, scales_fast)
+    rows = np.arange(w.m) if name in FULL else sample_rows(w.m, SAMPLE_ROWS)
+    rep = parity.fused_report(orc, w.A[rows], w.factors, gather(torch, codes, rows),
+                              gather(torch, scales, rows), gather(torch, y, rows))
+    print("[parity] %s %s" % (name, rep), flush=True)
+
+
+@pytest.mark.parametrize("kind", ["identity", "swap", "signflip", "pow2", "mixed"])
+def test_fused_exact_factors_reduce_to_quantizer(torch_dev, kq, orc, kind):
+    torch = torch_dev
+    case("fused exact factors " + kind)
+    w = workload("pixart_attn_4096x1152")
+    f = synth.special_factors(w.d // 32, kind)
+    A = dev_bf16(torch, w.A)
+    codes, scales = kq.transform_quantize_mxfp4(A, torch.from_numpy(f).cuda())
+    torch.cuda.synchronize()
+    c_ref, s_ref, _ = orc.transform_quantize(w.A, f, want_y=False)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    parity.assert_codes_equal_mod_signed_zero(codes.cpu().numpy(), c_ref, kind)
+    if kind == "identity":
+        q_codes, q_scales = kq.quantize_mxfp4(A)
+        assert torch.equal(q_scales, scales)
+        parity.assert_codes_equal_mod_signed_zero(q_codes.cpu().numpy(), codes.cpu().numpy())
+
+
+def test_fused_hadamard_worked_example(torch_dev, kq, orc):
+    torch = torch_dev
+    case("fused hadamard worked example")
+    A = np.zeros((4, 64), np.uint16)
+    A[:, 3] = synth.to_bf16_bits(np.array([80.0]))[0]
+    A[1, 32 + 7] = synth.to_bf16_bits(np.array([-3.0]))[0]
+    codes, scales = kq.transform_quantize_mxfp4(dev_bf16(torch, A),
+                                                torch.from_numpy(synth.hadamard_factors(2)).cuda())
+    n = parity.unpack(codes.cpu().numpy())
+    assert scales.cpu().numpy()[0, 0] == 128
+    for c in range(32):
+        assert n[0, c] == 7 | (8 if bin(3 & c).count("1") % 2 else 0)
+    c_ref, s_ref, _ = orc.transform_quantize(A, synth.hadamard_factors(2), want_y=False)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    parity.assert_codes_equal_mod_signed_zero(codes.cpu().numpy(), c_ref)
+
+
+# ---------------------------------------------------------------------------
+# exhaustive quantizer checks
+# ---------------------------------------------------------------------------
+
+def all_finite_bf16():
+    bits = np.arange(65536, dtype=np.uint32)
+    return bits[((bits >> 7) & 0xFF) != 0xFF].astype(np.uint16)
+
+
+def test_every_bf16_alone_and_in_context(torch_dev, kq, orc):
+    torch = torch_dev
+    case("exhaustive bf16 quantize")
+    b = all_finite_bf16()
+    n = b.size
+    rng = np.random.default_rng(4)
+    blocks = []
+    # alone in a block (position varies)
+    alone = np.zeros((n, 32), np.uint16)
+    alone[np.arange(n), np.arange(n) % 32] = b
+    blocks.append(alone)
+    # every value beside a block maximum from every binade (scale contexts)
+    ctx = np.zeros((n, 32), np.uint16)
+    ctx[:, :31] = b[rng.integers(0, n, (n, 31))]
+    ctx[:, 31] = b
+    blocks.append(ctx)
+    # 32 consecutive patterns per block
+    m32 = (n // 32) * 32
+    blocks.append(b[:m32].reshape(-1, 32))
+    A = np.concatenate(blocks, axis=0)
+    pad = (-A.shape[0]) % 8
+    A = np.concatenate([A, np.zeros((pad, 32), np.uint16)], axis=0)
+    A = np.ascontiguousarray(A.reshape(-1, 256))
+    codes, scales = kq.quantize_mxfp4(dev_bf16(torch, A))
+    c_ref, s_ref = orc.quantize_bf16(A)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+
+
+def boundary_f32_blocks(rng, nblocks):
+    """fp32 blocks whose elements sit on and next to every E2M1 rounding boundary."""
+    bounds = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 0.5, 1.0, 3.0, 4.0],
+                      dtype=np.float32)
+    X = np.zeros((nblocks, 32), np.float32)
+    e = rng.integers(-126, 125, nblocks)
+    for i in range(nblocks):
+        sc = np.float32(2.0) ** np.float32(e[i]) if e[i] > -126 else np.float32(2.0 ** -126)
+        v = bounds[rng.integers(0, bounds.size, 31)]
+        k = rng.integers(-3, 4, 31)
+        vals = np.array([np.float32(x) for x in v]) * sc
+        for j in range(31):
+            for _ in range(abs(k[j])):
+                vals[j] = np.nextafter(vals[j], np.float32(np.inf if k[j] > 0 else 0))
+        sign = np.where(rng.integers(0, 2, 31) == 1, -1, 1).astype(np.float32)
+        X[i, :31] = vals * sign
+        X[i, 31] = np.float32(rng.choice([4.0, 6.0, 7.5])) * sc
+    return X
+
+
+def test_f32_quantizer_at_rounding_boundaries(torch_dev, kq, orc):
+    torch = torch_dev
+    case("fp32 quantize boundaries")
+    rng = np.random.default_rng(6)
+    X = boundary_f32_blocks(rng, 4096).reshape(512, 256)
+    codes, scales = kq.quantize_mxfp4_f32(torch.from_numpy(X).cuda())
+    c_ref, s_ref = orc.quantize_f32(X)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+
+
+# ---------------------------------------------------------------------------
+# shapes, strides, streams, guard bytes, determinism
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,d,pad", [(1, 32, 0), (3, 96, 8), (37, 160, 0), (4133, 1152, 64),
+                                     (517, 4608, 0), (70, 512, 24), (1, 12288, 0)])
+def test_ragged_shapes_and_padded_rows(torch_dev, kq, orc, m, d, pad):
+    torch = torch_dev
+    case("ragged m=%d d=%d pad=%d" % (m, d, pad))
+    A_full = synth.random_bf16_matrix(m, d + pad, seed=m * 7 + d, scale=3.0)
+    A_full[:, min(5, d - 1)] = synth.to_bf16_bits(np.full(m, 300.0))
+    fac = synth.lu_perturbed_factors(d // 32, seed=d + 1)
+    inv = synth.smoothquant_inv_scale(A_full, d)
+    A = dev_bf16(torch, A_full)[:, :d]
+    assert A.stride(0) == d + pad
+    codes, scales = kq.quantize_mxfp4(A)
+    c_ref, s_ref = orc.quantize_bf16(A_full, d=d)
+    assert np.array_equal(codes.cpu().numpy(), c_ref) and np.array_equal(scales.cpu().numpy(), s_ref)
+    codes, scales = kq.smoothquant_quantize_mxfp4(A, torch.from_numpy(inv).cuda())
+    c_ref, s_ref = orc.smoothquant_quantize(A_full, inv, d=d)
+    assert np.array_equal(codes.cpu().numpy(), c_ref) and np.array_equal(scales.cpu().numpy(), s_ref)
+    y = torch.empty((m, d), dtype=torch.float32, device="cuda")
+    codes, scales = kq.transform_quantize_mxfp4(A, torch.from_numpy(fac).cuda(), y_debug=y)
+    parity.fused_report(orc, np.ascontiguousarray(A_full[:, :d]), fac, codes.cpu().numpy(),
+                        scales.cpu().numpy(), y.cpu().numpy())
+
+
+def test_guard_bytes_determinism_and_side_stream(torch_dev, kq):
+    torch = torch_dev
+    case("guard bytes / determinism / stream")
+    w = workload("pixart_attn_4096x1152")
+    m, d = w.m, w.d
+    A = dev_bf16(torch, w.A)
+    fac = torch.from_numpy(w.factors).cuda()
+    G = 4096
+    cbuf = torch.full((m * d // 2 + G,), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((m * d // 32 + G,), 0x5A, dtype=torch.uint8, device="cuda")
+    codes = cbuf[: m * d // 2].view(m, d // 2)
+    scales = sbuf[: m * d // 32].view(m, d // 32)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        kq.transform_quantize_mxfp4(A, fac, codes=codes, scales=scales, stream=s)
+    s.synchronize()
+    assert bool((cbuf[m * d // 2:] == 0xA5).all()) and bool((sbuf[m * d // 32:] == 0x5A).all())
+    c2, s2 = kq.transform_quantize_mxfp4(A, fac)
+    torch.cuda.synchronize()
+    assert torch.equal(c2, codes) and torch.equal(s2, scales)
+
+
+def test_empty_inputs(torch_dev, kq):
+    torch = torch_dev
+    case("empty inputs")
+    A = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    c, s = kq.quantize_mxfp4(A)
+    assert c.shape == (0, 128) and s.shape == (0, 8)
+    c, s = kq.transform_quantize_mxfp4(A, torch.zeros((8, 5, 2, 2), device="cuda"))
+    assert c.numel() == 0
+
+
+# ---------------------------------------------------------------------------
+# weight fold W T^{-T} and the fp32 quantizer on folded weights
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("o,d,seed", [(64, 256, 21), (3072, 3072, 1003)])
+def test_inverse_fold(torch_dev, kq, orc, o, d, seed):
+    torch = torch_dev
+    case("fold o=%d d=%d" % (o, d))
+    W = synth.weights(o, d, 1004)
+    fac = synth.lu_perturbed_factors(d // 32, seed)
+    Wf = kq.inverse_fold_weights(torch.from_numpy(W).cuda(), torch.from_numpy(fac).cuda())
+    got = Wf.cpu().numpy().astype(np.float64)
+    ref = orc.inverse_fold(W, fac)
+    err = np.abs(got - ref).reshape(o, d // 32, 32).max(axis=2)
+    nrm = np.sqrt((ref.reshape(o, d // 32, 32) ** 2).sum(axis=2))
+    assert np.all(err <= 1e-5 * nrm)
+    codes, scales = kq.quantize_mxfp4_f32(Wf)
+    c_ref, s_ref = orc.quantize_f32(Wf.cpu().numpy())
+    assert np.array_equal(codes.cpu().numpy(), c_ref) and np.array_equal(scales.cpu().numpy(), s_ref)
