@@ -1,10 +1,10 @@
 // Device building blocks for the KroQuant quantizer kernels on gfx950 (CDNA4).
 //
-// Lane layout shared by the bf16 kernels: a 32-channel block is held by a quad
-// of four consecutive lanes, lane `sub` (0..3) owning channels 8*sub .. 8*sub+7
-// (one 16-byte bf16 load). Channel bits 4 and 3 are therefore the two bits of
-// `sub`, bits 2..0 the position inside the lane. Cross-lane traffic never
-// leaves the quad, so it is done with DPP quad permutes.
+// Quad layout (quantize-only, SmoothQuant, butterfly transform, fp32 kernels):
+// a 32-channel block is held by four consecutive lanes, lane `sub` (0..3)
+// owning channels 8*sub .. 8*sub+7 (one 16-byte bf16 load). Channel bits 4 and
+// 3 are the two bits of `sub`, bits 2..0 the position inside the lane, and
+// cross-lane traffic stays inside the quad (DPP quad permutes).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,14 +12,29 @@
 
 namespace kq {
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
 // ---------------------------------------------------------------------------
-// Cross-lane moves inside a quad (DPP quad_perm; all four lanes must be active)
+// Cross-lane moves (all lanes taking part must be active)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float quad_xor1(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+__device__ __forceinline__ uint32_t quad_xor1_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
 }
-__device__ __forceinline__ float quad_xor2(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+__device__ __forceinline__ uint32_t quad_xor2_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ float quad_xor1(float v) { return __uint_as_float(quad_xor1_u(__float_as_uint(v))); }
+__device__ __forceinline__ float quad_xor2(float v) { return __uint_as_float(quad_xor2_u(__float_as_uint(v))); }
+
+// max over lanes l, l^16, l^32, l^48 (gfx950 row/half-wave swaps)
+__device__ __forceinline__ float max_xor16_xor32(float v) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
 // bf16 pairs packed in one dword -> two fp32 (exact widening).
@@ -37,62 +52,96 @@ __device__ __forceinline__ void widen8(const uint4 &q, float x[8]) {
 // MXFP4 block quantizer (OCP MX: E8M0 shared scale, E2M1 elements)
 // ---------------------------------------------------------------------------
 
-// E8M0 byte of a block from its largest magnitude (amax >= 0, finite):
-// e = max(floor(log2 amax) - 2, -127), byte = e + 127. For a normal amax the
-// biased exponent field E gives floor(log2 amax) = E - 127, so byte = E - 2; a
-// zero or subnormal amax (E = 0), and E = 1 or 2, clamp to byte 0.
+// E8M0 byte from the biased exponent field E of the block's largest magnitude:
+// e = max(floor(log2 amax) - 2, -127) and floor(log2 amax) = E - 127 for a
+// normal amax, so byte = e + 127 = E - 2; E <= 2 (including zero and
+// subnormal amax) clamps to byte 0.
+__device__ __forceinline__ uint32_t e8m0_from_exponent(uint32_t E) { return E > 2u ? E - 2u : 0u; }
 __device__ __forceinline__ uint32_t e8m0_byte(float amax) {
-    uint32_t E = __float_as_uint(amax) >> 23;
-    return E > 2u ? E - 2u : 0u;
+    return e8m0_from_exponent(__float_as_uint(amax) >> 23);
 }
 
-// 2^-e as fp32 for scale byte s = e + 127 (exponent field 254 - s, always normal).
-__device__ __forceinline__ float inv_scale_of(uint32_t sbyte) {
-    return __uint_as_float((254u - sbyte) << 23);
+// Scale operand of the gfx950 scaled FP4 converts: they divide by 2^(x - 127)
+// where x is the operand's fp32 exponent field, i.e. the E8M0 byte placed
+// there. Byte 0 (2^-127) works although the operand then reads as +0.0.
+__device__ __forceinline__ float cvt_scale(uint32_t sbyte) { return __uint_as_float(sbyte << 23); }
+
+// v_cvt_scalef32_pk_fp4_*: each call converts two values to E2M1 (first in the
+// low nibble) with round-to-nearest-even and saturation at 6, writing byte
+// `sel` of the result and keeping the other bytes of `old`.
+__device__ __forceinline__ uint32_t cvt8_f32(const float y[8], float sc) {
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[0], y[1], sc, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[2], y[3], sc, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[4], y[5], sc, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[6], y[7], sc, 3);
+    return r;
 }
 
-// E2M1 code of y given mul = 2^-e. v = |y| 2^-e is exact (power-of-two scaling;
-// results below 2^-126 may round but are far below the first rounding boundary
-// 0.25). Rounding to the E2M1 grid with ties to even: the grid step in the
-// binade of v is 2^(max(floor(log2 v), 0) - 1), i.e. 0.5 below 2, 1 in [2,4),
-// 2 in [4,8). Adding and subtracting M = 2^(max(floor(log2 v),0) + 22) rounds v
-// to a multiple of that step with the fp32 adder's round-to-nearest-even, and
-// the parity of the multiple equals the parity of the E2M1 code, so ties land
-// on the even code. The result is then saturated at 6 (v < 8 always holds).
-__device__ __forceinline__ uint32_t e2m1_code(float y, float mul) {
-    float v = fabsf(y) * mul;
-    uint32_t fl = __float_as_uint(v) & 0x7F800000u;
-    fl = fl > 0x3F800000u ? fl : 0x3F800000u;
-    float M = __uint_as_float(fl + (22u << 23));
-    float r = (v + M) - M;
-    r = fminf(r, 6.0f);
-    // r in {0, .5, 1, 1.5, 2, 3, 4, 6}: fp32 bits >> 22 are {0, 252, 254..259}
-    uint32_t t = __float_as_uint(r) >> 22;
-    uint32_t idx = (t > 251u ? t : 251u) - 251u;  // 0, 1, 3, 4, 5, 6, 7, 8
-    uint32_t code = idx - (idx > 2u ? 1u : 0u);
-    return code | ((__float_as_uint(y) >> 31) << 3);
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) {
+    bf16x2_t v;
+    __builtin_memcpy(&v, &w, 4);
+    return v;
 }
 
-// Quantize the 8 values a lane holds of a quad-held block. Returns the lane's
-// 8 codes packed as a dword (element 2k in the low nibble of byte k) and the
-// block's scale byte (identical in all four lanes).
-__device__ __forceinline__ uint32_t quantize_quad8(const float y[8], uint32_t &sbyte) {
-    float amax = fabsf(y[0]);
-#pragma unroll
-    for (int i = 1; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
-    amax = fmaxf(amax, quad_xor1(amax));
-    amax = fmaxf(amax, quad_xor2(amax));
+__device__ __forceinline__ uint32_t cvt8_bf16(const uint4 &q, float sc) {
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(q.x), sc, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(q.y), sc, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(q.z), sc, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(q.w), sc, 3);
+    return r;
+}
+
+// Largest |x| of 8 fp32 values.
+__device__ __forceinline__ float absmax8(const float y[8]) {
+    float a = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fabsf(y[2]));
+    float b = fmaxf(fmaxf(fabsf(y[3]), fabsf(y[4])), fabsf(y[5]));
+    float c = fmaxf(fabsf(y[6]), fabsf(y[7]));
+    return fmaxf(fmaxf(a, b), c);
+}
+
+// max(v, v of the partner lane) over a quad in one v_max_f32 with a DPP
+// operand each (s_nop 1: a DPP read after a VALU write of its source).
+__device__ __forceinline__ float quad_max(float v) {
+    asm("s_nop 1\n"
+        "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "s_nop 1\n"
+        "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+        : "+v"(v));
+    return v;
+}
+
+// Quad-held block from fp32 values: codes dword of this lane, scale byte.
+__device__ __forceinline__ uint32_t quantize_quad_f32(const float y[8], uint32_t &sbyte) {
+    const float amax = quad_max(absmax8(y));
     sbyte = e8m0_byte(amax);
-    const float mul = inv_scale_of(sbyte);
-    uint32_t packed = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) packed |= e2m1_code(y[i], mul) << (4 * i);
-    return packed;
+    return cvt8_f32(y, cvt_scale(sbyte));
+}
+
+// Quad-held block straight from bf16: the magnitude bits of finite bf16 values
+// order like unsigned integers, so the block maximum is an integer max.
+__device__ __forceinline__ uint32_t quantize_quad_bf16(const uint4 &q, uint32_t &sbyte) {
+    const uint32_t k = 0x7FFF7FFFu;
+    u16x2_t a, b, c, d;
+    const uint32_t ma = q.x & k, mb = q.y & k, mc = q.z & k, md = q.w & k;
+    __builtin_memcpy(&a, &ma, 4);
+    __builtin_memcpy(&b, &mb, 4);
+    __builtin_memcpy(&c, &mc, 4);
+    __builtin_memcpy(&d, &md, 4);
+    u16x2_t mx = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+    uint32_t m2;
+    __builtin_memcpy(&m2, &mx, 4);
+    uint32_t m = max(m2 & 0xFFFFu, m2 >> 16);
+    m = max(m, quad_xor1_u(m));
+    m = max(m, quad_xor2_u(m));
+    sbyte = e8m0_from_exponent(m >> 7);  // bf16 exponent field = fp32 exponent field
+    return cvt8_bf16(q, cvt_scale(sbyte));
 }
 
 // ---------------------------------------------------------------------------
-// Kronecker block K = G1 (x) ... (x) G5 applied as five 2x2 stages (Eq. 12):
-// stage k mixes each pair of channels that differ only in channel bit 5-k,
+// Butterfly form of K = G1 (x) ... (x) G5 (Eq. 12): stage k mixes each pair of
+// channels that differ only in channel bit 5-k,
 // (x0, x1) -> (x0 G[0][0] + x1 G[1][0], x0 G[0][1] + x1 G[1][1]).
 // ---------------------------------------------------------------------------
 struct KronLane {
@@ -129,13 +178,180 @@ __device__ __forceinline__ void inlane_stage(float x[8], const float g[4]) {
 }
 
 __device__ __forceinline__ void kron_apply8(float x[8], const KronLane &L) {
+    // partner * weight is a VOP2 multiply whose first operand can take the DPP
+    // permute directly (v_mul_f32_dpp), then one fma adds this lane's term
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = fmaf(quad_xor2(x[i]), L.o1, x[i] * L.s1);
+    for (int i = 0; i < 8; ++i) x[i] = fmaf(x[i], L.s1, quad_xor2(x[i]) * L.o1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = fmaf(quad_xor1(x[i]), L.o2, x[i] * L.s2);
+    for (int i = 0; i < 8; ++i) x[i] = fmaf(x[i], L.s2, quad_xor1(x[i]) * L.o2);
     inlane_stage<4>(x, L.g3);
     inlane_stage<2>(x, L.g4);
     inlane_stage<1>(x, L.g5);
+}
+
+// ---------------------------------------------------------------------------
+// Shear form of the same butterfly. Each factor splits exactly as
+//   G = S D,  S = [[1, G01/G11], [G10/G00, 1]],  D = diag(G00, G11),
+// and by the mixed-product rule of Kronecker products
+//   K = (S1 D1) (x) ... (x) (S5 D5) = (S1 (x) ... (x) S5) (D1 (x) ... (x) D5).
+// So the five stages become unit-diagonal shears, one fma per element each,
+// (x0, x1) -> (x0 + q x1, x1 + p x0) with p = G01/G11, q = G10/G00, followed by
+// one multiply per channel with the product of the five diagonal entries that
+// belong to it. Every intermediate is the direct butterfly's intermediate
+// divided by a per-channel constant, so rounding errors stay relative to the
+// same quantities. A block takes this path only if every G00 and G11 is
+// nonzero and the ratios stay below 2^20 in magnitude; otherwise (a swap
+// factor, say) it runs the general stages above.
+// ---------------------------------------------------------------------------
+struct ShearLane {
+    float c1, c2;                  // cross-lane: y_self = x_self + c * x_partner
+    float p3, q3, p4, q4, p5, q5;  // in-lane stages
+    float dscale[8];               // per-channel product of the diagonal entries
+    bool ok;
+};
+
+// The ratios use the hardware reciprocal (about 1 ulp); they are coefficients
+// of an exact refactoring, so a last-bit difference only moves y by rounding.
+__device__ __forceinline__ void shear_lane_setup(const float *f20, int sub, ShearLane &S) {
+    float p[5], q[5];
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+        const float g00 = f20[4 * k], g01 = f20[4 * k + 1], g10 = f20[4 * k + 2], g11 = f20[4 * k + 3];
+        const float lim = 0x1.0p20f;
+        ok = ok && fabsf(g01) <= lim * fabsf(g11) && fabsf(g10) <= lim * fabsf(g00) && g00 != 0.f && g11 != 0.f;
+        p[k] = g01 * __builtin_amdgcn_rcpf(g11);
+        q[k] = g10 * __builtin_amdgcn_rcpf(g00);
+    }
+    const int b4 = (sub >> 1) & 1, b3 = sub & 1;
+    S.c1 = b4 ? p[0] : q[0];
+    S.c2 = b3 ? p[1] : q[1];
+    S.p3 = p[2]; S.q3 = q[2];
+    S.p4 = p[3]; S.q4 = q[3];
+    S.p5 = p[4]; S.q5 = q[4];
+    const float d12 = f20[0 + 3 * b4] * f20[4 + 3 * b3];  // G1[b4][b4] G2[b3][b3]
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        S.dscale[i] = d12 * f20[8 + 3 * ((i >> 2) & 1)] * f20[12 + 3 * ((i >> 1) & 1)] * f20[16 + 3 * (i & 1)];
+    S.ok = ok;
+}
+
+// The block's 20 factor entries with five 16-byte loads (factors are 16-byte aligned).
+__device__ __forceinline__ void load_factors20(const float *p, float f[20]) {
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+        const float4 v = reinterpret_cast<const float4 *>(p)[k];
+        f[4 * k] = v.x; f[4 * k + 1] = v.y; f[4 * k + 2] = v.z; f[4 * k + 3] = v.w;
+    }
+}
+
+template <int STRIDE>
+__device__ __forceinline__ void shear_stage(float x[8], float p, float q) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (i & STRIDE) continue;
+        const float x0 = x[i], x1 = x[i + STRIDE];
+        x[i] = fmaf(x1, q, x0);
+        x[i + STRIDE] = fmaf(x0, p, x1);
+    }
+}
+
+// x[i] += c * (x[i] of the partner lane) for the 8 values, as v_fmac_f32 with a
+// DPP quad permute on its first operand (one instruction per value; the
+// compiler does not fold the permute into an fmac by itself). The leading
+// s_nop covers the wait a DPP read needs after a VALU write of its source;
+// inside the block no instruction reads what the one before it wrote.
+#define KQ_FMAC_DPP8(PERM)                                                        \
+    asm("s_nop 1\n"                                                              \
+        "v_fmac_f32_dpp %0, %0, %8 " PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+        "v_fmac_f32_dpp %1, %1, %8 " PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+        "v_fmac_f32_dpp %2, %2, %8 " PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+        "v_fmac_f32_dpp %3, %3, %8 " PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+        "v_fmac_f32_dpp %4, %4, %8 " PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+        "v_fmac_f32_dpp %5, %5, %8 " PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+        "v_fmac_f32_dpp %6, %6, %8 " PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+        "v_fmac_f32_dpp %7, %7, %8 " PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1"   \
+        : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]),  \
+          "+v"(x[6]), "+v"(x[7])                                                  \
+        : "v"(c))
+
+__device__ __forceinline__ void fmac_partner_xor2(float x[8], float c) { KQ_FMAC_DPP8("quad_perm:[2,3,0,1]"); }
+__device__ __forceinline__ void fmac_partner_xor1(float x[8], float c) { KQ_FMAC_DPP8("quad_perm:[1,0,3,2]"); }
+
+__device__ __forceinline__ void shear_apply8(float x[8], const ShearLane &S) {
+    fmac_partner_xor2(x, S.c1);  // G1: channel bit 4 = bit 1 of sub
+    fmac_partner_xor1(x, S.c2);  // G2: channel bit 3 = bit 0 of sub
+    shear_stage<4>(x, S.p3, S.q3);
+    shear_stage<2>(x, S.p4, S.q4);
+    shear_stage<1>(x, S.p5, S.q5);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = x[i] * S.dscale[i];
+}
+
+// ---------------------------------------------------------------------------
+// Materialized form on MFMA: per block, D = K^T X^T with
+// v_mfma_f32_16x16x32_bf16 (A operand 16x32 from K^T, B operand 32x16 from 16
+// tokens' bf16 channels, fp32 accumulate). Lane l supplies B[k][n] for token
+// n = l % 16, input channels k = 8 (l / 16) + t (one 16-byte load), and A[i][k]
+// for output row i = l % 16; it receives D[i][n] for i = 4 (l / 16) + t.
+// Output rows are mapped to channels c(h, i) = 8 (i / 4) + 4 h + i % 4 for the
+// two halves h, so lane l ends up with channels 8 (l / 16) .. +7 of its token.
+// K is carried as three bf16 terms (hi + mid + lo), which represent the fp32
+// entries exactly; each product with a bf16 input is exact and the sums
+// accumulate in fp32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t bf16_rne_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+struct KSplit {
+    bf16x8_t t[3][2];  // [term hi/mid/lo][half h]
+};
+
+// Entries K[r][c] for r = 8 g + t (t = 0..7), c = c(h, l % 16), from Eq. 12.
+__device__ __forceinline__ void ksplit_setup(const float *f20, int lane, KSplit &S) {
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = 8 * (i >> 2) + 4 * h + (i & 3);
+        const float pc = f20[0 + 2 * (g >> 1) + ((c >> 4) & 1)] * f20[4 + 2 * (g & 1) + ((c >> 3) & 1)];
+        uint16_t hv[8], mv[8], lv[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float k = pc * f20[8 + 2 * ((t >> 2) & 1) + ((c >> 2) & 1)] *
+                            f20[12 + 2 * ((t >> 1) & 1) + ((c >> 1) & 1)] *
+                            f20[16 + 2 * (t & 1) + (c & 1)];
+            hv[t] = bf16_rne_bits(k);
+            const float r1 = k - __uint_as_float((uint32_t)hv[t] << 16);  // exact
+            mv[t] = bf16_rne_bits(r1);
+            lv[t] = bf16_rne_bits(r1 - __uint_as_float((uint32_t)mv[t] << 16));  // exact
+        }
+        __builtin_memcpy(&S.t[0][h], hv, 16);
+        __builtin_memcpy(&S.t[1][h], mv, 16);
+        __builtin_memcpy(&S.t[2][h], lv, 16);
+    }
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 &q) {
+    bf16x8_t v;
+    __builtin_memcpy(&v, &q, 16);
+    return v;
+}
+
+// y[0..7] = channels 8 (lane / 16) .. +7 of this lane's token, fp32.
+__device__ __forceinline__ void kron_mfma8(const KSplit &S, const uint4 &q, float y[8]) {
+    const bf16x8_t b = as_bf16x8(q);
+    floatx4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+    d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(S.t[2][0], b, d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(S.t[2][1], b, d1, 0, 0, 0);
+    d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(S.t[1][0], b, d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(S.t[1][1], b, d1, 0, 0, 0);
+    d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(S.t[0][0], b, d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(S.t[0][1], b, d1, 0, 0, 0);
+    y[0] = d0[0]; y[1] = d0[1]; y[2] = d0[2]; y[3] = d0[3];
+    y[4] = d1[0]; y[5] = d1[1]; y[6] = d1[2]; y[7] = d1[3];
 }
 
 }  // namespace kq

@@ -14,6 +14,8 @@
 // 2 bytes in, 0.5 + 1/32 bytes out per element.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "kq.h"
 #include "kq_device.hpp"
@@ -24,75 +26,261 @@ constexpr int kThreads = 256;
 
 enum Mode { kQuantOnly = 0, kSmooth = 1, kKron = 2 };
 
+// Workgroup -> work mapping of the quad kernels (a workgroup is 64 quads, a
+// quad owns one 32-channel block of one row at a time).
+//  kStrip: the 64 quads cover CB = 2^cb_log2 consecutive blocks of R = 64 / CB
+//          consecutive rows; workgroup w takes column group w % ncg and row
+//          slab w / ncg and walks `iters` row tiles of that slab (rstep = R).
+//  kFlat:  blocks are numbered row-major (b = row * nblk + j); workgroup w,
+//          quad q starts at block 64 w + q and advances by the whole grid
+//          (64 gridDim.x blocks, a multiple of nblk, so j stays fixed) per
+//          sweep, i.e. by rstep = 64 gridDim.x / nblk rows.
+// In both, a quad keeps one block column for its whole life, so per-block
+// parameters load once.
+enum Map { kStrip = 0, kFlat = 1 };
+
 struct Geom {
-    int64_t m, lda, d;
-    int nblk, cb_log2, iters, ncg;
+    int64_t m, lda, d, rstep;
+    int nblk, iters, cb_log2, ncg;
 };
 
-// Row, block column and lane-in-quad of this lane for row tile `it`.
-__device__ __forceinline__ void lane_coords(const Geom &g, int &j, int &sub, int64_t &row0, int &R) {
-    const int tid = threadIdx.x;
-    const int quad = tid >> 2;
-    sub = tid & 3;
-    const int cg = blockIdx.x % g.ncg;
-    const int slab = blockIdx.x / g.ncg;
-    R = 64 >> g.cb_log2;
-    j = (cg << g.cb_log2) + (quad & ((1 << g.cb_log2) - 1));
-    row0 = (int64_t)slab * R * g.iters + (quad >> g.cb_log2);
+template <int MAP>
+__device__ __forceinline__ void lane_coords(const Geom &g, int &j, int &sub, int64_t &row0) {
+    sub = threadIdx.x & 3;
+    const int quad = threadIdx.x >> 2;
+    if (MAP == kFlat) {
+        const int64_t b0 = (int64_t)blockIdx.x * 64 + quad;
+        j = (int)(b0 % g.nblk);
+        row0 = b0 / g.nblk;
+    } else {
+        const int cg = (int)(blockIdx.x % (unsigned)g.ncg);
+        const int64_t slab = blockIdx.x / (unsigned)g.ncg;
+        j = (cg << g.cb_log2) + (quad & ((1 << g.cb_log2) - 1));
+        row0 = slab * g.rstep * g.iters + (quad >> g.cb_log2);
+    }
 }
 
-template <int MODE, bool DEBUG>
-__global__ __launch_bounds__(kThreads) void bf16_quant_kernel(
+// 16-byte load; NT marks it non-temporal (streamed once, no reuse expected).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4 *p, bool nt) {
+    if (!nt) return *p;
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Walks this quad's rows row0 + k rstep (k < iters), U rows' loads issued
+// together (PF: the next group's loads are issued before this group is
+// processed), and calls body(q, row) for each row below m. The row test is
+// uniform within a quad, so DPP inside `body` sees all four lanes.
+template <int U, bool NT, bool PF, typename Body>
+__device__ __forceinline__ void for_rows(const Geom &g, const uint16_t *__restrict__ A, int64_t row0,
+                                         int64_t c0, Body body) {
+    const int64_t R = g.rstep;
+    auto load_rows = [&](int it, uint4 (&q)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = row0 + (int64_t)(it + u) * R;
+            q[u] = row < g.m ? load_stream(reinterpret_cast<const uint4 *>(A + row * g.lda + c0), NT)
+                             : make_uint4(0, 0, 0, 0);
+        }
+    };
+    uint4 q[U];
+    load_rows(0, q);
+    for (int it = 0; it < g.iters; it += U) {
+        if (row0 + (int64_t)it * R >= g.m) break;
+        const bool more = it + U < g.iters;
+        uint4 qn[U];
+        if (PF && more) load_rows(it + U, qn);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = row0 + (int64_t)(it + u) * R;
+            if (row >= g.m) break;
+            body(q[u], row);
+        }
+        if (more) {
+            if (!PF) load_rows(it + U, qn);
+#pragma unroll
+            for (int u = 0; u < U; ++u) q[u] = qn[u];
+        }
+    }
+}
+
+// Quantize fp32 values of a quad-held block and store codes and scale
+// (and y itself in check mode).
+template <bool DEBUG>
+__device__ __forceinline__ void finish_f32(const float y[8], const Geom &g, int64_t row, int j, int sub,
+                                           int64_t c0, uint8_t *__restrict__ codes,
+                                           uint8_t *__restrict__ scales, float *__restrict__ ydbg) {
+    if (DEBUG) {
+        float4 *o = reinterpret_cast<float4 *>(ydbg + row * g.d + c0);
+        o[0] = make_float4(y[0], y[1], y[2], y[3]);
+        o[1] = make_float4(y[4], y[5], y[6], y[7]);
+    }
+    uint32_t sbyte;
+    const uint32_t packed = quantize_quad_f32(y, sbyte);
+    *reinterpret_cast<uint32_t *>(codes + row * (g.d / 2) + (int64_t)j * 16 + sub * 4) = packed;
+    if (sub == 0) scales[row * g.nblk + j] = (uint8_t)sbyte;
+}
+
+// bf16 input, quad layout: quantize-only (T = I), SmoothQuant (T = diag(inv_scale))
+// or the Kronecker transform (shear form, or the general stages for blocks
+// that do not admit it).
+template <int MODE, bool DEBUG, int U, bool NT, bool PF, int MAP>
+__global__ __launch_bounds__(kThreads) void bf16_quad_kernel(
     const uint16_t *__restrict__ A, Geom g, const float *__restrict__ params,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ ydbg) {
-    int j, sub, R;
+    int j, sub;
     int64_t row0;
-    lane_coords(g, j, sub, row0, R);
+    lane_coords<MAP>(g, j, sub, row0);
     const int64_t c0 = (int64_t)j * 32 + sub * 8;
 
-    KronLane L;
-    float sq[8];
-    if (MODE == kKron) kron_lane_setup(params + (int64_t)j * 20, sub, L);
-    if (MODE == kSmooth) {
+    if (MODE == kQuantOnly) {
+        for_rows<U, NT, PF>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
+            uint32_t sbyte;
+            const uint32_t packed = quantize_quad_bf16(q, sbyte);
+            *reinterpret_cast<uint32_t *>(codes + row * (g.d / 2) + (int64_t)j * 16 + sub * 4) = packed;
+            if (sub == 0) scales[row * g.nblk + j] = (uint8_t)sbyte;
+        });
+    } else if (MODE == kSmooth) {
+        float sq[8];
         const float4 a = *reinterpret_cast<const float4 *>(params + c0);
         const float4 b = *reinterpret_cast<const float4 *>(params + c0 + 4);
         sq[0] = a.x; sq[1] = a.y; sq[2] = a.z; sq[3] = a.w;
         sq[4] = b.x; sq[5] = b.y; sq[6] = b.z; sq[7] = b.w;
-    }
-
-    for (int it = 0; it < g.iters; ++it) {
-        const int64_t row = row0 + (int64_t)it * R;
-        if (row >= g.m) break;  // uniform within a quad
-        const uint4 q = *reinterpret_cast<const uint4 *>(A + row * g.lda + c0);
-        float y[8];
-        widen8(q, y);
-        if (MODE == kSmooth) {
+        for_rows<U, NT, PF>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
+            float y[8];
+            widen8(q, y);
 #pragma unroll
             for (int i = 0; i < 8; ++i) y[i] = y[i] * sq[i];
+            finish_f32<DEBUG>(y, g, row, j, sub, c0, codes, scales, ydbg);
+        });
+    } else {
+        // Per-block setup is shared through LDS when the workgroup's first row
+        // of quads holds all its blocks (strip mapping): those quads (wave 0
+        // for CB = 16) derive the shear coefficients, everyone reads them back.
+        ShearLane S;
+        if (MAP == kStrip) {
+            __shared__ ShearLane lds[64];
+            const int quad = threadIdx.x >> 2;
+            if ((quad >> g.cb_log2) == 0) {
+                float f[20];
+                load_factors20(params + (int64_t)j * 20, f);
+                shear_lane_setup(f, sub, lds[threadIdx.x]);
+            }
+            __syncthreads();
+            S = lds[((quad & ((1 << g.cb_log2) - 1)) << 2) | sub];
+        } else {
+            float f[20];
+            load_factors20(params + (int64_t)j * 20, f);
+            shear_lane_setup(f, sub, S);
         }
-        if (MODE == kKron) kron_apply8(y, L);
-        if (DEBUG) {
-            float4 *o = reinterpret_cast<float4 *>(ydbg + row * g.d + c0);
-            o[0] = make_float4(y[0], y[1], y[2], y[3]);
-            o[1] = make_float4(y[4], y[5], y[6], y[7]);
+        if (S.ok) {  // one block per quad: uniform within the quad
+            for_rows<U, NT, PF>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
+                float y[8];
+                widen8(q, y);
+                shear_apply8(y, S);
+                finish_f32<DEBUG>(y, g, row, j, sub, c0, codes, scales, ydbg);
+            });
+        } else {
+            float f[20];
+            load_factors20(params + (int64_t)j * 20, f);
+            KronLane L;
+            kron_lane_setup(f, sub, L);
+            for_rows<U, NT, PF>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
+                float y[8];
+                widen8(q, y);
+                kron_apply8(y, L);
+                finish_f32<DEBUG>(y, g, row, j, sub, c0, codes, scales, ydbg);
+            });
         }
-        uint32_t sbyte;
-        const uint32_t packed = quantize_quad8(y, sbyte);
-        *reinterpret_cast<uint32_t *>(codes + row * (g.d / 2) + (int64_t)j * 16 + sub * 4) = packed;
-        if (sub == 0) scales[row * g.nblk + j] = (uint8_t)sbyte;
     }
 }
 
-// fp32 input: the same quad layout with two 16-byte loads per lane.
-// MODE kQuantOnly quantizes X; MODE kKron writes X . (K^(j))^{-T} (the weight
-// fold) to `out` instead of quantizing.
+// MFMA form of the fused kernel. Each wave owns NB consecutive blocks and walks
+// `iters` tiles of 16 tokens of one slab; a workgroup is 4 such waves with
+// consecutive wave ids (neighbouring column groups).
+struct MGeom {
+    int64_t m, lda, d, nwaves;
+    int nblk, ncg, iters;
+};
+
+template <int NB, bool DEBUG, int U, bool NT, bool PF>
+__global__ __launch_bounds__(kThreads) void kron_mfma_kernel(
+    const uint16_t *__restrict__ A, MGeom g, const float *__restrict__ factors,
+    uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ ydbg) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (wid >= g.nwaves) return;  // whole waves only
+    const int cgw = (int)(wid % g.ncg);
+    const int64_t tile0 = (wid / g.ncg) * g.iters;
+    const int grp = lane >> 4;
+
+    KSplit S[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) ksplit_setup(factors + (int64_t)(cgw * NB + nb) * 20, lane, S[nb]);
+
+    auto load_tiles = [&](int it, uint4 (&q)[U][NB]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t tok = (tile0 + it + u) * 16 + (lane & 15);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int64_t off = tok * g.lda + (int64_t)(cgw * NB + nb) * 32 + grp * 8;
+                q[u][nb] = tok < g.m ? load_stream(reinterpret_cast<const uint4 *>(A + off), NT)
+                                     : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+
+    uint4 q[U][NB];
+    load_tiles(0, q);
+    for (int it = 0; it < g.iters; it += U) {
+        if ((tile0 + it) * 16 >= g.m) break;  // uniform within the wave
+        const bool more = it + U < g.iters;
+        uint4 qn[U][NB];
+        if (PF && more) load_tiles(it + U, qn);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t tok = (tile0 + it + u) * 16 + (lane & 15);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int jb = cgw * NB + nb;
+                float y[8];
+                kron_mfma8(S[nb], q[u][nb], y);  // all 64 lanes take part
+                const float amax = max_xor16_xor32(absmax8(y));
+                const uint32_t sbyte = e8m0_byte(amax);
+                const uint32_t packed = cvt8_f32(y, cvt_scale(sbyte));
+                if (tok < g.m) {
+                    if (DEBUG) {
+                        float4 *o = reinterpret_cast<float4 *>(ydbg + tok * g.d + (int64_t)jb * 32 + grp * 8);
+                        o[0] = make_float4(y[0], y[1], y[2], y[3]);
+                        o[1] = make_float4(y[4], y[5], y[6], y[7]);
+                    }
+                    *reinterpret_cast<uint32_t *>(codes + tok * (g.d / 2) + (int64_t)jb * 16 + grp * 4) = packed;
+                    if (grp == 0) scales[tok * g.nblk + jb] = (uint8_t)sbyte;
+                }
+            }
+        }
+        if (more) {
+            if (!PF) load_tiles(it + U, qn);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) q[u][nb] = qn[u][nb];
+        }
+    }
+}
+
+// fp32 input, quad layout: quantize (MODE kQuantOnly) or, with MODE kKron,
+// write X . (K^(j))^{-T} (the weight fold) to `out` instead of quantizing.
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void f32_kernel(
     const float *__restrict__ X, Geom g, const float *__restrict__ factors,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ out) {
-    int j, sub, R;
+    int j, sub;
     int64_t row0;
-    lane_coords(g, j, sub, row0, R);
+    lane_coords<kFlat>(g, j, sub, row0);
+    const int64_t R = g.rstep;
     const int64_t c0 = (int64_t)j * 32 + sub * 8;
 
     KronLane L;
@@ -126,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void f32_kernel(
             o[1] = make_float4(y[4], y[5], y[6], y[7]);
         } else {
             uint32_t sbyte;
-            const uint32_t packed = quantize_quad8(y, sbyte);
+            const uint32_t packed = quantize_quad_f32(y, sbyte);
             *reinterpret_cast<uint32_t *>(codes + row * (g.d / 2) + (int64_t)j * 16 + sub * 4) = packed;
             if (sub == 0) scales[row * g.nblk + j] = (uint8_t)sbyte;
         }
@@ -154,33 +342,92 @@ kq_status check_shape(int64_t m, int64_t d, int64_t ld) {
     return KQ_OK;
 }
 
-int pick_cb_log2(int64_t nblk) {
-    for (int l = 4; l > 0; --l)
+int64_t gcd64(int64_t a, int64_t b) {
+    while (b) {
+        const int64_t t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+int pick_cb_log2(int64_t nblk, int max_log2) {
+    for (int l = max_log2; l > 0; --l)
         if (nblk % (1 << l) == 0) return l;
     return 0;
 }
 
-// Grid: one workgroup per (column group, row slab); slabs sized so that the
-// launch has about 16 workgroups per CU when the matrix is large enough.
-bool make_geom(int64_t m, int64_t d, int64_t ld, kq::Geom &g, unsigned &nwg) {
+// kFlat: about `target_wg` workgroups (fewer if the matrix is small), a multiple
+// of nblk / gcd(64, nblk) so that 64 * gridDim.x is a multiple of nblk.
+// `iters` (sweeps per workgroup) is rounded up to a multiple of `unroll`.
+bool make_geom_flat(int64_t m, int64_t d, int64_t ld, int unroll, int64_t target_wg, kq::Geom &g,
+                    unsigned &nwg) {
     g.m = m;
     g.d = d;
     g.lda = ld;
     g.nblk = (int)(d / 32);
-    g.cb_log2 = pick_cb_log2(g.nblk);
+    g.cb_log2 = 0;
+    g.ncg = 1;
+    const int64_t k0 = g.nblk / gcd64(64, g.nblk);
+    const int64_t need = (m * g.nblk + 63) / 64;
+    int64_t w = need < target_wg ? need : target_wg;
+    w = (w + k0 - 1) / k0 * k0;
+    if (w > 0x7FFFFFFF) return false;
+    g.rstep = w * 64 / g.nblk;
+    int64_t iters = (m + g.rstep - 1) / g.rstep;
+    iters = (iters + unroll - 1) / unroll * unroll;
+    if (iters > 0x7FFFFFFF) return false;
+    g.iters = (int)iters;
+    nwg = (unsigned)w;
+    return true;
+}
+
+// kStrip: column groups of CB blocks (the largest power of two <= 2^max_cb_log2
+// dividing nblk), row tiles of R = 64 / CB rows, `iters_per_wg` row tiles per
+// workgroup (rounded up to a multiple of `unroll`).
+bool make_geom_strip(int64_t m, int64_t d, int64_t ld, int unroll, int64_t iters_per_wg, kq::Geom &g,
+                     unsigned &nwg, int max_cb_log2 = 4) {
+    g.m = m;
+    g.d = d;
+    g.lda = ld;
+    g.nblk = (int)(d / 32);
+    g.cb_log2 = pick_cb_log2(g.nblk, max_cb_log2);
     g.ncg = g.nblk >> g.cb_log2;
-    const int64_t R = 64 >> g.cb_log2;
-    const int64_t row_tiles = (m + R - 1) / R;
-    const int64_t units = row_tiles * g.ncg;
-    const int64_t target = 256 * 16;
-    int64_t iters = (units + target - 1) / target;
-    if (iters < 1) iters = 1;
-    if (iters > (1 << 20)) iters = 1 << 20;
+    g.rstep = 64 >> g.cb_log2;
+    const int64_t row_tiles = (m + g.rstep - 1) / g.rstep;
+    int64_t iters = iters_per_wg < 1 ? 1 : iters_per_wg;
+    iters = (iters + unroll - 1) / unroll * unroll;
+    if (iters > row_tiles) iters = (row_tiles + unroll - 1) / unroll * unroll;
     const int64_t nslab = (row_tiles + iters - 1) / iters;
     const int64_t total = nslab * g.ncg;
-    if (total > 0x7FFFFFFF) return false;
+    if (total > 0x7FFFFFFF || iters > 0x7FFFFFFF) return false;
     g.iters = (int)iters;
     nwg = (unsigned)total;
+    return true;
+}
+
+// MFMA form: waves own NB blocks and `iters` 16-token tiles (a multiple of the unroll).
+bool make_mgeom(int64_t m, int64_t d, int64_t lda, int nb, int unroll, kq::MGeom &g, unsigned &nwg,
+                int64_t target_waves = 0) {
+    g.m = m;
+    g.d = d;
+    g.lda = lda;
+    g.nblk = (int)(d / 32);
+    g.ncg = g.nblk / nb;
+    const int64_t tiles = (m + 15) / 16;
+    const int64_t units = tiles * g.ncg;
+    // default: about one resident round of waves, occupancy 4 (NB = 2) or 6 (NB = 1) per SIMD
+    if (target_waves <= 0) target_waves = 256 * 4 * (nb == 2 ? 4 : 6);
+    int64_t iters = (units + target_waves - 1) / target_waves;
+    if (iters < 1) iters = 1;
+    if (iters > (1 << 20)) iters = 1 << 20;
+    iters = (iters + unroll - 1) / unroll * unroll;
+    const int64_t nslab = (tiles + iters - 1) / iters;
+    g.nwaves = nslab * g.ncg;
+    const int64_t wg = (g.nwaves + 3) / 4;
+    if (wg > 0x7FFFFFFF) return false;
+    g.iters = (int)iters;
+    nwg = (unsigned)wg;
     return true;
 }
 
@@ -193,15 +440,51 @@ kq_status launched() {
     return KQ_OK;
 }
 
+// Launch shape of the bf16 quad kernels (column strips, row tiles of 64 / CB
+// rows, U rows' loads in flight, non-temporal loads). Workgroups are kept
+// short: the quantizers walk 2 row tiles, the transform 8 (its per-block setup
+// is amortized over more rows).
 template <int MODE, bool DEBUG>
-kq_status launch_bf16(const uint16_t *A, int64_t m, int64_t d, int64_t lda, const float *params,
+kq_status launch_quad(const uint16_t *A, int64_t m, int64_t d, int64_t lda, const float *params,
                       uint8_t *codes, uint8_t *scales, float *ydbg, kq_stream_t stream) {
+    constexpr int U = 2;
+    const int64_t iters = MODE == kq::kKron ? 8 : 2;
     kq::Geom g;
     unsigned nwg;
-    if (!make_geom(m, d, lda, g, nwg)) return KQ_ERR_SHAPE;
-    hipLaunchKernelGGL((kq::bf16_quant_kernel<MODE, DEBUG>), dim3(nwg), dim3(kq::kThreads), 0,
-                       (hipStream_t)stream, A, g, params, codes, scales, ydbg);
+    if (!make_geom_strip(m, d, lda, U, iters, g, nwg)) return KQ_ERR_SHAPE;
+    hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, DEBUG, U, true, false, kq::kStrip>), dim3(nwg),
+                       dim3(kq::kThreads), 0, (hipStream_t)stream, A, g, params, codes, scales, ydbg);
     return launched();
+}
+
+template <int NB, bool DEBUG>
+kq_status launch_mfma(const uint16_t *A, int64_t m, int64_t d, int64_t lda, const float *factors,
+                      uint8_t *codes, uint8_t *scales, float *ydbg, kq_stream_t stream) {
+    kq::MGeom g;
+    unsigned nwg;
+    if (!make_mgeom(m, d, lda, NB, 2, g, nwg)) return KQ_ERR_SHAPE;
+    hipLaunchKernelGGL((kq::kron_mfma_kernel<NB, DEBUG, 2, false, false>), dim3(nwg), dim3(kq::kThreads), 0,
+                       (hipStream_t)stream, A, g, factors, codes, scales, ydbg);
+    return launched();
+}
+
+// Which form of the transform the fused entry point runs: five in-register
+// 2x2 stages (shear form, default) or the materialized 32x32 block on MFMA.
+// KQ_TRANSFORM_FORM=mfma selects the latter (read at every call). Measured on
+// the FLUX shapes the MFMA form is bound by its 16-token tiles' strided
+// accesses, so it is kept for comparison only.
+bool use_mfma() {
+    const char *v = getenv("KQ_TRANSFORM_FORM");
+    return v && strcmp(v, "mfma") == 0;
+}
+
+template <bool DEBUG>
+kq_status launch_fused(const uint16_t *A, int64_t m, int64_t d, int64_t lda, const float *factors,
+                       uint8_t *codes, uint8_t *scales, float *ydbg, kq_stream_t stream) {
+    if (!use_mfma()) return launch_quad<kq::kKron, DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
+    if ((d / 32) % 2 == 0)
+        return launch_mfma<2, DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
+    return launch_mfma<1, DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
 }
 
 kq_status check_bf16_io(const uint16_t *A, int64_t lda, const uint8_t *codes, const uint8_t *scales) {
@@ -220,7 +503,7 @@ kq_status kq_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda
     if (s != KQ_OK) return s;
     if (m == 0 || d == 0) return KQ_OK;
     if ((s = check_bf16_io(A, lda, codes, scales)) != KQ_OK) return s;
-    return launch_bf16<kq::kQuantOnly, false>(A, m, d, lda, nullptr, codes, scales, nullptr, stream);
+    return launch_quad<kq::kQuantOnly, false>(A, m, d, lda, nullptr, codes, scales, nullptr, stream);
 }
 
 kq_status kq_transform_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
@@ -232,9 +515,8 @@ kq_status kq_transform_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, i
     if ((s = check_bf16_io(A, lda, codes, scales)) != KQ_OK) return s;
     if (!factors) return KQ_ERR_NULL;
     if (!aligned(factors, 16) || (y_debug && !aligned(y_debug, 16))) return KQ_ERR_ALIGN;
-    if (y_debug)
-        return launch_bf16<kq::kKron, true>(A, m, d, lda, factors, codes, scales, y_debug, stream);
-    return launch_bf16<kq::kKron, false>(A, m, d, lda, factors, codes, scales, nullptr, stream);
+    if (y_debug) return launch_fused<true>(A, m, d, lda, factors, codes, scales, y_debug, stream);
+    return launch_fused<false>(A, m, d, lda, factors, codes, scales, nullptr, stream);
 }
 
 kq_status kq_smoothquant_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
@@ -246,7 +528,7 @@ kq_status kq_smoothquant_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d,
     if ((s = check_bf16_io(A, lda, codes, scales)) != KQ_OK) return s;
     if (!inv_scale) return KQ_ERR_NULL;
     if (!aligned(inv_scale, 16)) return KQ_ERR_ALIGN;
-    return launch_bf16<kq::kSmooth, false>(A, m, d, lda, inv_scale, codes, scales, nullptr, stream);
+    return launch_quad<kq::kSmooth, false>(A, m, d, lda, inv_scale, codes, scales, nullptr, stream);
 }
 
 kq_status kq_quantize_mxfp4_f32(const float *X, int64_t m, int64_t d, int64_t ldx, uint8_t *codes,
@@ -258,7 +540,7 @@ kq_status kq_quantize_mxfp4_f32(const float *X, int64_t m, int64_t d, int64_t ld
     if (!aligned(X, 16) || ldx % 4 != 0 || !aligned(codes, 16)) return KQ_ERR_ALIGN;
     kq::Geom g;
     unsigned nwg;
-    if (!make_geom(m, d, ldx, g, nwg)) return KQ_ERR_SHAPE;
+    if (!make_geom_flat(m, d, ldx, 1, 256 * 8, g, nwg)) return KQ_ERR_SHAPE;
     hipLaunchKernelGGL((kq::f32_kernel<kq::kQuantOnly>), dim3(nwg), dim3(kq::kThreads), 0,
                        (hipStream_t)stream, X, g, nullptr, codes, scales, nullptr);
     return launched();
@@ -273,7 +555,7 @@ kq_status kq_inverse_fold_weights(const float *W, int64_t o, int64_t d, const fl
     if (!aligned(W, 16) || !aligned(factors, 16) || !aligned(W_folded, 16)) return KQ_ERR_ALIGN;
     kq::Geom g;
     unsigned nwg;
-    if (!make_geom(o, d, d, g, nwg)) return KQ_ERR_SHAPE;
+    if (!make_geom_flat(o, d, d, 1, 256 * 8, g, nwg)) return KQ_ERR_SHAPE;
     hipLaunchKernelGGL((kq::f32_kernel<kq::kKron>), dim3(nwg), dim3(kq::kThreads), 0,
                        (hipStream_t)stream, W, g, factors, nullptr, nullptr, W_folded);
     return launched();

@@ -102,10 +102,17 @@ def test_smoothquant_bit_exact(torch_dev, kq, orc, name):
 # fused Kronecker transform + quantize
 # ---------------------------------------------------------------------------
 
+@pytest.fixture(params=["mfma", "butterfly"])
+def form(request, monkeypatch):
+    """Transform form the library runs (read by libkq.so at every call)."""
+    monkeypatch.setenv("KQ_TRANSFORM_FORM", request.param)  # "butterfly" is the default form
+    return request.param
+
+
 @pytest.mark.parametrize("name", FULL + SAMPLED)
-def test_fused_against_oracle(torch_dev, kq, orc, name):
+def test_fused_against_oracle(torch_dev, kq, orc, name, form):
     torch = torch_dev
-    case("fused " + name)
+    case("fused %s form=%s" % (name, form))
     w = workload(name)
     A = dev_bf16(torch, w.A)
     fac = torch.from_numpy(w.factors).cuda()
@@ -118,13 +125,13 @@ def test_fused_against_oracle(torch_dev, kq, orc, name):
     rows = np.arange(w.m) if name in FULL else sample_rows(w.m, SAMPLE_ROWS)
     rep = parity.fused_report(orc, w.A[rows], w.factors, gather(torch, codes, rows),
                               gather(torch, scales, rows), gather(torch, y, rows))
-    print("[parity] %s %s" % (name, rep), flush=True)
+    print("[parity] %s %s %s" % (name, form, rep), flush=True)
 
 
 @pytest.mark.parametrize("kind", ["identity", "swap", "signflip", "pow2", "mixed"])
-def test_fused_exact_factors_reduce_to_quantizer(torch_dev, kq, orc, kind):
+def test_fused_exact_factors_reduce_to_quantizer(torch_dev, kq, orc, kind, form):
     torch = torch_dev
-    case("fused exact factors " + kind)
+    case("fused exact factors %s form=%s" % (kind, form))
     w = workload("pixart_attn_4096x1152")
     f = synth.special_factors(w.d // 32, kind)
     A = dev_bf16(torch, w.A)
@@ -139,9 +146,9 @@ def test_fused_exact_factors_reduce_to_quantizer(torch_dev, kq, orc, kind):
         parity.assert_codes_equal_mod_signed_zero(q_codes.cpu().numpy(), codes.cpu().numpy())
 
 
-def test_fused_hadamard_worked_example(torch_dev, kq, orc):
+def test_fused_hadamard_worked_example(torch_dev, kq, orc, form):
     torch = torch_dev
-    case("fused hadamard worked example")
+    case("fused hadamard worked example form=" + form)
     A = np.zeros((4, 64), np.uint16)
     A[:, 3] = synth.to_bf16_bits(np.array([80.0]))[0]
     A[1, 32 + 7] = synth.to_bf16_bits(np.array([-3.0]))[0]
@@ -231,9 +238,9 @@ def test_f32_quantizer_at_rounding_boundaries(torch_dev, kq, orc):
 
 @pytest.mark.parametrize("m,d,pad", [(1, 32, 0), (3, 96, 8), (37, 160, 0), (4133, 1152, 64),
                                      (517, 4608, 0), (70, 512, 24), (1, 12288, 0)])
-def test_ragged_shapes_and_padded_rows(torch_dev, kq, orc, m, d, pad):
+def test_ragged_shapes_and_padded_rows(torch_dev, kq, orc, m, d, pad, form):
     torch = torch_dev
-    case("ragged m=%d d=%d pad=%d" % (m, d, pad))
+    case("ragged m=%d d=%d pad=%d form=%s" % (m, d, pad, form))
     A_full = synth.random_bf16_matrix(m, d + pad, seed=m * 7 + d, scale=3.0)
     A_full[:, min(5, d - 1)] = synth.to_bf16_bits(np.full(m, 300.0))
     fac = synth.lu_perturbed_factors(d // 32, seed=d + 1)
@@ -252,9 +259,9 @@ def test_ragged_shapes_and_padded_rows(torch_dev, kq, orc, m, d, pad):
                         scales.cpu().numpy(), y.cpu().numpy())
 
 
-def test_guard_bytes_determinism_and_side_stream(torch_dev, kq):
+def test_guard_bytes_determinism_and_side_stream(torch_dev, kq, form):
     torch = torch_dev
-    case("guard bytes / determinism / stream")
+    case("guard bytes / determinism / stream form=" + form)
     w = workload("pixart_attn_4096x1152")
     m, d = w.m, w.d
     A = dev_bf16(torch, w.A)
@@ -272,6 +279,25 @@ def test_guard_bytes_determinism_and_side_stream(torch_dev, kq):
     c2, s2 = kq.transform_quantize_mxfp4(A, fac)
     torch.cuda.synchronize()
     assert torch.equal(c2, codes) and torch.equal(s2, scales)
+
+
+def test_fused_tiny_and_mixed_magnitudes(torch_dev, kq, orc, form):
+    """Blocks of bf16 subnormals, of values near the bottom of the normal range and of
+    mixed magnitudes spanning 60 binades."""
+    torch = torch_dev
+    case("fused tiny magnitudes form=" + form)
+    rng = np.random.default_rng(12)
+    m, d = 96, 256
+    X = rng.standard_normal((m, d))
+    X[:32] *= 2.0 ** -130      # subnormal bf16
+    X[32:64] *= 2.0 ** -120    # small normals
+    X[64:] *= 2.0 ** rng.integers(-30, 30, (32, d))
+    A = synth.to_bf16_bits(X)
+    fac = synth.lu_perturbed_factors(d // 32, 77)
+    y = torch.empty((m, d), dtype=torch.float32, device="cuda")
+    codes, scales = kq.transform_quantize_mxfp4(dev_bf16(torch, A), torch.from_numpy(fac).cuda(), y_debug=y)
+    rep = parity.fused_report(orc, A, fac, codes.cpu().numpy(), scales.cpu().numpy(), y.cpu().numpy())
+    print("[parity] tiny %s %s" % (form, rep), flush=True)
 
 
 def test_empty_inputs(torch_dev, kq):
