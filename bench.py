@@ -49,6 +49,16 @@ def parse():
                     help="minimum host time spent on the CPU-oracle baseline (0 disables it)")
     ap.add_argument("--only", choices=["fused", "smoothquant", "quantize"], default=None,
                     help="time only one kernel (for profiler runs)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time steps as eager launches instead of replaying one HIP graph per step")
+    ap.add_argument("--tensor", type=int, choices=[3072, 12288], default=None,
+                    help="time only the tensor with this d (for profiler runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy, 10 times (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                         "COPY_WRITE_DIR", "OUT_JSON"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of the fused d=12288 "
+                         "launch and of the copy calibration into HBM bytes per launch")
     return ap.parse_args()
 
 
@@ -72,11 +82,15 @@ class Sets:
     def next(self):
         k = self.i % self.n
         self.i += 1
+        return self.get(k)
+
+    def get(self, k):
+        k %= self.n
         return self.A[k], self.codes[k], self.scales[k]
 
 
-def run_kernel(kq, kind, s: Sets, stream):
-    A, c, sc = s.next()
+def run_kernel(kq, kind, s: Sets, stream, k=None):
+    A, c, sc = s.next() if k is None else s.get(k)
     if kind == "fused":
         kq.transform_quantize_mxfp4(A, s.factors, codes=c, scales=sc, stream=stream)
     elif kind == "smoothquant":
@@ -112,6 +126,41 @@ def time_kernel(torch, kq, kind, sets, steps, warmup):
         d = np.array([a.elapsed_time(b) for a, b in ev[si]]) * 1e3  # microseconds
         per.append(d)
     return wall_ms, per
+
+
+def time_step_graphs(torch, kq, kind, sets, steps, warmup):
+    """Wall time per step with each step replayed as one captured HIP graph.
+
+    One graph per rotation index r (the step's launches on buffer set r of every
+    tensor), replayed in turn, so the rotation past the Infinity Cache is kept.
+    Returns ms per step (synchronize on both sides of the timed replays).
+    """
+    nrot = 1
+    for s in sets:
+        nrot = nrot * s.n // math.gcd(nrot, s.n)
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one eager pass on the capture stream first
+        for r in range(nrot):
+            for s in sets:
+                run_kernel(kq, kind, s, side, k=r)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(nrot):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in sets:
+                run_kernel(kq, kind, s, torch.cuda.current_stream(), k=r)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % nrot].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % nrot].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
 
 
 def summarize(d_us, s: Sets):
@@ -164,8 +213,80 @@ def cpu_baseline(ws, seconds):
             "Gelem_per_s": round(done_elems / t_used / 1e9, 4)}
 
 
+COPY_BYTES = 1 << 30
+COPY_KERNEL = "neg"
+
+
+def copy_calibration():
+    """A plain streaming kernel of known traffic: y = -x over 1 GiB of fp32, i.e.
+    1 GiB read + 1 GiB written per call (torch's elementwise negation kernel)."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "calls": 10}))
+
+
+def _pmc_rows(d, counter):
+    """(kernel name, grid size, value) per dispatch from a rocprofv3 --pmc csv directory."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                rows.append((r.get("Kernel_Name", ""), int(float(r.get("Grid_Size", 0) or 0)),
+                             float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_json):
+    """Counter-derived HBM traffic of the fused 18432x12288 launch.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
+    counters read for the 1 GiB copy calibration (known bytes / counted bytes).
+    """
+    def largest_kernel(rows, name_part):
+        sel = [r for r in rows if name_part in r[0]]
+        grid = max(r[1] for r in sel)
+        vals = [r[2] for r in sel if r[1] == grid]
+        return sum(vals) / len(vals), len(vals), sel[0][0], grid
+    f_fused, n_f, kname, grid = largest_kernel(_pmc_rows(fetch_dir, "FETCH_SIZE"), "bf16_quad_kernel<2")
+    w_fused, n_w, _, _ = largest_kernel(_pmc_rows(write_dir, "WRITE_SIZE"), "bf16_quad_kernel<2")
+    f_copy, n_cf, cname, _ = largest_kernel(_pmc_rows(cfetch_dir, "FETCH_SIZE"), COPY_KERNEL)
+    w_copy, n_cw, _, _ = largest_kernel(_pmc_rows(cwrite_dir, "WRITE_SIZE"), COPY_KERNEL)
+    kf = COPY_BYTES / (f_copy * 1024.0)
+    kw = COPY_BYTES / (w_copy * 1024.0)
+    fetch_b = f_fused * 1024.0 * kf
+    write_b = w_fused * 1024.0 * kw
+    alg = 18432 * 12288 * BYTES_PER_ELEM
+    out = {"kernel": kname, "grid_size": grid, "dispatches": [n_f, n_w],
+           "fetch_kib_per_launch": round(f_fused, 1), "write_kib_per_launch": round(w_fused, 1),
+           "copy_kernel": cname, "copy_fetch_kib": round(f_copy, 1), "copy_write_kib": round(w_copy, 1),
+           "scale_fetch": round(kf, 4), "scale_write": round(kw, 4),
+           "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
+           "bytes_per_launch": round(fetch_b + write_b),
+           "algorithmic_bytes_per_launch": round(alg),
+           "traffic_over_algorithmic": round((fetch_b + write_b) / alg, 4),
+           "source_digest": source_digest()}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the quantizer needs no collectives); "
               "run with --gpus 1", file=sys.stderr)
@@ -177,18 +298,24 @@ def main():
 
     kq.lib()
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
-    log("generating inputs " + " ".join(WORKLOAD))
-    ws = [synth.workload(n) for n in WORKLOAD]
+    names = [n for n in WORKLOAD if args.tensor is None or n.endswith("x%d" % args.tensor)]
+    log("generating inputs " + " ".join(names))
+    ws = [synth.workload(n) for n in names]
     sets = [Sets(torch, w) for w in ws]
     log("buffer sets per tensor: %s" % [s.n for s in sets])
     kinds = [args.only] if args.only else ["fused", "smoothquant", "quantize"]
     res = {}
     for kind in kinds:
-        log("timing %s: %d warmup + %d steps" % (kind, args.warmup, args.steps))
-        wall_ms, per = time_kernel(torch, kq, kind, sets, args.steps, args.warmup)
-        res[kind] = {"wall_ms_per_step": wall_ms, "per_tensor": [summarize(d, s) for d, s in zip(per, sets)],
+        log("timing %s: %d warmup + %d steps, eager launches with HIP events" % (kind, args.warmup, args.steps))
+        eager_ms, per = time_kernel(torch, kq, kind, sets, args.steps, args.warmup)
+        wall_ms = eager_ms
+        if not args.eager:
+            log("timing %s: %d warmup + %d steps, one HIP graph per step" % (kind, args.warmup, args.steps))
+            wall_ms = time_step_graphs(torch, kq, kind, sets, args.steps, args.warmup)
+        res[kind] = {"wall_ms_per_step": wall_ms, "eager_ms_per_step": eager_ms,
+                     "per_tensor": [summarize(d, s) for d, s in zip(per, sets)],
                      "per_tensor_mean_us": [float(d.mean()) for d in per]}
-        log("%s: %.4f ms/step; %s" % (kind, wall_ms, res[kind]["per_tensor"]))
+        log("%s: %.4f ms/step (eager %.4f); %s" % (kind, wall_ms, eager_ms, res[kind]["per_tensor"]))
     head = res[kinds[0]]
     step_bytes = sum(s.bytes for s in sets)
     step_elems = sum(s.elems for s in sets)
@@ -207,6 +334,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "step_launch": "eager" if args.eager else "hip_graph",
+        "eager_ms_per_step": round(head["eager_ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -440,14 +440,16 @@ kq_status launched() {
     return KQ_OK;
 }
 
-// Launch shape of the bf16 quad kernels (column strips, row tiles of 64 / CB
-// rows, U rows' loads in flight, non-temporal loads). Workgroups are kept
-// short: the quantizers walk 2 row tiles, the transform 8 (its per-block setup
-// is amortized over more rows).
+// Launch shape of the bf16 quad kernels: column strips of 16 blocks, row tiles
+// of 4 rows, non-temporal loads. Workgroups are kept short, which the HBM
+// system rewards: the quantizers walk 2 row tiles (both loads in flight), the
+// transform 8 row tiles, 4 at a time (its per-block setup is amortized over
+// more rows). Chosen by sweeping tile counts, unroll depth, prefetching and
+// both mappings on the 18432 x 3072 and 18432 x 12288 shapes.
 template <int MODE, bool DEBUG>
 kq_status launch_quad(const uint16_t *A, int64_t m, int64_t d, int64_t lda, const float *params,
                       uint8_t *codes, uint8_t *scales, float *ydbg, kq_stream_t stream) {
-    constexpr int U = 2;
+    constexpr int U = MODE == kq::kKron ? 4 : 2;
     const int64_t iters = MODE == kq::kKron ? 8 : 2;
     kq::Geom g;
     unsigned nwg;

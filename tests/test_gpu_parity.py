@@ -300,6 +300,47 @@ def test_fused_tiny_and_mixed_magnitudes(torch_dev, kq, orc, form):
     print("[parity] tiny %s %s" % (form, rep), flush=True)
 
 
+@pytest.mark.parametrize("kind", ["fused", "smoothquant", "quantize"])
+def test_hip_graph_replays_match_eager(torch_dev, kq, kind):
+    """The kernels inside a captured HIP graph (as bench.py replays them): every
+    replay, with eager work and synchronizations in between, writes the eager bytes."""
+    torch = torch_dev
+    case("hip graph replay " + kind)
+    w = workload("pixart_attn_4096x1152")
+    A = dev_bf16(torch, w.A)
+    fac = torch.from_numpy(w.factors).cuda()
+    inv = torch.from_numpy(w.inv_scale).cuda()
+
+    def call(codes=None, scales=None):
+        if kind == "fused":
+            return kq.transform_quantize_mxfp4(A, fac, codes=codes, scales=scales)
+        if kind == "smoothquant":
+            return kq.smoothquant_quantize_mxfp4(A, inv, codes=codes, scales=scales)
+        return kq.quantize_mxfp4(A, codes=codes, scales=scales)
+
+    ref_c, ref_s = call()
+    torch.cuda.synchronize()
+    codes = torch.empty_like(ref_c)
+    scales = torch.empty_like(ref_s)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(codes, scales)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(codes, scales)
+    for rep in range(3):
+        codes.zero_()
+        scales.zero_()
+        other_c, _ = kq.quantize_mxfp4(A)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(codes, ref_c) and torch.equal(scales, ref_s), "replay %d" % rep
+        assert other_c.shape == ref_c.shape
+
+
 def test_empty_inputs(torch_dev, kq):
     torch = torch_dev
     case("empty inputs")
