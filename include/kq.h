@@ -120,6 +120,24 @@ kq_status kq_quantize_mxfp4_f32(const float *X, int64_t m, int64_t d, int64_t ld
 kq_status kq_inverse_fold_weights(const float *W, int64_t o, int64_t d, const float *factors,
                                   float *W_folded, kq_stream_t stream);
 
+/*
+ * W4A4 GEMM on MXFP4 operands (the downstream product of Eq. 2,
+ * Q(A T) Q(W T^{-T})^T, used to check the quantizer's output end to end):
+ *   O[i][j] = sum_k deq(A)[i][k] * deq(W)[j][k],  deq(code, scale) = E2M1(code) * 2^(scale - 127),
+ * fp32 accumulation on gfx950's scaled FP4 matrix instructions.
+ *   codes_a   device, [m][k/2] bytes (layout of kq_quantize_mxfp4), 16-byte aligned
+ *   scales_a  device, [m][k/32]
+ *   codes_w   device, [n][k/2] bytes (e.g. kq_quantize_mxfp4_f32 of the folded weights), 16-byte aligned
+ *   scales_w  device, [n][k/32]
+ *   O         device, fp32 [m][ldo], ldo >= n; written, not accumulated into
+ * k must be a multiple of 32 (KQ_ERR_SHAPE) and k/2 a multiple of 16 (KQ_ERR_ALIGN).
+ * Summation order inside the matrix instruction is the hardware's; results
+ * agree with an fp64 sum of the same dequantized products to fp32 rounding.
+ */
+kq_status kq_mxfp4_gemm(const uint8_t *codes_a, const uint8_t *scales_a, const uint8_t *codes_w,
+                        const uint8_t *scales_w, int64_t m, int64_t n, int64_t k, float *O, int64_t ldo,
+                        kq_stream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *kq_status_string(kq_status s);
 

@@ -27,6 +27,7 @@ EXPORTS = (
     "kq_smoothquant_quantize_mxfp4",
     "kq_quantize_mxfp4_f32",
     "kq_inverse_fold_weights",
+    "kq_mxfp4_gemm",
     "kq_status_string",
     "kq_last_hip_error",
     "kq_factors_from_lu",
@@ -59,6 +60,7 @@ def lib():
             "kq_quantize_mxfp4_f32": [p, i64, i64, i64, p, p, p],
             "kq_inverse_fold_weights": [p, i64, i64, p, p, p],
             "kq_factors_from_lu": [p, i64, p],
+            "kq_mxfp4_gemm": [p, p, p, p, i64, i64, i64, p, i64, p],
         }.items():
             fn = getattr(L, name)
             fn.argtypes = args
@@ -199,6 +201,30 @@ def inverse_fold_weights(W, factors, out=None, stream=None):
         raise ValueError("out must be a contiguous fp32 tensor shaped like W")
     _check("kq_inverse_fold_weights",
            lib().kq_inverse_fold_weights(_p(W), o, d, _p(factors), _p(out), _stream_ptr(stream)))
+    return out
+
+
+def mxfp4_gemm(codes_a, scales_a, codes_w, scales_w, out=None, stream=None):
+    """O = deq(A) deq(W)^T in fp32 from MXFP4 operands (codes [rows][k/2], scales [rows][k/32])."""
+    torch = _torch()
+    for t, nm in ((codes_a, "codes_a"), (scales_a, "scales_a"), (codes_w, "codes_w"), (scales_w, "scales_w")):
+        _dev(t, nm, (torch.uint8,))
+        if not t.is_contiguous():
+            raise ValueError(nm + " must be contiguous")
+    m, kb = codes_a.shape
+    n = codes_w.shape[0]
+    k = kb * 2
+    if tuple(codes_w.shape) != (n, kb) or tuple(scales_a.shape) != (m, k // 32) or \
+            tuple(scales_w.shape) != (n, k // 32):
+        raise ValueError("operand shapes do not match")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=codes_a.device)
+    _dev(out, "out", (torch.float32,))
+    if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
+        raise ValueError("out must be fp32 [m][n] with unit column stride")
+    _check("kq_mxfp4_gemm",
+           lib().kq_mxfp4_gemm(_p(codes_a), _p(scales_a), _p(codes_w), _p(scales_w), m, n, k, _p(out),
+                               out.stride(0), _stream_ptr(stream)))
     return out
 
 

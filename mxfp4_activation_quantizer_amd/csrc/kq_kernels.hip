@@ -321,6 +321,80 @@ __global__ __launch_bounds__(kThreads) void f32_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// W4A4 GEMM on MXFP4 operands: O[i][j] = sum_k deq(A)[i][k] deq(W)[j][k]
+// (Eq. 2's Q(A T) Q(W T^{-T})^T), fp32 accumulation on
+// v_mfma_scale_f32_16x16x128_f8f6f4 with both operands in E2M1. Lane l of a
+// wave supplies row l % 16 and the 32 consecutive k of group l / 16 (16 code
+// bytes) with that group's E8M0 byte as its scale, which is exactly the MX
+// layout of the codes/scales arrays; it receives O rows 4 (l / 16) + t, column
+// l % 16. A workgroup of 4 waves computes a 64 x 64 tile, each wave 32 x 32
+// (2 x 2 MFMA tiles), walking k in steps of 128. Rows and columns past m or n
+// read zero codes and are not stored; k must be a multiple of 32, and k
+// groups past k read zero codes.
+// ---------------------------------------------------------------------------
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+struct GemmGeom {
+    int64_t m, n, k, ldo, tiles_n;
+};
+
+__device__ __forceinline__ i32x8_t load_fp4_operand(const uint8_t *codes, int64_t row, int64_t nrows,
+                                                     int64_t kbytes, int64_t kbyte0, int &scale,
+                                                     const uint8_t *scales, int64_t kblocks, int64_t kblk) {
+    i32x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
+    scale = 127;
+    if (row < nrows && kbyte0 < kbytes) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(codes + row * kbytes + kbyte0);
+        v[0] = (int)q.x; v[1] = (int)q.y; v[2] = (int)q.z; v[3] = (int)q.w;
+        scale = scales[row * kblocks + kblk];
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(kThreads) void mxfp4_gemm_kernel(
+    const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const uint8_t *__restrict__ cw,
+    const uint8_t *__restrict__ sw, GemmGeom g, float *__restrict__ O) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t tm = blockIdx.x / g.tiles_n, tn = blockIdx.x % g.tiles_n;
+    const int64_t row0 = tm * 64 + (wave >> 1) * 32, col0 = tn * 64 + (wave & 1) * 32;
+    const int r = lane & 15, grp = lane >> 4;
+    const int64_t kbytes = g.k / 2, kblocks = g.k / 32;
+    floatx4_t acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int64_t k0 = 0; k0 < g.k; k0 += 128) {
+        const int64_t kb0 = k0 / 2 + grp * 16, kblk = k0 / 32 + grp;
+        i32x8_t av[2], bv[2];
+        int as[2], bs[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+            av[a] = load_fp4_operand(ca, row0 + a * 16 + r, g.m, kbytes, kb0, as[a], sa, kblocks, kblk);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            bv[b] = load_fp4_operand(cw, col0 + b * 16 + r, g.n, kbytes, kb0, bs[b], sw, kblocks, kblk);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[a], bv[b], acc[a][b], 4, 4, 0,
+                                                                             as[a], 0, bs[b]);
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int64_t col = col0 + b * 16 + r;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int64_t row = row0 + a * 16 + grp * 4 + t;
+                if (row < g.m && col < g.n) O[row * g.ldo + col] = acc[a][b][t];
+            }
+        }
+}
+
 }  // namespace kq
 
 // ===========================================================================
@@ -560,6 +634,21 @@ kq_status kq_inverse_fold_weights(const float *W, int64_t o, int64_t d, const fl
     if (!make_geom_flat(o, d, d, 1, 256 * 8, g, nwg)) return KQ_ERR_SHAPE;
     hipLaunchKernelGGL((kq::f32_kernel<kq::kKron>), dim3(nwg), dim3(kq::kThreads), 0,
                        (hipStream_t)stream, W, g, factors, nullptr, nullptr, W_folded);
+    return launched();
+}
+
+kq_status kq_mxfp4_gemm(const uint8_t *codes_a, const uint8_t *scales_a, const uint8_t *codes_w,
+                        const uint8_t *scales_w, int64_t m, int64_t n, int64_t k, float *O, int64_t ldo,
+                        kq_stream_t stream) {
+    if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || ldo < n) return KQ_ERR_SHAPE;
+    if (m == 0 || n == 0) return KQ_OK;
+    if (!codes_a || !scales_a || !codes_w || !scales_w || !O) return KQ_ERR_NULL;
+    if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || (k / 2) % 16 != 0) return KQ_ERR_ALIGN;
+    const int64_t tiles_m = (m + 63) / 64, tiles_n = (n + 63) / 64;
+    if (tiles_m * tiles_n > 0x7FFFFFFF || m > INT64_MAX / 4 / (ldo > 0 ? ldo : 1)) return KQ_ERR_SHAPE;
+    kq::GemmGeom g{m, n, k, ldo, tiles_n};
+    hipLaunchKernelGGL(kq::mxfp4_gemm_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kq::kThreads), 0,
+                       (hipStream_t)stream, codes_a, scales_a, codes_w, scales_w, g, O);
     return launched();
 }
 

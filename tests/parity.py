@@ -4,8 +4,11 @@ Quantize-only, SmoothQuant and fp32 quantize: codes and scales bit-exact.
 
 Fused transform + quantize (tolerances as the build states them):
   1. per block, max |y_gpu - y_ref| <= 1e-5 * ||y_ref||_2 (y_ref in float64);
-  2. the GPU's codes and scales equal the oracle's quantization of the GPU's
-     own y (bit-exact, except that code 0x8 (-0) and 0x0 (+0) are equivalent);
+  2. the GPU's codes and scales are the quantization of the GPU's own y: the
+     scale byte follows max|y_gpu| and each code is the nearest-even E2M1 level
+     of |y_gpu| / 2^e with the sign of y_gpu (codes 0x8 and 0x0 equivalent).
+     This is checked here with numpy on the GPU's output; the oracle itself only
+     ever sees the seeded inputs;
   3. against the oracle's quantization of y_ref: at most 1e-4 of the elements
      differ, each by at most one E2M1 level, and only where a rounding
      boundary lies between y_ref / 2^e and y_gpu / 2^e (a rounding tie). A
@@ -40,6 +43,39 @@ def assert_codes_equal_mod_signed_zero(c1, c2, what=""):
     assert bad.size == 0, "%s: %d nibbles differ, first at %s" % (what, len(bad), bad[:5].tolist())
 
 
+def expected_levels(v: np.ndarray) -> np.ndarray:
+    """E2M1 magnitude index of v >= 0 (exact float64): count of rounding boundaries
+    passed; at a boundary between levels i and i+1 the even one wins, i.e. ties at
+    0.75, 1.75 and 3.5 go up and ties at 0.25, 1.25, 2.5 and 5 stay down."""
+    idx = np.zeros(v.shape, dtype=np.int8)
+    for i, b in enumerate(BOUNDS):
+        up_on_tie = (i + 1) % 2 == 0
+        idx += (v > b) | ((v == b) & up_on_tie)
+    return idx
+
+
+def check_self_consistent(codes_g, scales_g, y_g, rows_per_chunk=2048):
+    """Rule 2 on the GPU's own y (numpy; no oracle call)."""
+    m, d = y_g.shape
+    nblk = d // 32
+    for r0 in range(0, m, rows_per_chunk):
+        y = y_g[r0:r0 + rows_per_chunk].astype(np.float64)
+        mm = y.shape[0]
+        yb = y.reshape(mm, nblk, 32)
+        amax = np.abs(yb).max(axis=2)
+        _, ex = np.frexp(amax)  # amax = f 2^ex, 0.5 <= f < 1, so floor(log2 amax) = ex - 1
+        e = np.where(amax == 0, -127, np.clip(ex - 3, -127, 127))
+        sg = scales_g[r0:r0 + mm]
+        assert np.array_equal(sg.astype(np.int64), e + 127), "scale not implied by max|y_gpu|"
+        v = np.abs(yb) * np.exp2(-e.astype(np.float64))[..., None]
+        lvl = expected_levels(v).reshape(mm, d)
+        sign = np.signbit(y).astype(np.int8) * 8
+        want = np.where(lvl == 0, 0, lvl | sign)
+        got = zero_equiv(unpack(codes_g[r0:r0 + mm]))
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, "code not the quantization of y_gpu at %s" % (bad[:5] + [r0, 0]).tolist()
+
+
 def fused_report(orc, A_rows, factors, codes_g, scales_g, y_g, y_ref=None):
     """Apply rules 1-3 to rows already gathered from a GPU run; returns stats."""
     m, d = A_rows.shape[0], y_g.shape[1]
@@ -55,9 +91,7 @@ def fused_report(orc, A_rows, factors, codes_g, scales_g, y_g, y_ref=None):
     assert not bad1.any(), "y error above 1e-5 * block norm in %d blocks; worst ratio %g" % (
         bad1.sum(), (err / np.maximum(nrm, 1e-300)).max())
     # rule 2
-    cq, sq = orc.quantize_f64(yg)
-    assert np.array_equal(sq, scales_g), "scales differ from Q(y_gpu) in %d blocks" % (sq != scales_g).sum()
-    assert_codes_equal_mod_signed_zero(cq, codes_g, "codes vs Q(y_gpu)")
+    check_self_consistent(codes_g, scales_g, y_g)
     # rule 3
     cr, sr = orc.quantize_f64(y_ref)
     scale_tie = sr != scales_g

@@ -60,6 +60,11 @@ GOOD = P(0x10000)  # never dereferenced: every case below fails before a launch
     ("kq_inverse_fold_weights", (GOOD, 4, 64, None, GOOD, None), kq.KQ_ERR_NULL),
     ("kq_inverse_fold_weights", (GOOD, 4, 64, GOOD, P(0x10004), None), kq.KQ_ERR_ALIGN),
     ("kq_inverse_fold_weights", (None, 0, 64, None, None, None), kq.KQ_OK),
+    ("kq_mxfp4_gemm", (GOOD, GOOD, GOOD, GOOD, 4, 4, 48, GOOD, 4, None), kq.KQ_ERR_SHAPE),
+    ("kq_mxfp4_gemm", (GOOD, GOOD, GOOD, GOOD, 4, 4, 64, GOOD, 3, None), kq.KQ_ERR_SHAPE),
+    ("kq_mxfp4_gemm", (GOOD, None, GOOD, GOOD, 4, 4, 64, GOOD, 4, None), kq.KQ_ERR_NULL),
+    ("kq_mxfp4_gemm", (P(0x10008), GOOD, GOOD, GOOD, 4, 4, 64, GOOD, 4, None), kq.KQ_ERR_ALIGN),
+    ("kq_mxfp4_gemm", (None, None, None, None, 0, 4, 64, None, 4, None), kq.KQ_OK),
 ])
 def test_host_argument_checks(L, fn, args, status):
     assert getattr(L, fn)(*args) == status

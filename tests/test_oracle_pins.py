@@ -381,3 +381,13 @@ def test_dequantize_and_gemm(orc):
     assert np.array_equal(O, da @ dw.T) or np.allclose(O, da @ dw.T, rtol=1e-15, atol=0)
     O2 = orc.gemm_dequant(ca, sa, cw, sw, 64, rows=[4, 1])
     assert np.array_equal(O2, O[[4, 1]])
+
+
+def test_parity_rule2_levels_match_oracle(orc):
+    """The test-side level rule used on GPU output agrees with the oracle's quantizer."""
+    from tests import parity
+    vals = np.array([k / 64 for k in range(512)] + [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5, 7.9])
+    vals = np.concatenate([vals, np.nextafter(vals, 0), np.nextafter(vals, 10)])
+    got = parity.expected_levels(vals)
+    want = np.array([orc.e2m1_round_index(v) for v in vals])
+    assert np.array_equal(got, want)
