@@ -51,6 +51,8 @@ def parse():
                     help="time only one kernel (for profiler runs)")
     ap.add_argument("--eager", action="store_true",
                     help="time steps as eager launches instead of replaying one HIP graph per step")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other configs, the MFMA form, the fold and the W4A4 GEMM timings")
     ap.add_argument("--tensor", type=int, choices=[3072, 12288], default=None,
                     help="time only the tensor with this d (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -161,6 +163,76 @@ def time_step_graphs(torch, kq, kind, sets, steps, warmup):
         graphs[i % nrot].replay()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def _events_us(torch, fn, reps, warmup):
+    """Per-call durations (microseconds) of fn() by HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+
+
+def extras(torch, kq, synth, flux_sets, reps=100, warmup=20):
+    """Context measurements kept beside the headline step (same rotation rules):
+    the PixArt-shaped inputs, the MFMA form of the transform on the FLUX inputs,
+    the weight fold and fp32 quantizer on 3072 x 3072 weights, and the W4A4 GEMM."""
+    out = {"other_configs": {}}
+    for name in ("pixart_attn_4096x1152", "pixart_ffn_8192x4608"):
+        w = synth.workload(name)
+        s = Sets(torch, w)
+        per = {}
+        for kind in ("fused", "smoothquant", "quantize"):
+            _, d = time_kernel(torch, kq, kind, [s], reps, warmup)
+            per[kind] = summarize(d[0], s)
+        out["other_configs"][name] = per
+        log("%s: %s" % (name, per))
+        del s
+    old = os.environ.get("KQ_TRANSFORM_FORM")
+    try:
+        for form in ("mfma", "mfma_lds"):
+            os.environ["KQ_TRANSFORM_FORM"] = form
+            _, d = time_kernel(torch, kq, "fused", flux_sets, reps, warmup)
+            out["fused_%s_form" % form] = [summarize(x, s) for x, s in zip(d, flux_sets)]
+            log("%s form: %s" % (form, out["fused_%s_form" % form]))
+    finally:
+        if old is None:
+            del os.environ["KQ_TRANSFORM_FORM"]
+        else:
+            os.environ["KQ_TRANSFORM_FORM"] = old
+    # weight side: fold and fp32 quantize of a 3072 x 3072 fp32 weight
+    W = torch.from_numpy(synth.weights(3072, 3072, 1004)).cuda()
+    fac = flux_sets[0].factors
+    Wf = torch.empty_like(W)
+    d_fold = _events_us(torch, lambda: kq.inverse_fold_weights(W, fac, out=Wf), reps, warmup)
+    cw, sw = kq.quantize_mxfp4_f32(Wf)
+    d_q32 = _events_us(torch, lambda: kq.quantize_mxfp4_f32(Wf, codes=cw, scales=sw), reps, warmup)
+    nW = W.numel()
+    fold_b, q32_b = nW * 8.0, nW * (4 + 0.5 + 1 / 32)
+    out["weight_fold_3072x3072"] = {
+        "median_us": round(float(np.median(d_fold)), 3),
+        "GBps": round(fold_b / (np.median(d_fold) * 1e-6) / 1e9, 1),
+        "quantize_f32_median_us": round(float(np.median(d_q32)), 3),
+        "quantize_f32_GBps": round(q32_b / (np.median(d_q32) * 1e-6) / 1e9, 1),
+        "note": "small (37.7 MB) and L2/Infinity-Cache resident across repeats; offline step"}
+    # W4A4 GEMM on the FLUX 18432 x 3072 activations and the folded weights
+    A, ca, sa = flux_sets[0].get(0)
+    kq.transform_quantize_mxfp4(A, fac, codes=ca, scales=sa)
+    O = torch.empty((A.shape[0], 3072), dtype=torch.float32, device="cuda")
+    d_g = _events_us(torch, lambda: kq.mxfp4_gemm(ca, sa, cw, sw, out=O), 20, 3)
+    flops = 2.0 * A.shape[0] * 3072 * 3072
+    med = float(np.median(d_g))
+    out["w4a4_gemm_18432x3072x3072"] = {"median_us": round(med, 1),
+                                         "TFLOPs": round(flops / (med * 1e-6) / 1e12, 1),
+                                         "pct_fp4_peak": round(100 * flops / (med * 1e-6) / 10.1e15, 2)}
+    log("weight side / gemm: %s %s" % (out["weight_fold_3072x3072"], out["w4a4_gemm_18432x3072x3072"]))
+    return out
 
 
 def summarize(d_us, s: Sets):
@@ -349,12 +421,14 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "kq::bf16_quant_kernel (%s) on %dx%d" % (kinds[0], sets[big].m, sets[big].d)},
+                     "kernel": "kq::bf16_quad_kernel (%s) on %dx%d" % (kinds[0], sets[big].m, sets[big].d)},
         "kernels": {k: v["per_tensor"] for k, v in res.items()},
     }
     if "fused" in res and "smoothquant" in res:
         out["fused_vs_smoothquant_speedup"] = round(
             res["smoothquant"]["wall_ms_per_step"] / res["fused"]["wall_ms_per_step"], 3)
+    if not args.only and not args.no_extras:
+        out["extras"] = extras(torch, kq, synth, sets)
     if args.cpu_seconds > 0 and not args.only:
         log("CPU oracle baseline (>= %.0f s)" % args.cpu_seconds)
         out["cpu_baseline"] = cpu_baseline(ws, args.cpu_seconds)

@@ -271,6 +271,83 @@ __global__ __launch_bounds__(kThreads) void kron_mfma_kernel(
     }
 }
 
+// MFMA form with LDS staging. A workgroup (4 waves) owns a strip of 16
+// consecutive blocks and walks `iters` tiles of 16 tokens. Each tile (16 rows x
+// 1 KB of bf16) is loaded with fully coalesced 16-byte loads (one 1 KB row per
+// 64 lanes) into LDS, double-buffered so the next tile's loads are in flight
+// while this one is transformed; wave w then reads the MFMA operand of its
+// blocks 4w .. 4w+3 (token l % 16, channels 8 (l / 16) .. +7) from LDS. LDS rows
+// are padded by 16 bytes, so the 16 lanes of a read phase hit distinct banks.
+struct LGeom {
+    int64_t m, lda, d;
+    int nblk, nstrip, iters;
+};
+
+template <bool DEBUG>
+__global__ __launch_bounds__(kThreads) void kron_mfma_lds_kernel(
+    const uint16_t *__restrict__ A, LGeom g, const float *__restrict__ factors,
+    uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ ydbg) {
+    __shared__ uint4 xs[2][16][65];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
+    const int strip = (int)(blockIdx.x % (unsigned)g.nstrip);
+    const int64_t tile0 = (int64_t)(blockIdx.x / (unsigned)g.nstrip) * g.iters;
+    const int jb0 = strip * 16 + wave * 4;
+
+    KSplit S[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ksplit_setup(factors + (int64_t)(jb0 + q) * 20, lane, S[q]);
+
+    // tile t: thread tid moves rows 4 r + tid / 64 (r < 4), 16-byte column tid % 64
+    const uint16_t *Astrip = A + (int64_t)strip * 512 + (tid & 63) * 8;
+    auto load_tile = [&](int64_t t, uint4 (&v)[4]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t tok = t * 16 + 4 * r + (tid >> 6);
+            v[r] = tok < g.m ? load_stream(reinterpret_cast<const uint4 *>(Astrip + tok * g.lda), true)
+                             : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_tile = [&](int buf, const uint4 (&v)[4]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xs[buf][4 * r + (tid >> 6)][tid & 63] = v[r];
+    };
+
+    uint4 v[4];
+    if (tile0 * 16 >= g.m) return;  // uniform within the workgroup
+    load_tile(tile0, v);
+    store_tile(0, v);
+    __syncthreads();
+    for (int it = 0; it < g.iters; ++it) {
+        const int64_t t = tile0 + it;
+        if (t * 16 >= g.m) break;  // uniform within the workgroup
+        const bool more = it + 1 < g.iters && (t + 1) * 16 < g.m;
+        if (more) load_tile(t + 1, v);
+        const int buf = it & 1;
+        const int64_t tok = t * 16 + (lane & 15);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int jb = jb0 + q;
+            const uint4 x = xs[buf][lane & 15][(wave * 4 + q) * 4 + grp];
+            float y[8];
+            kron_mfma8(S[q], x, y);  // all 64 lanes take part
+            const float amax = max_xor16_xor32(absmax8(y));
+            const uint32_t sbyte = e8m0_byte(amax);
+            const uint32_t packed = cvt8_f32(y, cvt_scale(sbyte));
+            if (tok < g.m) {
+                if (DEBUG) {
+                    float4 *o = reinterpret_cast<float4 *>(ydbg + tok * g.d + (int64_t)jb * 32 + grp * 8);
+                    o[0] = make_float4(y[0], y[1], y[2], y[3]);
+                    o[1] = make_float4(y[4], y[5], y[6], y[7]);
+                }
+                *reinterpret_cast<uint32_t *>(codes + tok * (g.d / 2) + (int64_t)jb * 16 + grp * 4) = packed;
+                if (grp == 0) scales[tok * g.nblk + jb] = (uint8_t)sbyte;
+            }
+        }
+        if (more) store_tile(buf ^ 1, v);
+        __syncthreads();
+    }
+}
+
 // fp32 input, quad layout: quantize (MODE kQuantOnly) or, with MODE kKron,
 // write X . (K^(j))^{-T} (the weight fold) to `out` instead of quantizing.
 template <int MODE>
@@ -544,20 +621,57 @@ kq_status launch_mfma(const uint16_t *A, int64_t m, int64_t d, int64_t lda, cons
     return launched();
 }
 
-// Which form of the transform the fused entry point runs: five in-register
-// 2x2 stages (shear form, default) or the materialized 32x32 block on MFMA.
-// KQ_TRANSFORM_FORM=mfma selects the latter (read at every call). Measured on
-// the FLUX shapes the MFMA form is bound by its 16-token tiles' strided
-// accesses, so it is kept for comparison only.
-bool use_mfma() {
+// LDS-staged MFMA form: strips of 16 blocks (nblk % 16 == 0), `iters` tiles of
+// 16 tokens per workgroup.
+bool make_lgeom(int64_t m, int64_t d, int64_t lda, int64_t iters_per_wg, kq::LGeom &g, unsigned &nwg) {
+    g.m = m;
+    g.d = d;
+    g.lda = lda;
+    g.nblk = (int)(d / 32);
+    if (g.nblk % 16 != 0) return false;
+    g.nstrip = g.nblk / 16;
+    const int64_t tiles = (m + 15) / 16;
+    int64_t iters = iters_per_wg < 1 ? 1 : iters_per_wg;
+    if (iters > tiles) iters = tiles;
+    const int64_t nslab = (tiles + iters - 1) / iters;
+    const int64_t total = nslab * g.nstrip;
+    if (total > 0x7FFFFFFF || iters > 0x7FFFFFFF) return false;
+    g.iters = (int)iters;
+    nwg = (unsigned)total;
+    return true;
+}
+
+template <bool DEBUG>
+kq_status launch_mfma_lds(const uint16_t *A, int64_t m, int64_t d, int64_t lda, const float *factors,
+                          uint8_t *codes, uint8_t *scales, float *ydbg, kq_stream_t stream) {
+    kq::LGeom g;
+    unsigned nwg;
+    if (!make_lgeom(m, d, lda, 8, g, nwg)) return KQ_ERR_SHAPE;
+    hipLaunchKernelGGL((kq::kron_mfma_lds_kernel<DEBUG>), dim3(nwg), dim3(kq::kThreads), 0,
+                       (hipStream_t)stream, A, g, factors, codes, scales, ydbg);
+    return launched();
+}
+
+// Which form of the transform the fused entry point runs (KQ_TRANSFORM_FORM,
+// read at every call): "butterfly" = five in-register 2x2 stages in shear
+// form (default); "mfma" = the materialized 32x32 block on MFMA, operands
+// loaded directly; "mfma_lds" = the same through LDS-staged row-major tiles
+// (needs d a multiple of 512, else the butterfly runs).
+enum Form { kFormButterfly, kFormMfma, kFormMfmaLds };
+Form transform_form() {
     const char *v = getenv("KQ_TRANSFORM_FORM");
-    return v && strcmp(v, "mfma") == 0;
+    if (v && strcmp(v, "mfma") == 0) return kFormMfma;
+    if (v && strcmp(v, "mfma_lds") == 0) return kFormMfmaLds;
+    return kFormButterfly;
 }
 
 template <bool DEBUG>
 kq_status launch_fused(const uint16_t *A, int64_t m, int64_t d, int64_t lda, const float *factors,
                        uint8_t *codes, uint8_t *scales, float *ydbg, kq_stream_t stream) {
-    if (!use_mfma()) return launch_quad<kq::kKron, DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
+    const Form f = transform_form();
+    if (f == kFormMfmaLds && (d / 32) % 16 == 0)
+        return launch_mfma_lds<DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
+    if (f != kFormMfma) return launch_quad<kq::kKron, DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
     if ((d / 32) % 2 == 0)
         return launch_mfma<2, DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
     return launch_mfma<1, DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);

@@ -102,7 +102,7 @@ def test_smoothquant_bit_exact(torch_dev, kq, orc, name):
 # fused Kronecker transform + quantize
 # ---------------------------------------------------------------------------
 
-@pytest.fixture(params=["mfma", "butterfly"])
+@pytest.fixture(params=["butterfly", "mfma", "mfma_lds"])
 def form(request, monkeypatch):
     """Transform form the library runs (read by libkq.so at every call)."""
     monkeypatch.setenv("KQ_TRANSFORM_FORM", request.param)  # "butterfly" is the default form
