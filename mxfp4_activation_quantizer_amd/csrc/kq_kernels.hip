@@ -68,39 +68,30 @@ __device__ __forceinline__ uint4 load_stream(const uint4 *p, bool nt) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Walks this quad's rows row0 + k rstep (k < iters), U rows' loads issued
-// together (PF: the next group's loads are issued before this group is
-// processed), and calls body(q, row) for each row below m. The row test is
-// uniform within a quad, so DPP inside `body` sees all four lanes.
-template <int U, bool NT, bool PF, typename Body>
+// Walks this quad's rows row0 + k rstep (k < iters), issuing U rows' loads
+// together, and calls body(q, row) for each row below m. The row test is
+// uniform within a quad, so DPP inside `body` sees all four lanes. (Issuing
+// the next group's loads before processing this one, with or without raised
+// wave priority, measured slower on the FLUX shapes: it costs registers and
+// occupancy.)
+template <int U, bool NT, typename Body>
 __device__ __forceinline__ void for_rows(const Geom &g, const uint16_t *__restrict__ A, int64_t row0,
                                          int64_t c0, Body body) {
     const int64_t R = g.rstep;
-    auto load_rows = [&](int it, uint4 (&q)[U]) {
+    for (int it = 0; it < g.iters; it += U) {
+        if (row0 + (int64_t)it * R >= g.m) break;
+        uint4 q[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = row0 + (int64_t)(it + u) * R;
             q[u] = row < g.m ? load_stream(reinterpret_cast<const uint4 *>(A + row * g.lda + c0), NT)
                              : make_uint4(0, 0, 0, 0);
         }
-    };
-    uint4 q[U];
-    load_rows(0, q);
-    for (int it = 0; it < g.iters; it += U) {
-        if (row0 + (int64_t)it * R >= g.m) break;
-        const bool more = it + U < g.iters;
-        uint4 qn[U];
-        if (PF && more) load_rows(it + U, qn);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = row0 + (int64_t)(it + u) * R;
             if (row >= g.m) break;
             body(q[u], row);
-        }
-        if (more) {
-            if (!PF) load_rows(it + U, qn);
-#pragma unroll
-            for (int u = 0; u < U; ++u) q[u] = qn[u];
         }
     }
 }
@@ -125,7 +116,7 @@ __device__ __forceinline__ void finish_f32(const float y[8], const Geom &g, int6
 // bf16 input, quad layout: quantize-only (T = I), SmoothQuant (T = diag(inv_scale))
 // or the Kronecker transform (shear form, or the general stages for blocks
 // that do not admit it).
-template <int MODE, bool DEBUG, int U, bool NT, bool PF, int MAP>
+template <int MODE, bool DEBUG, int U, bool NT, int MAP>
 __global__ __launch_bounds__(kThreads) void bf16_quad_kernel(
     const uint16_t *__restrict__ A, Geom g, const float *__restrict__ params,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ ydbg) {
@@ -135,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void bf16_quad_kernel(
     const int64_t c0 = (int64_t)j * 32 + sub * 8;
 
     if (MODE == kQuantOnly) {
-        for_rows<U, NT, PF>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
+        for_rows<U, NT>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
             uint32_t sbyte;
             const uint32_t packed = quantize_quad_bf16(q, sbyte);
             *reinterpret_cast<uint32_t *>(codes + row * (g.d / 2) + (int64_t)j * 16 + sub * 4) = packed;
@@ -147,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void bf16_quad_kernel(
         const float4 b = *reinterpret_cast<const float4 *>(params + c0 + 4);
         sq[0] = a.x; sq[1] = a.y; sq[2] = a.z; sq[3] = a.w;
         sq[4] = b.x; sq[5] = b.y; sq[6] = b.z; sq[7] = b.w;
-        for_rows<U, NT, PF>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
+        for_rows<U, NT>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
             float y[8];
             widen8(q, y);
 #pragma unroll
@@ -175,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void bf16_quad_kernel(
             shear_lane_setup(f, sub, S);
         }
         if (S.ok) {  // one block per quad: uniform within the quad
-            for_rows<U, NT, PF>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
+            for_rows<U, NT>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
                 float y[8];
                 widen8(q, y);
                 shear_apply8(y, S);
@@ -186,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void bf16_quad_kernel(
             load_factors20(params + (int64_t)j * 20, f);
             KronLane L;
             kron_lane_setup(f, sub, L);
-            for_rows<U, NT, PF>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
+            for_rows<U, NT>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
                 float y[8];
                 widen8(q, y);
                 kron_apply8(y, L);
@@ -204,7 +195,7 @@ struct MGeom {
     int nblk, ncg, iters;
 };
 
-template <int NB, bool DEBUG, int U, bool NT, bool PF>
+template <int NB, bool DEBUG, int U, bool NT>
 __global__ __launch_bounds__(kThreads) void kron_mfma_kernel(
     const uint16_t *__restrict__ A, MGeom g, const float *__restrict__ factors,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ ydbg) {
@@ -232,13 +223,10 @@ __global__ __launch_bounds__(kThreads) void kron_mfma_kernel(
         }
     };
 
-    uint4 q[U][NB];
-    load_tiles(0, q);
     for (int it = 0; it < g.iters; it += U) {
         if ((tile0 + it) * 16 >= g.m) break;  // uniform within the wave
-        const bool more = it + U < g.iters;
-        uint4 qn[U][NB];
-        if (PF && more) load_tiles(it + U, qn);
+        uint4 q[U][NB];
+        load_tiles(it, q);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t tok = (tile0 + it + u) * 16 + (lane & 15);
@@ -260,13 +248,6 @@ __global__ __launch_bounds__(kThreads) void kron_mfma_kernel(
                     if (grp == 0) scales[tok * g.nblk + jb] = (uint8_t)sbyte;
                 }
             }
-        }
-        if (more) {
-            if (!PF) load_tiles(it + U, qn);
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) q[u][nb] = qn[u][nb];
         }
     }
 }
@@ -605,7 +586,7 @@ kq_status launch_quad(const uint16_t *A, int64_t m, int64_t d, int64_t lda, cons
     kq::Geom g;
     unsigned nwg;
     if (!make_geom_strip(m, d, lda, U, iters, g, nwg)) return KQ_ERR_SHAPE;
-    hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, DEBUG, U, true, false, kq::kStrip>), dim3(nwg),
+    hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, DEBUG, U, true, kq::kStrip>), dim3(nwg),
                        dim3(kq::kThreads), 0, (hipStream_t)stream, A, g, params, codes, scales, ydbg);
     return launched();
 }
@@ -616,7 +597,7 @@ kq_status launch_mfma(const uint16_t *A, int64_t m, int64_t d, int64_t lda, cons
     kq::MGeom g;
     unsigned nwg;
     if (!make_mgeom(m, d, lda, NB, 2, g, nwg)) return KQ_ERR_SHAPE;
-    hipLaunchKernelGGL((kq::kron_mfma_kernel<NB, DEBUG, 2, false, false>), dim3(nwg), dim3(kq::kThreads), 0,
+    hipLaunchKernelGGL((kq::kron_mfma_kernel<NB, DEBUG, 2, false>), dim3(nwg), dim3(kq::kThreads), 0,
                        (hipStream_t)stream, A, g, factors, codes, scales, ydbg);
     return launched();
 }
