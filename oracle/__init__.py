@@ -18,6 +18,9 @@ What each function follows in the KroQuant paper (arXiv 2607.21446v1):
 - ``inverse_fold``: Eq. 1's W -> W T^{-T}.
 - ``gemm_dequant``: Eq. 2's Q(AT) Q(WT^{-T})^T in float64.
 - ``factors_from_lu``: Eq. 6.
+- ``hadamard_quantize`` / ``hadamard_f64``: the fixed block-Hadamard baselines
+  (Sec. 1; Sec. 3.2 "Hadamard initialization" defines H_n; Sec. 4.4, Table 2's
+  Hadamard-32 row and Table 3's full-width FWHT), then the same quantizer.
 """
 from __future__ import annotations
 
@@ -74,6 +77,10 @@ def _bind(lib):
     lib.kqo_dequantize.argtypes = [p, p, i64, i64, p]
     lib.kqo_gemm_dequant.restype = i32
     lib.kqo_gemm_dequant.argtypes = [p, p, p, p, i64, i64, p, i64, p, i32]
+    lib.kqo_hadamard_quantize.restype = i32
+    lib.kqo_hadamard_quantize.argtypes = [p, i64, i64, i64, i64, p, p, p, i32]
+    lib.kqo_hadamard_f64.restype = i32
+    lib.kqo_hadamard_f64.argtypes = [p, i64, i64, i64, i64, p, i32]
     return lib
 
 
@@ -233,6 +240,27 @@ class Oracle:
         if rc != 0:
             raise MemoryError("oracle gemm")
         return O
+
+    def hadamard_quantize(self, A, n, d=None, want_y=True, want_codes=True):
+        """Each group of n channels times H_n / sqrt(n), then MXFP4."""
+        A = _c(A, np.uint16)
+        m, lda = A.shape
+        d = lda if d is None else d
+        codes, scales = self._out(m, d) if want_codes else (None, None)
+        y = np.empty((m, d), dtype=np.float64) if want_y else None
+        rc = self.lib.kqo_hadamard_quantize(_p(A), m, d, lda, n, _p(codes), _p(scales), _p(y),
+                                            self.nthreads)
+        if rc != 0:
+            raise ValueError("oracle hadamard: n must be a power of two dividing d")
+        return codes, scales, y
+
+    def hadamard_f64(self, X, n):
+        X = _c(X, np.float64)
+        m, d = X.shape
+        y = np.empty((m, d), dtype=np.float64)
+        if self.lib.kqo_hadamard_f64(_p(X), m, d, d, n, _p(y), self.nthreads) != 0:
+            raise ValueError("oracle hadamard: n must be a power of two dividing d")
+        return y
 
 
 _default = None

@@ -19,6 +19,11 @@
  *   Sec. 4.1 "Data format" and Appendix D: MXFP4 E2M1 elements, FP8 E8M0
  *                      block scale, block size 32, per the OCP MX spec.
  *   Appendix D.2       SmoothQuant per-channel vector gamma.
+ *   Sec. 3.2 "Hadamard initialization", Sec. 1, Sec. 4.4 (Table 2's
+ *                      Hadamard-32 row, Table 3's FWHT): the normalized
+ *                      Hadamard matrix of order n = 2^k, the k-fold Kronecker
+ *                      power of [[1,1],[1,-1]]/sqrt(2), applied to each group
+ *                      of n consecutive channels (n = d: full-width transform).
  *
  * Readings taken where the paper is silent (OCP MX v1.0 conventions):
  *   - shared exponent e = floor(log2(max|y|)) - 2 (2 = largest E2M1 exponent),
@@ -444,5 +449,80 @@ int kqo_gemm_dequant(const uint8_t *codes_a, const uint8_t *scales_a, const uint
     gctx c = {codes_a, scales_a, codes_w, scales_w, nout, k, rows, O, Wdq};
     parallel_rows(nrows, nthreads, rows_gemm, &c);
     free(Wdq);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block Hadamard (the fixed-rotation baselines)                             */
+/* ------------------------------------------------------------------------ */
+
+/* Sylvester form of the k-fold Kronecker power of [[1,1],[1,-1]]:
+ * H_n[r][c] = (-1)^popcount(r & c); the normalized matrix divides by sqrt(n).
+ * For each row and each group g of n channels,
+ *     y[g n + c] = (1 / sqrt(n)) * sum_{r = 0..n-1} x[g n + r] H_n[r][c],
+ * summed in float64 with r in order (a dense O(n^2) product per group). */
+static void hadamard_group(const double *x, int64_t n, double inv_sqrt_n, double *y) {
+    for (int64_t col = 0; col < n; ++col) {
+        double s = 0.0;
+        for (int64_t r = 0; r < n; ++r) {
+            if (__builtin_popcountll((unsigned long long)(r & col)) & 1)
+                s -= x[r];
+            else
+                s += x[r];
+        }
+        y[col] = s * inv_sqrt_n;
+    }
+}
+
+typedef struct {
+    const uint16_t *A; /* bf16 bits [m][lda], or NULL */
+    const double *X;   /* fp64 [m][lda], or NULL */
+    int64_t d, lda, n;
+    uint8_t *codes, *scales;
+    double *y_out;
+} hctx;
+
+static void rows_hadamard(void *p, int64_t r0, int64_t r1) {
+    hctx *c = (hctx *)p;
+    double *x = (double *)malloc(sizeof(double) * (size_t)c->d);
+    double *y = (double *)malloc(sizeof(double) * (size_t)c->d);
+    if (!x || !y) {
+        free(x);
+        free(y);
+        return;
+    }
+    const double inv_sqrt_n = 1.0 / sqrt((double)c->n);
+    for (int64_t i = r0; i < r1; ++i) {
+        for (int64_t t = 0; t < c->d; ++t)
+            x[t] = c->A ? kqo_bf16_to_double(c->A[i * c->lda + t]) : c->X[i * c->lda + t];
+        for (int64_t g = 0; g < c->d / c->n; ++g) hadamard_group(x + g * c->n, c->n, inv_sqrt_n, y + g * c->n);
+        if (c->y_out)
+            for (int64_t t = 0; t < c->d; ++t) c->y_out[i * c->d + t] = y[t];
+        if (c->codes)
+            for (int64_t j = 0; j < c->d / 32; ++j)
+                kqo_quantize_block(y + 32 * j, c->codes + i * (c->d / 2) + 16 * j, c->scales + i * (c->d / 32) + j);
+    }
+    free(x);
+    free(y);
+}
+
+/* Block-Hadamard transform of bf16 A (group size n, a power of two dividing d),
+ * then quantize; codes/scales (both) and y_out may be NULL. Returns -1 on a
+ * bad n. */
+int kqo_hadamard_quantize(const uint16_t *A, int64_t m, int64_t d, int64_t lda, int64_t n,
+                          uint8_t *codes, uint8_t *scales, double *y_out, int nthreads) {
+    if (n < 1 || (n & (n - 1)) != 0 || d % n != 0) return -1;
+    hctx c = {.A = A, .d = d, .lda = lda, .n = n, .codes = codes, .scales = scales, .y_out = y_out};
+    parallel_rows(m, nthreads, rows_hadamard, &c);
+    return 0;
+}
+
+/* The same transform of float64 rows (no quantization), for checking the
+ * transform on inputs that are not bf16. */
+int kqo_hadamard_f64(const double *X, int64_t m, int64_t d, int64_t ldx, int64_t n, double *y_out,
+                     int nthreads) {
+    if (n < 1 || (n & (n - 1)) != 0 || d % n != 0) return -1;
+    hctx c = {.X = X, .d = d, .lda = ldx, .n = n, .y_out = y_out};
+    parallel_rows(m, nthreads, rows_hadamard, &c);
     return 0;
 }

@@ -2,7 +2,8 @@
 
 Each case copies the oracle's C source, plants one mistake (a wrong tie rule,
 an off-by-one exponent, a reversed Kronecker bit order, a transposed operand,
-a lost sign of zero, swapped nibbles, a wrong exponent clamp), builds it into a
+a lost sign of zero, swapped nibbles, a wrong exponent clamp, a wrong
+Hadamard sign, a lost normalization, a wrong group offset), builds it into a
 temporary library on the CPU and checks that at least one of the pins in
 test_oracle_pins.py fails against it. The shipped oracle is untouched.
 """
@@ -12,6 +13,7 @@ import subprocess
 import pytest
 
 import oracle
+import tests.test_oracle_hadamard_pins as hpins
 import tests.test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "kq_oracle.c")
@@ -35,6 +37,13 @@ MUTANTS = {
                         [pins.test_worked_examples_golden]),
     "inverse_sign_slip": ("Gi[k][0][1] = -G[k][0][1] / det;", "Gi[k][0][1] = G[k][0][1] / det;",
                           [pins.test_inverse_is_kron_of_inverses]),
+    "hadamard_or_not_and": ("popcountll((unsigned long long)(r & col))",
+                            "popcountll((unsigned long long)(r | col))",
+                            [lambda o: hpins.test_matches_scipy_hadamard(o, 64)]),
+    "hadamard_unnormalized": ("y[col] = s * inv_sqrt_n;", "y[col] = s;",
+                              [lambda o: hpins.test_involution_and_norm(o, 256)]),
+    "hadamard_group_offset": ("hadamard_group(x + g * c->n, c->n", "hadamard_group(x + g, c->n",
+                              [hpins.test_groups_are_independent]),
 }
 
 
