@@ -138,6 +138,28 @@ kq_status kq_mxfp4_gemm(const uint8_t *codes_a, const uint8_t *scales_a, const u
                         const uint8_t *scales_w, int64_t m, int64_t n, int64_t k, float *O, int64_t ldo,
                         kq_stream_t stream);
 
+/*
+ * Block-Hadamard transform + quantize: the fixed-rotation baselines the paper
+ * compares against -- Sec. 1 and Table 2 (Hadamard at the MXFP4 block size,
+ * n = 32) and Sec. 4.4 / Table 3 (the fast Walsh-Hadamard transform over the
+ * whole power-of-two width, n = d). For every row a of A and every group of n
+ * consecutive channels starting at a multiple of n,
+ *   y = a[g n : g n + n] . H_n / sqrt(n),  H_n[r][c] = (-1)^popcount(r & c),
+ * the normalized Sylvester matrix (Sec. 3.2 "Hadamard initialization": the
+ * k-fold Kronecker power of [[1,1],[1,-1]]/sqrt(2)); at n = 32 this is the
+ * Kronecker transform with every factor equal to that 2x2. y is computed in
+ * fp32 and quantized as above.
+ *   n        power of two with 32 <= n <= 16384 and d % n == 0 (else
+ *            KQ_ERR_SHAPE; a power of two above 16384: KQ_ERR_UNSUPPORTED).
+ *            Non-power-of-two widths need padding, which this call does not do.
+ *   y_debug  device or NULL; fp32 [m][d] receives y (check mode), 16-byte aligned.
+ * m * (d / n) must stay below 2^32 (KQ_ERR_UNSUPPORTED). Other arguments as
+ * kq_quantize_mxfp4.
+ */
+kq_status kq_hadamard_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda, int64_t n,
+                                     uint8_t *codes, uint8_t *scales, float *y_debug,
+                                     kq_stream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *kq_status_string(kq_status s);
 

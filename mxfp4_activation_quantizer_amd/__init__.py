@@ -28,6 +28,7 @@ EXPORTS = (
     "kq_quantize_mxfp4_f32",
     "kq_inverse_fold_weights",
     "kq_mxfp4_gemm",
+    "kq_hadamard_quantize_mxfp4",
     "kq_status_string",
     "kq_last_hip_error",
     "kq_factors_from_lu",
@@ -61,6 +62,7 @@ def lib():
             "kq_inverse_fold_weights": [p, i64, i64, p, p, p],
             "kq_factors_from_lu": [p, i64, p],
             "kq_mxfp4_gemm": [p, p, p, p, i64, i64, i64, p, i64, p],
+            "kq_hadamard_quantize_mxfp4": [p, i64, i64, i64, i64, p, p, p, p],
         }.items():
             fn = getattr(L, name)
             fn.argtypes = args
@@ -156,6 +158,24 @@ def transform_quantize_mxfp4(A, factors, codes=None, scales=None, y_debug=None, 
     _check("kq_transform_quantize_mxfp4",
            lib().kq_transform_quantize_mxfp4(_p(A), m, d, lda, _p(factors), _p(codes), _p(scales),
                                              _p(y_debug), _stream_ptr(stream)))
+    return codes, scales
+
+
+def hadamard_quantize_mxfp4(A, n, codes=None, scales=None, y_debug=None, stream=None):
+    """Block-Hadamard baseline: each group of n channels times H_n / sqrt(n), then MXFP4.
+
+    n = 32 is the block-size Hadamard, n = d the full-width transform (FWHT).
+    """
+    torch = _torch()
+    m, d, lda = _bf16_input(A)
+    if y_debug is not None:
+        _dev(y_debug, "y_debug", (torch.float32,))
+        if tuple(y_debug.shape) != (m, d) or not y_debug.is_contiguous():
+            raise ValueError("y_debug must be a contiguous fp32 [m][d] tensor")
+    codes, scales = _outputs(m, d, A.device, codes, scales)
+    _check("kq_hadamard_quantize_mxfp4",
+           lib().kq_hadamard_quantize_mxfp4(_p(A), m, d, lda, int(n), _p(codes), _p(scales),
+                                            _p(y_debug), _stream_ptr(stream)))
     return codes, scales
 
 

@@ -37,6 +37,14 @@ __device__ __forceinline__ float max_xor16_xor32(float v) {
     return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
+// 16-byte load; NT marks it non-temporal (streamed once, no reuse expected).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4 *p, bool nt) {
+    if (!nt) return *p;
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // bf16 pairs packed in one dword -> two fp32 (exact widening).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

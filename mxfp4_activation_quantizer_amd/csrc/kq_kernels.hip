@@ -19,6 +19,7 @@
 
 #include "kq.h"
 #include "kq_device.hpp"
+#include "kq_host.hpp"
 
 namespace kq {
 
@@ -58,14 +59,6 @@ __device__ __forceinline__ void lane_coords(const Geom &g, int &j, int &sub, int
         j = (cg << g.cb_log2) + (quad & ((1 << g.cb_log2) - 1));
         row0 = slab * g.rstep * g.iters + (quad >> g.cb_log2);
     }
-}
-
-// 16-byte load; NT marks it non-temporal (streamed once, no reuse expected).
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load_stream(const uint4 *p, bool nt) {
-    if (!nt) return *p;
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Walks this quad's rows row0 + k rstep (k < iters), issuing U rows' loads
@@ -460,19 +453,10 @@ __global__ __launch_bounds__(kThreads) void mxfp4_gemm_kernel(
 // ===========================================================================
 namespace {
 
-thread_local int g_last_hip_error = 0;
-
-bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-// Shape checks common to every [m][ld] x d operand.
-kq_status check_shape(int64_t m, int64_t d, int64_t ld) {
-    if (m < 0 || d < 0 || ld < 0) return KQ_ERR_SHAPE;
-    if (d % 32 != 0) return KQ_ERR_SHAPE;
-    if (ld < d) return KQ_ERR_SHAPE;
-    if (d / 32 > (int64_t)0x7FFFFFFF) return KQ_ERR_SHAPE;
-    if (ld > 0 && m > INT64_MAX / 4 / ld) return KQ_ERR_SHAPE;  // byte offsets of fp32 rows fit
-    return KQ_OK;
-}
+using kqhost::aligned;
+using kqhost::check_bf16_io;
+using kqhost::check_shape;
+using kqhost::launched;
 
 int64_t gcd64(int64_t a, int64_t b) {
     while (b) {
@@ -563,15 +547,6 @@ bool make_mgeom(int64_t m, int64_t d, int64_t lda, int nb, int unroll, kq::MGeom
     return true;
 }
 
-kq_status launched() {
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) {
-        g_last_hip_error = (int)e;
-        return KQ_ERR_HIP;
-    }
-    return KQ_OK;
-}
-
 // Launch shape of the bf16 quad kernels: column strips of 16 blocks, row tiles
 // of 4 rows, non-temporal loads. Workgroups are kept short, which the HBM
 // system rewards: the quantizers walk 2 row tiles (both loads in flight), the
@@ -656,12 +631,6 @@ kq_status launch_fused(const uint16_t *A, int64_t m, int64_t d, int64_t lda, con
     if ((d / 32) % 2 == 0)
         return launch_mfma<2, DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
     return launch_mfma<1, DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
-}
-
-kq_status check_bf16_io(const uint16_t *A, int64_t lda, const uint8_t *codes, const uint8_t *scales) {
-    if (!A || !codes || !scales) return KQ_ERR_NULL;
-    if (!aligned(A, 16) || lda % 8 != 0 || !aligned(codes, 16)) return KQ_ERR_ALIGN;
-    return KQ_OK;
 }
 
 }  // namespace
@@ -759,7 +728,7 @@ const char *kq_status_string(kq_status s) {
     return "unknown kq_status";
 }
 
-int kq_last_hip_error(void) { return g_last_hip_error; }
+int kq_last_hip_error(void) { return kqhost::g_last_hip_error; }
 
 kq_status kq_factors_from_lu(const double *abc, int64_t nblk, float *factors) {
     if (nblk < 0) return KQ_ERR_SHAPE;

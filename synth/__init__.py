@@ -288,6 +288,13 @@ WORKLOADS = {
     # FLUX.1-schnell: batch 4 x (4096 image + 512 text) tokens = 18432 rows.
     "flux_18432x3072": dict(m=18432, d=3072, seed=1003, kind="pixart"),
     "flux_18432x12288": dict(m=18432, d=12288, seed=1013, kind="pixart"),
+    # Power-of-two widths of the paper's kernel-latency table (Sec. 4.4, Table 3),
+    # where the full-width Walsh-Hadamard transform applies without padding.
+    "pow2_4096x1024": dict(m=4096, d=1024, seed=1021, kind="pixart"),
+    "pow2_4096x4096": dict(m=4096, d=4096, seed=1022, kind="pixart"),
+    "pow2_4096x16384": dict(m=4096, d=16384, seed=1023, kind="pixart"),
+    "pow2_512x4096": dict(m=512, d=4096, seed=1024, kind="pixart"),
+    "pow2_512x16384": dict(m=512, d=16384, seed=1025, kind="pixart"),
 }
 
 

@@ -65,6 +65,15 @@ GOOD = P(0x10000)  # never dereferenced: every case below fails before a launch
     ("kq_mxfp4_gemm", (GOOD, None, GOOD, GOOD, 4, 4, 64, GOOD, 4, None), kq.KQ_ERR_NULL),
     ("kq_mxfp4_gemm", (P(0x10008), GOOD, GOOD, GOOD, 4, 4, 64, GOOD, 4, None), kq.KQ_ERR_ALIGN),
     ("kq_mxfp4_gemm", (None, None, None, None, 0, 4, 64, None, 4, None), kq.KQ_OK),
+    ("kq_hadamard_quantize_mxfp4", (GOOD, 4, 96, 96, 48, GOOD, GOOD, None, None), kq.KQ_ERR_SHAPE),
+    ("kq_hadamard_quantize_mxfp4", (GOOD, 4, 64, 64, 16, GOOD, GOOD, None, None), kq.KQ_ERR_SHAPE),
+    ("kq_hadamard_quantize_mxfp4", (GOOD, 4, 96, 96, 64, GOOD, GOOD, None, None), kq.KQ_ERR_SHAPE),
+    ("kq_hadamard_quantize_mxfp4", (GOOD, 4, 32768, 32768, 32768, GOOD, GOOD, None, None),
+     kq.KQ_ERR_UNSUPPORTED),
+    ("kq_hadamard_quantize_mxfp4", (None, 4, 64, 64, 64, GOOD, GOOD, None, None), kq.KQ_ERR_NULL),
+    ("kq_hadamard_quantize_mxfp4", (GOOD, 4, 64, 64, 64, GOOD, GOOD, P(0x10004), None), kq.KQ_ERR_ALIGN),
+    ("kq_hadamard_quantize_mxfp4", (GOOD, 4, 64, 68, 64, GOOD, GOOD, None, None), kq.KQ_ERR_ALIGN),
+    ("kq_hadamard_quantize_mxfp4", (None, 0, 1024, 1024, 1024, None, None, None, None), kq.KQ_OK),
 ])
 def test_host_argument_checks(L, fn, args, status):
     assert getattr(L, fn)(*args) == status
