@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum host time spent on the CPU-oracle baseline (0 disables it)")
-    ap.add_argument("--only", choices=["fused", "smoothquant", "quantize"], default=None,
+    ap.add_argument("--only", choices=["fused", "smoothquant", "quantize", "hadamard32"], default=None,
                     help="time only one kernel (for profiler runs)")
     ap.add_argument("--eager", action="store_true",
                     help="time steps as eager launches instead of replaying one HIP graph per step")
@@ -97,6 +97,10 @@ def run_kernel(kq, kind, s: Sets, stream, k=None):
         kq.transform_quantize_mxfp4(A, s.factors, codes=c, scales=sc, stream=stream)
     elif kind == "smoothquant":
         kq.smoothquant_quantize_mxfp4(A, s.inv, codes=c, scales=sc, stream=stream)
+    elif kind == "hadamard32":
+        kq.hadamard_quantize_mxfp4(A, 32, codes=c, scales=sc, stream=stream)
+    elif kind == "fwht":
+        kq.hadamard_quantize_mxfp4(A, s.d, codes=c, scales=sc, stream=stream)
     else:
         kq.quantize_mxfp4(A, codes=c, scales=sc, stream=stream)
 
@@ -181,9 +185,11 @@ def _events_us(torch, fn, reps, warmup):
 
 def extras(torch, kq, synth, flux_sets, reps=100, warmup=20):
     """Context measurements kept beside the headline step (same rotation rules):
-    the PixArt-shaped inputs, the MFMA form of the transform on the FLUX inputs,
+    the PixArt-shaped inputs, the paper's power-of-two kernel-table shapes with
+    the Hadamard baselines, the MFMA form of the transform on the FLUX inputs,
     the weight fold and fp32 quantizer on 3072 x 3072 weights, and the W4A4 GEMM."""
     out = {"other_configs": {}}
+    out["kernel_table_pow2"] = kernel_table(torch, kq, synth, reps, warmup)
     for name in ("pixart_attn_4096x1152", "pixart_ffn_8192x4608"):
         w = synth.workload(name)
         s = Sets(torch, w)
@@ -235,6 +241,28 @@ def extras(torch, kq, synth, flux_sets, reps=100, warmup=20):
     return out
 
 
+def kernel_table(torch, kq, synth, reps, warmup):
+    """The kernel-latency comparison of the paper (Sec. 4.4, Table 3) on this GPU:
+    quantize-only (Q4), SmoothQuant (Scale), the fused Kronecker kernel (K2),
+    block Hadamard-32 and the full-width Walsh-Hadamard transform (FWHT), each
+    fused with the MXFP4 quantizer, at the table's power-of-two shapes."""
+    table = {}
+    for name in ("pow2_4096x1024", "pow2_4096x4096", "pow2_4096x16384", "pow2_512x4096",
+                 "pow2_512x16384"):
+        w = synth.workload(name)
+        s = Sets(torch, w)
+        per = {}
+        for kind in ("quantize", "smoothquant", "fused", "hadamard32", "fwht"):
+            _, d = time_kernel(torch, kq, kind, [s], reps, warmup)
+            per[kind] = summarize(d[0], s)
+        per["scale_over_fused"] = round(per["smoothquant"]["median_us"] / per["fused"]["median_us"], 3)
+        per["fwht_over_fused"] = round(per["fwht"]["median_us"] / per["fused"]["median_us"], 3)
+        table[name] = per
+        log("%s: %s" % (name, {k: (v["median_us"] if isinstance(v, dict) else v) for k, v in per.items()}))
+        del s
+    return table
+
+
 def summarize(d_us, s: Sets):
     med = float(np.median(d_us))
     return {"m": s.m, "d": s.d, "median_us": round(med, 3), "mean_us": round(float(d_us.mean()), 3),
@@ -246,11 +274,11 @@ def summarize(d_us, s: Sets):
 
 
 def source_digest():
-    import glob
+    """Hash of the sources the dominant (fused) kernel is built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mxfp4_activation_quantizer_amd", "csrc")
-    for p in sorted(glob.glob(os.path.join(csrc, "*"))):
-        h.update(open(p, "rb").read())
+    for f in ("kq_kernels.hip", "kq_device.hpp"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 

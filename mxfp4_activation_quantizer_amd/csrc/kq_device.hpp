@@ -12,6 +12,10 @@
 
 namespace kq {
 
+// What a quad kernel applies before quantizing: nothing (quantize-only), a
+// per-channel scale (SmoothQuant) or the Kronecker transform.
+enum Mode { kQuantOnly = 0, kSmooth = 1, kKron = 2 };
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));

@@ -1,11 +1,25 @@
-// Block-Hadamard transform + MXFP4 quantizer on gfx950: the fixed-rotation
-// baselines of KroQuant (arXiv 2607.21446v1) -- Sec. 1 and Table 2 (Hadamard
-// at block size 32) and Sec. 4.4 / Table 3 (the fast Walsh-Hadamard transform
-// over the full power-of-two width). For every row and every group of n
-// consecutive channels (n = 2^LOGN, 32 <= n <= 16384) y = x . H_n / sqrt(n),
-// H_n the Sylvester matrix (Sec. 3.2 "Hadamard initialization": the k-fold
-// Kronecker power of [[1,1],[1,-1]]/sqrt(2)), computed in fp32 and quantized
-// to MXFP4 exactly as the fused Kronecker kernel does.
+// Flat-tile kernels on gfx950: quantize-only MXFP4, and the block-Hadamard
+// transform + MXFP4 (the fixed-rotation baselines of KroQuant, arXiv
+// 2607.21446v1 -- Sec. 1 and Table 2: Hadamard at block size 32; Sec. 4.4 /
+// Table 3: the fast Walsh-Hadamard transform over the full power-of-two
+// width).
+//
+// Flat tiles. The matrix is walked as its flattened rows (element E = row d +
+// col, which is also the element's index in the contiguous [m][d] outputs).
+// A wave owns a tile of WT = 512 R elements: lane t holds R chunks of 8
+// consecutive elements, chunk j at tile offset 512 j + 8 t (16-byte loads; a
+// wave-wide load covers 1 KB and the R loads of a wave 512 R contiguous
+// elements, all issued at once). Offset bits 0-2 are in-register, bits 3-8
+// the lane bits, bits 9.. the chunk index; each quad holds one 32-element
+// block. With nothing per column to fetch, quantize-only streams best this way
+// (one load phase per wave, workgroups covering 16 KB of contiguous input).
+//
+// Block Hadamard: for every row and every group of n consecutive channels
+// (n = 2^LOGN, 32 <= n <= 16384) y = x . H_n / sqrt(n), H_n the Sylvester
+// matrix (Sec. 3.2 "Hadamard initialization": the k-fold Kronecker power of
+// [[1,1],[1,-1]]/sqrt(2)), computed in fp32 and quantized to MXFP4 exactly as
+// the fused Kronecker kernel does. Group row q = row (d / n) + group holds
+// channels c < n, E = q n + c.
 //
 // Butterflies in signed form. A stage on channel bit b maps each pair
 // (x0, x1) that differs in bit b to (x0 + x1, x1 - x0): [[1,1],[1,-1]]
@@ -15,13 +29,7 @@
 // collect into (-1)^popcount(c) for output channel c, which the final
 // multiply by +-1/sqrt(n) removes.
 //
-// Layout. The matrix is walked as its flattened group rows (element
-// E = q n + c for group row q = row (d / n) + group, channel c < n), which is
-// also the element's index in the contiguous [m][d] outputs. A wave owns a
-// tile of WT = 512 R elements: lane t holds R chunks of 8 consecutive
-// elements, chunk j at tile offset 512 j + 8 t (16-byte loads; a wave-wide
-// load covers 1 KB). Offset bits 0-2 are in-register, bits 3-8 the lane bits,
-// bits 9.. the chunk index. Where each channel bit's stage runs:
+// Where each channel bit's stage runs:
 //   0-2          in-register pairs;
 //   3, 4         DPP quad permutes (lane xor 1, xor 2);
 //   5            ds_swizzle (lane xor 4 inside 32 lanes);
@@ -33,8 +41,8 @@
 //                those wave bits for chunk bits, then in-register pairs.
 // The swaps and the exchange change which elements a chunk holds, never the
 // shape: each lane still has 8 consecutive channels per chunk and each quad
-// one 32-channel block, so the quad quantizer of the fused kernel applies and
-// only the store addresses follow the new assignment.
+// one 32-channel block, so the quad quantizer applies and only the store
+// addresses follow the new assignment.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -109,7 +117,9 @@ __global__ __launch_bounds__(256) void hadamard_kernel(const uint16_t *__restric
     constexpr int R = H::R;
     constexpr int64_t WT = (int64_t)1 << H::LOGWT;
     constexpr int64_t NMASK = ((int64_t)1 << LOGN) - 1;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wave index is the same in every lane; saying so keeps the tile
+    // arithmetic on the scalar unit
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t tbase = ((int64_t)blockIdx.x * 4 + wave) * WT;
 
     float x[R][8];
@@ -262,6 +272,45 @@ __global__ __launch_bounds__(256) void hadamard_kernel(const uint16_t *__restric
     }
 }
 
+// Quantize-only on flat tiles (R = 4). Rows may be padded (lda > d): then the
+// row of a chunk is its 32-block index divided by d / 32.
+__global__ __launch_bounds__(256) void flat_quantize_kernel(const uint16_t *__restrict__ A, HGeom g,
+                                                            uint8_t *__restrict__ codes,
+                                                            uint8_t *__restrict__ scales) {
+    constexpr int R = 4;
+    constexpr int64_t WT = 512 * R;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t tbase = ((int64_t)blockIdx.x * 4 + wave) * WT;
+    uint4 q[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t E = tbase + 512 * j + 8 * lane;
+        q[j] = make_uint4(0, 0, 0, 0);
+        if (E < g.total) {
+            const uint16_t *p;
+            if (g.contig) {
+                p = A + E;
+            } else {
+                const uint32_t blk = (uint32_t)(E >> 5);
+                const uint32_t row = blk / g.G;
+                p = A + (int64_t)row * g.lda + ((int64_t)(blk - row * g.G) << 5) + (E & 31);
+            }
+            q[j] = load_stream(reinterpret_cast<const uint4 *>(p), true);
+        }
+    }
+    const int sub = lane & 3;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t E = tbase + 512 * j + 8 * lane;
+        uint32_t sbyte;
+        const uint32_t packed = quantize_quad_bf16(q[j], sbyte);
+        if (E < g.total) {
+            *reinterpret_cast<uint32_t *>(codes + (E >> 1)) = packed;
+            if (sub == 0) scales[E >> 5] = (uint8_t)sbyte;
+        }
+    }
+}
+
 }  // namespace kq
 
 namespace {
@@ -299,6 +348,26 @@ kq_status dispatch_hadamard(int logn, const uint16_t *A, const kq::HGeom &g, uin
 }  // namespace
 
 extern "C" {
+
+kq_status kq_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda, uint8_t *codes,
+                            uint8_t *scales, kq_stream_t stream) {
+    kq_status s = kqhost::check_shape(m, d, lda);
+    if (s != KQ_OK) return s;
+    if (m == 0 || d == 0) return KQ_OK;
+    if ((s = kqhost::check_bf16_io(A, lda, codes, scales)) != KQ_OK) return s;
+    if (m > (int64_t)0xFFFFFFFF / (d / 32)) return KQ_ERR_UNSUPPORTED;  // block index in 32 bits
+    kq::HGeom g;
+    g.total = m * d;
+    g.lda = lda;
+    g.G = (uint32_t)(d / 32);
+    g.contig = lda == d;
+    g.inv_sqrt_n = 1.0f;
+    const int64_t nwg = ((g.total + 2047) / 2048 + 3) / 4;
+    if (nwg > 0x7FFFFFFF) return KQ_ERR_SHAPE;
+    hipLaunchKernelGGL(kq::flat_quantize_kernel, dim3((unsigned)nwg), dim3(256), 0, (hipStream_t)stream, A, g,
+                       codes, scales);
+    return kqhost::launched();
+}
 
 kq_status kq_hadamard_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda, int64_t n,
                                      uint8_t *codes, uint8_t *scales, float *y_debug,

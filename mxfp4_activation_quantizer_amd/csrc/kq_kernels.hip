@@ -5,7 +5,9 @@
 // j, y = a . K^(j) with K^(j) = G1 (x) G2 (x) G3 (x) G4 (x) G5 (Sec. 3.2 Eq. 5,
 // Sec. 3.5.1 Eq. 12), then MXFP4 (Sec. 3.1; Sec. 4.1 "Data format", App. D).
 //
-// Work mapping (all bf16 kernels): a workgroup of 256 lanes = 64 quads; a quad
+// Work mapping (the strip kernels here: SmoothQuant and the fused transform;
+// quantize-only and the Hadamard baselines use the flat tiles of kq_flat.hip):
+// a workgroup of 256 lanes = 64 quads; a quad
 // owns one 32-channel block of one row (16 bytes per lane). The 64 quads cover
 // CB = 2^cb_log2 consecutive blocks of R = 64 / CB consecutive rows, so every
 // row segment a workgroup touches is CB * 64 contiguous bytes. A workgroup
@@ -25,7 +27,6 @@ namespace kq {
 
 constexpr int kThreads = 256;
 
-enum Mode { kQuantOnly = 0, kSmooth = 1, kKron = 2 };
 
 // Workgroup -> work mapping of the quad kernels (a workgroup is 64 quads, a
 // quad owns one 32-channel block of one row at a time).
@@ -61,25 +62,32 @@ __device__ __forceinline__ void lane_coords(const Geom &g, int &j, int &sub, int
     }
 }
 
-// Walks this quad's rows row0 + k rstep (k < iters), issuing U rows' loads
-// together, and calls body(q, row) for each row below m. The row test is
-// uniform within a quad, so DPP inside `body` sees all four lanes. (Issuing
-// the next group's loads before processing this one, with or without raised
-// wave priority, measured slower on the FLUX shapes: it costs registers and
-// occupancy.)
+// Loads of this quad's rows row0 + (it + u) rstep, u < U (zeros past m).
+template <int U, bool NT>
+__device__ __forceinline__ void load_rows(const Geom &g, const uint16_t *__restrict__ A, int64_t row0,
+                                          int64_t c0, int it, uint4 q[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t row = row0 + (int64_t)(it + u) * g.rstep;
+        q[u] = row < g.m ? load_stream(reinterpret_cast<const uint4 *>(A + row * g.lda + c0), NT)
+                         : make_uint4(0, 0, 0, 0);
+    }
+}
+
+// Walks this quad's rows row0 + k rstep (k < iters), U rows' loads at a time,
+// and calls body(q, row) for each row below m. `q` holds the first group's
+// loads already when `preloaded` (issued before the per-block setup, so their
+// latency overlaps it). The row test is uniform within a quad, so DPP inside
+// `body` sees all four lanes. (Issuing the next group's loads before
+// processing this one, with or without raised wave priority, measured slower
+// on the FLUX shapes: it costs registers and occupancy.)
 template <int U, bool NT, typename Body>
 __device__ __forceinline__ void for_rows(const Geom &g, const uint16_t *__restrict__ A, int64_t row0,
-                                         int64_t c0, Body body) {
+                                         int64_t c0, uint4 q[U], bool preloaded, Body body) {
     const int64_t R = g.rstep;
     for (int it = 0; it < g.iters; it += U) {
         if (row0 + (int64_t)it * R >= g.m) break;
-        uint4 q[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t row = row0 + (int64_t)(it + u) * R;
-            q[u] = row < g.m ? load_stream(reinterpret_cast<const uint4 *>(A + row * g.lda + c0), NT)
-                             : make_uint4(0, 0, 0, 0);
-        }
+        if (it > 0 || !preloaded) load_rows<U, NT>(g, A, row0, c0, it, q);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = row0 + (int64_t)(it + u) * R;
@@ -106,34 +114,29 @@ __device__ __forceinline__ void finish_f32(const float y[8], const Geom &g, int6
     if (sub == 0) scales[row * g.nblk + j] = (uint8_t)sbyte;
 }
 
-// bf16 input, quad layout: quantize-only (T = I), SmoothQuant (T = diag(inv_scale))
-// or the Kronecker transform (shear form, or the general stages for blocks
-// that do not admit it).
-template <int MODE, bool DEBUG, int U, bool NT, int MAP>
+// bf16 input, quad layout: SmoothQuant (T = diag(inv_scale)) or the Kronecker
+// transform (shear form, or the general stages for blocks that do not admit
+// it). Quantize-only runs on the flat tiles of kq_flat.hip.
+template <int MODE, bool DEBUG, int U, bool NT, int MAP, bool PRE>
 __global__ __launch_bounds__(kThreads) void bf16_quad_kernel(
     const uint16_t *__restrict__ A, Geom g, const float *__restrict__ params,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ ydbg) {
+    static_assert(MODE == kSmooth || MODE == kKron, "quantize-only runs on the flat kernel");
     int j, sub;
     int64_t row0;
     lane_coords<MAP>(g, j, sub, row0);
     const int64_t c0 = (int64_t)j * 32 + sub * 8;
+    uint4 q[U];
 
-    if (MODE == kQuantOnly) {
-        for_rows<U, NT>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
-            uint32_t sbyte;
-            const uint32_t packed = quantize_quad_bf16(q, sbyte);
-            *reinterpret_cast<uint32_t *>(codes + row * (g.d / 2) + (int64_t)j * 16 + sub * 4) = packed;
-            if (sub == 0) scales[row * g.nblk + j] = (uint8_t)sbyte;
-        });
-    } else if (MODE == kSmooth) {
+    if (MODE == kSmooth) {
         float sq[8];
         const float4 a = *reinterpret_cast<const float4 *>(params + c0);
         const float4 b = *reinterpret_cast<const float4 *>(params + c0 + 4);
         sq[0] = a.x; sq[1] = a.y; sq[2] = a.z; sq[3] = a.w;
         sq[4] = b.x; sq[5] = b.y; sq[6] = b.z; sq[7] = b.w;
-        for_rows<U, NT>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
+        for_rows<U, NT>(g, A, row0, c0, q, false, [&](const uint4 &x, int64_t row) {
             float y[8];
-            widen8(q, y);
+            widen8(x, y);
 #pragma unroll
             for (int i = 0; i < 8; ++i) y[i] = y[i] * sq[i];
             finish_f32<DEBUG>(y, g, row, j, sub, c0, codes, scales, ydbg);
@@ -142,26 +145,28 @@ __global__ __launch_bounds__(kThreads) void bf16_quad_kernel(
         // Per-block setup is shared through LDS when the workgroup's first row
         // of quads holds all its blocks (strip mapping): those quads (wave 0
         // for CB = 16) derive the shear coefficients, everyone reads them back.
+        // With PRE the first rows' loads are in flight during the setup.
         ShearLane S;
         if (MAP == kStrip) {
             __shared__ ShearLane lds[64];
             const int quad = threadIdx.x >> 2;
-            if ((quad >> g.cb_log2) == 0) {
-                float f[20];
-                load_factors20(params + (int64_t)j * 20, f);
-                shear_lane_setup(f, sub, lds[threadIdx.x]);
-            }
+            const bool setter = (quad >> g.cb_log2) == 0;
+            float f[20];
+            if (setter) load_factors20(params + (int64_t)j * 20, f);
+            if (PRE && row0 < g.m) load_rows<U, NT>(g, A, row0, c0, 0, q);
+            if (setter) shear_lane_setup(f, sub, lds[threadIdx.x]);
             __syncthreads();
             S = lds[((quad & ((1 << g.cb_log2) - 1)) << 2) | sub];
         } else {
             float f[20];
             load_factors20(params + (int64_t)j * 20, f);
+            if (PRE && row0 < g.m) load_rows<U, NT>(g, A, row0, c0, 0, q);
             shear_lane_setup(f, sub, S);
         }
         if (S.ok) {  // one block per quad: uniform within the quad
-            for_rows<U, NT>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
+            for_rows<U, NT>(g, A, row0, c0, q, PRE, [&](const uint4 &x, int64_t row) {
                 float y[8];
-                widen8(q, y);
+                widen8(x, y);
                 shear_apply8(y, S);
                 finish_f32<DEBUG>(y, g, row, j, sub, c0, codes, scales, ydbg);
             });
@@ -170,9 +175,9 @@ __global__ __launch_bounds__(kThreads) void bf16_quad_kernel(
             load_factors20(params + (int64_t)j * 20, f);
             KronLane L;
             kron_lane_setup(f, sub, L);
-            for_rows<U, NT>(g, A, row0, c0, [&](const uint4 &q, int64_t row) {
+            for_rows<U, NT>(g, A, row0, c0, q, PRE, [&](const uint4 &x, int64_t row) {
                 float y[8];
-                widen8(q, y);
+                widen8(x, y);
                 kron_apply8(y, L);
                 finish_f32<DEBUG>(y, g, row, j, sub, c0, codes, scales, ydbg);
             });
@@ -549,19 +554,33 @@ bool make_mgeom(int64_t m, int64_t d, int64_t lda, int nb, int unroll, kq::MGeom
 
 // Launch shape of the bf16 quad kernels: column strips of 16 blocks, row tiles
 // of 4 rows, non-temporal loads. Workgroups are kept short, which the HBM
-// system rewards: the quantizers walk 2 row tiles (both loads in flight), the
+// system rewards: SmoothQuant walks 2 row tiles (both loads in flight), the
 // transform 8 row tiles, 4 at a time (its per-block setup is amortized over
-// more rows). Chosen by sweeping tile counts, unroll depth, prefetching and
-// both mappings on the 18432 x 3072 and 18432 x 12288 shapes.
+// more rows, and the first 4 rows' loads are issued before the setup). Chosen
+// by sweeping tile counts, unroll depth, prefetching and the strip, flat and
+// column-per-wave mappings on the 18432 x 3072 and 18432 x 12288 shapes.
 template <int MODE, bool DEBUG>
 kq_status launch_quad(const uint16_t *A, int64_t m, int64_t d, int64_t lda, const float *params,
                       uint8_t *codes, uint8_t *scales, float *ydbg, kq_stream_t stream) {
-    constexpr int U = MODE == kq::kKron ? 4 : 2;
-    const int64_t iters = MODE == kq::kKron ? 8 : 2;
     kq::Geom g;
     unsigned nwg;
-    if (!make_geom_strip(m, d, lda, U, iters, g, nwg)) return KQ_ERR_SHAPE;
-    hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, DEBUG, U, true, kq::kStrip>), dim3(nwg),
+    if (MODE == kq::kKron) {
+        // 8 row tiles per workgroup, 4 rows' loads at a time; when that leaves
+        // fewer than 1024 workgroups (4 per CU), 2 row tiles of 2 rows instead:
+        // small inputs need the parallelism more than the amortized setup.
+        if (!make_geom_strip(m, d, lda, 4, 8, g, nwg)) return KQ_ERR_SHAPE;
+        if (nwg >= 1024) {
+            hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, DEBUG, 4, true, kq::kStrip, true>), dim3(nwg),
+                               dim3(kq::kThreads), 0, (hipStream_t)stream, A, g, params, codes, scales, ydbg);
+            return launched();
+        }
+        if (!make_geom_strip(m, d, lda, 2, 2, g, nwg)) return KQ_ERR_SHAPE;
+        hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, DEBUG, 2, true, kq::kStrip, true>), dim3(nwg),
+                           dim3(kq::kThreads), 0, (hipStream_t)stream, A, g, params, codes, scales, ydbg);
+        return launched();
+    }
+    if (!make_geom_strip(m, d, lda, 2, 2, g, nwg)) return KQ_ERR_SHAPE;
+    hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, DEBUG, 2, true, kq::kStrip, false>), dim3(nwg),
                        dim3(kq::kThreads), 0, (hipStream_t)stream, A, g, params, codes, scales, ydbg);
     return launched();
 }
@@ -636,15 +655,6 @@ kq_status launch_fused(const uint16_t *A, int64_t m, int64_t d, int64_t lda, con
 }  // namespace
 
 extern "C" {
-
-kq_status kq_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda, uint8_t *codes,
-                            uint8_t *scales, kq_stream_t stream) {
-    kq_status s = check_shape(m, d, lda);
-    if (s != KQ_OK) return s;
-    if (m == 0 || d == 0) return KQ_OK;
-    if ((s = check_bf16_io(A, lda, codes, scales)) != KQ_OK) return s;
-    return launch_quad<kq::kQuantOnly, false>(A, m, d, lda, nullptr, codes, scales, nullptr, stream);
-}
 
 kq_status kq_transform_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
                                       const float *factors, uint8_t *codes, uint8_t *scales,
