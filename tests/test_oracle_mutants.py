@@ -13,6 +13,9 @@ import subprocess
 import pytest
 
 import oracle
+import importlib.util
+
+import tests.test_oracle_calib_pins as cpins
 import tests.test_oracle_hadamard_pins as hpins
 import tests.test_oracle_pins as pins
 
@@ -64,3 +67,31 @@ def test_pins_catch_planted_mistake(name, tmp_path):
         except AssertionError:
             caught = True
     assert caught, "pins did not notice the planted mistake " + name
+
+
+# Planted mistakes in the calibration oracle (oracle/calib.py): each mutated copy
+# is loaded as a separate module and the finite-difference pin must reject it.
+CALIB_SRC = os.path.join(os.path.dirname(oracle.__file__), "calib.py")
+CALIB_MUTANTS = {
+    "inverse_term_sign": ("dK = dK - KinvT @", "dK = dK + KinvT @"),
+    "inverse_not_transposed": ("KinvT @ np.transpose(dP, (0, 2, 1)) @ KinvT", "KinvT @ dP @ KinvT"),
+    "eq6_chain_sign": ("g00 + c * g10 + g11 / (a * a)", "g00 + c * g10 - g11 / (a * a)"),
+    "regularizer_sign": ("- lam_A * 2.0 / (M * d) * (f[\"Xq\"] - f[\"X\"])",
+                         "+ lam_A * 2.0 / (M * d) * (f[\"Xq\"] - f[\"X\"])"),
+    "kron_bit_order": ("((r >> (4 - k)) & 1, (c >> (4 - k)) & 1)", "((r >> k) & 1, (c >> k) & 1)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CALIB_MUTANTS))
+def test_calibration_pins_catch_planted_mistake(name, tmp_path, orc):
+    old, new = CALIB_MUTANTS[name]
+    src = open(CALIB_SRC).read()
+    assert src.count(old) == 1, "mutation site not found: " + old
+    path = tmp_path / "calib_mutant.py"
+    path.write_text(src.replace(old, new).replace("from . import get as _get_oracle",
+                                                  "from oracle import get as _get_oracle"))
+    spec = importlib.util.spec_from_file_location("calib_mutant_" + name, str(path))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    with pytest.raises(AssertionError):
+        cpins.check_gradient(orc, mod, 2)
