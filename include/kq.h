@@ -160,6 +160,49 @@ kq_status kq_hadamard_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, in
                                      uint8_t *codes, uint8_t *scales, float *y_debug,
                                      kq_stream_t stream);
 
+/*
+ * fp32 GEMM: D = alpha op(A) op(B) + beta C, row-major operands; op(A) is m x k
+ * (A is m x k, or k x m when transa), op(B) is k x n (B is k x n, or n x k when
+ * transb). C may be NULL when beta == 0; C and D use the row strides ldc, ldd.
+ * fp32 fused multiply-adds in ascending k. Used by the calibration below and
+ * usable on its own.
+ */
+kq_status kq_gemm_f32(int transa, int transb, int64_t m, int64_t n, int64_t k, float alpha, const float *A,
+                      int64_t lda, const float *B, int64_t ldb, float beta, const float *C, int64_t ldc, float *D,
+                      int64_t ldd, kq_stream_t stream);
+
+/*
+ * Layer-wise calibration of the Kronecker factors (Sec. 3.3, Eq. 6-10): Adam
+ * on the 15 parameters per block theta[j][k][0..2] = (a, b, c) of
+ * G_k = [[a, b], [c a, c b - 1/a]] (Eq. 6) against
+ *   L = ||Q(A T) Q(W T^{-T})^T - A W^T||^2/(M o) + lambda_A ||Q(A T) - A T||^2/(M d)
+ *     + lambda_W ||Q(W T^{-T}) - W T^{-T}||^2/(o d)                       (Eq. 7-9)
+ * with a straight-through estimator: Q passes gradients unchanged inside the
+ * first term, and its value is held fixed inside the other two (so they pull
+ * A T and W T^{-T} toward their quantized values). Q is the MXFP4 quantizer of
+ * this library (quantize, then decode).
+ *   A          device, bf16 [M][d] calibration activations (M = N m rows)
+ *   W          device, fp32 [o][d] layer weights
+ *   workspace  device, 256-byte aligned, at least kq_calib_workspace_bytes();
+ *              init fills it with A in fp32 and A W^T; step reuses it. Owned
+ *              by the caller; no other allocation is made.
+ * kq_calib_step (t >= 1 is Adam's step count; beta1, beta2 in [0, 1), eps, lr >= 0):
+ *   theta, adam_m, adam_v  device fp32 [d/32][5][3], updated in place
+ *   lambdas    device fp32 [2] = (lambda_A, lambda_W); with auto_lambda != 0 they
+ *              are first set by Eq. 10 from this step's loss terms (call it so
+ *              at the starting point; a term that is zero there gets weight 0)
+ *   losses     device fp32 [3] = (L_out, L_A, L_W) at theta before the update
+ *   grad_theta device fp32 [d/32][5][3] or NULL: dL/dtheta at theta
+ * M, o, d > 0, d % 32 == 0, and M d, o d, M o below 2^31 (KQ_ERR_UNSUPPORTED).
+ */
+kq_status kq_calib_workspace_bytes(int64_t M, int64_t d, int64_t o, int64_t *bytes);
+kq_status kq_calib_init(const uint16_t *A, int64_t M, int64_t d, const float *W, int64_t o, void *workspace,
+                        int64_t workspace_bytes, kq_stream_t stream);
+kq_status kq_calib_step(const float *W, int64_t M, int64_t d, int64_t o, float *theta, float *adam_m, float *adam_v,
+                        int64_t t, float lr, float beta1, float beta2, float eps, float *lambdas, int auto_lambda,
+                        float *losses, float *grad_theta, void *workspace, int64_t workspace_bytes,
+                        kq_stream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *kq_status_string(kq_status s);
 

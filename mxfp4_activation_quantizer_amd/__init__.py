@@ -29,6 +29,10 @@ EXPORTS = (
     "kq_inverse_fold_weights",
     "kq_mxfp4_gemm",
     "kq_hadamard_quantize_mxfp4",
+    "kq_gemm_f32",
+    "kq_calib_workspace_bytes",
+    "kq_calib_init",
+    "kq_calib_step",
     "kq_status_string",
     "kq_last_hip_error",
     "kq_factors_from_lu",
@@ -63,6 +67,12 @@ def lib():
             "kq_factors_from_lu": [p, i64, p],
             "kq_mxfp4_gemm": [p, p, p, p, i64, i64, i64, p, i64, p],
             "kq_hadamard_quantize_mxfp4": [p, i64, i64, i64, i64, p, p, p, p],
+            "kq_gemm_f32": [st, st, i64, i64, i64, ctypes.c_float, p, i64, p, i64, ctypes.c_float, p, i64, p,
+                            i64, p],
+            "kq_calib_workspace_bytes": [i64, i64, i64, p],
+            "kq_calib_init": [p, i64, i64, p, i64, p, i64, p],
+            "kq_calib_step": [p, i64, i64, i64, p, p, p, i64, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                              ctypes.c_float, p, st, p, p, p, i64, p],
         }.items():
             fn = getattr(L, name)
             fn.argtypes = args
@@ -246,6 +256,91 @@ def mxfp4_gemm(codes_a, scales_a, codes_w, scales_w, out=None, stream=None):
            lib().kq_mxfp4_gemm(_p(codes_a), _p(scales_a), _p(codes_w), _p(scales_w), m, n, k, _p(out),
                                out.stride(0), _stream_ptr(stream)))
     return out
+
+
+def gemm_f32(A, B, transa=False, transb=False, alpha=1.0, beta=0.0, C=None, out=None, stream=None):
+    """D = alpha op(A) op(B) + beta C in fp32 (row-major operands)."""
+    torch = _torch()
+    for t, nm in ((A, "A"), (B, "B")):
+        _dev(t, nm, (torch.float32,))
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(nm + " must be 2-D with unit column stride")
+    m, k = (A.shape[1], A.shape[0]) if transa else (A.shape[0], A.shape[1])
+    kb, n = (B.shape[1], B.shape[0]) if transb else (B.shape[0], B.shape[1])
+    if kb != k:
+        raise ValueError("inner dimensions do not match")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=A.device)
+    _dev(out, "out", (torch.float32,))
+    if tuple(out.shape) != (m, n) or out.stride(1) != 1:
+        raise ValueError("out must be fp32 [m][n] with unit column stride")
+    if beta != 0.0:
+        _dev(C, "C", (torch.float32,))
+        if tuple(C.shape) != (m, n) or C.stride(1) != 1 or C.stride(0) != out.stride(0):
+            raise ValueError("C must be fp32 [m][n] with the row stride of out")
+    _check("kq_gemm_f32",
+           lib().kq_gemm_f32(int(transa), int(transb), m, n, k, float(alpha), _p(A), A.stride(0), _p(B),
+                             B.stride(0), float(beta), _p(C) if beta != 0.0 else None, out.stride(0), _p(out),
+                             out.stride(0), _stream_ptr(stream)))
+    return out
+
+
+class Calibration:
+    """Layer-wise calibration of the Kronecker factors (Sec. 3.3) on one GPU.
+
+    Holds the device state: the 15 parameters per block (a, b, c of Eq. 6 for
+    each of the five factors), Adam's moments, the Eq. 10 weights and the
+    workspace. Every computation runs in libkq.so (kq_calib_init / kq_calib_step).
+    """
+
+    def __init__(self, A, W, theta=None, stream=None):
+        torch = _torch()
+        _dev(A, "A", (torch.bfloat16, torch.int16, torch.uint16))
+        _dev(W, "W", (torch.float32,))
+        if not A.is_contiguous() or not W.is_contiguous() or A.dim() != 2 or W.dim() != 2:
+            raise ValueError("A [M][d] and W [o][d] must be contiguous")
+        self.M, self.d = A.shape
+        self.o = W.shape[0]
+        if W.shape[1] != self.d:
+            raise ValueError("W must be [o][d]")
+        self.W = W
+        self.stream = stream
+        nbytes = ctypes.c_int64(0)
+        _check("kq_calib_workspace_bytes",
+               lib().kq_calib_workspace_bytes(self.M, self.d, self.o, ctypes.byref(nbytes)))
+        self.ws = torch.empty(nbytes.value + 256, dtype=torch.uint8, device=A.device)
+        self._ws_ptr = (self.ws.data_ptr() + 255) // 256 * 256
+        nblk = self.d // 32
+        if theta is None:  # Hadamard initialization (Sec. 3.2): a = b = 1/sqrt(2), c = 1
+            theta = torch.tensor([2.0 ** -0.5, 2.0 ** -0.5, 1.0], dtype=torch.float32).repeat(nblk, 5, 1)
+        self.theta = theta.to(device=A.device, dtype=torch.float32).contiguous().clone()
+        if self.theta.numel() != nblk * 15:
+            raise ValueError("theta must hold 15 parameters per block")
+        self.m = torch.zeros_like(self.theta)
+        self.v = torch.zeros_like(self.theta)
+        self.lambdas = torch.zeros(2, dtype=torch.float32, device=A.device)
+        self.losses = torch.zeros(3, dtype=torch.float32, device=A.device)
+        self.grad = torch.zeros_like(self.theta)
+        self.t = 0
+        _check("kq_calib_init",
+               lib().kq_calib_init(_p(A), self.M, self.d, _p(W), self.o, ctypes.c_void_p(self._ws_ptr),
+                                   self.ws.numel() - 256, _stream_ptr(stream)))
+
+    def step(self, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, auto_lambda=None):
+        """One Adam step; the first step (at the starting point) sets lambda by Eq. 10
+        unless ``auto_lambda`` is False (then ``self.lambdas`` is used as set)."""
+        self.t += 1
+        auto = (self.t == 1) if auto_lambda is None else bool(auto_lambda)
+        _check("kq_calib_step",
+               lib().kq_calib_step(_p(self.W), self.M, self.d, self.o, _p(self.theta), _p(self.m), _p(self.v),
+                                   self.t, float(lr), float(beta1), float(beta2), float(eps), _p(self.lambdas),
+                                   int(auto), _p(self.losses), _p(self.grad), ctypes.c_void_p(self._ws_ptr),
+                                   self.ws.numel() - 256, _stream_ptr(self.stream)))
+        return self.losses
+
+    def factors(self):
+        """The current 2x2 factors, fp32 [d/32][5][2][2] (Eq. 6), for the fused quantizer."""
+        return factors_from_lu(self.theta.double().cpu().numpy())
 
 
 def factors_from_lu(abc):

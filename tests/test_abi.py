@@ -74,6 +74,25 @@ GOOD = P(0x10000)  # never dereferenced: every case below fails before a launch
     ("kq_hadamard_quantize_mxfp4", (GOOD, 4, 64, 64, 64, GOOD, GOOD, P(0x10004), None), kq.KQ_ERR_ALIGN),
     ("kq_hadamard_quantize_mxfp4", (GOOD, 4, 64, 68, 64, GOOD, GOOD, None, None), kq.KQ_ERR_ALIGN),
     ("kq_hadamard_quantize_mxfp4", (None, 0, 1024, 1024, 1024, None, None, None, None), kq.KQ_OK),
+    ("kq_gemm_f32", (0, 0, 4, 4, 4, 1.0, None, 4, GOOD, 4, 0.0, None, 4, GOOD, 4, None), kq.KQ_ERR_NULL),
+    ("kq_gemm_f32", (0, 0, 4, 4, 8, 1.0, GOOD, 4, GOOD, 4, 0.0, None, 4, GOOD, 4, None), kq.KQ_ERR_SHAPE),
+    ("kq_gemm_f32", (0, 0, 4, 4, 4, 1.0, GOOD, 4, GOOD, 4, 1.0, None, 4, GOOD, 4, None), kq.KQ_ERR_NULL),
+    ("kq_gemm_f32", (0, 0, -1, 4, 4, 1.0, GOOD, 4, GOOD, 4, 0.0, None, 4, GOOD, 4, None), kq.KQ_ERR_SHAPE),
+    ("kq_gemm_f32", (0, 0, 0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, None, 4, None), kq.KQ_OK),
+    ("kq_calib_init", (GOOD, 64, 48, GOOD, 16, GOOD, 1 << 30, None), kq.KQ_ERR_SHAPE),
+    ("kq_calib_init", (None, 64, 64, GOOD, 16, GOOD, 1 << 30, None), kq.KQ_ERR_NULL),
+    ("kq_calib_init", (GOOD, 64, 64, GOOD, 16, P(0x10010), 1 << 30, None), kq.KQ_ERR_ALIGN),
+    ("kq_calib_init", (GOOD, 64, 64, GOOD, 16, GOOD, 1024, None), kq.KQ_ERR_SHAPE),
+    ("kq_calib_step", (GOOD, 64, 64, 16, GOOD, GOOD, GOOD, 0, 1e-3, 0.9, 0.999, 1e-8, GOOD, 1, GOOD, None,
+                       GOOD, 1 << 30, None), kq.KQ_ERR_SHAPE),
+    ("kq_calib_step", (GOOD, 64, 64, 16, GOOD, GOOD, GOOD, 1, 1e-3, 1.0, 0.999, 1e-8, GOOD, 1, GOOD, None,
+                       GOOD, 1 << 30, None), kq.KQ_ERR_SHAPE),
+    ("kq_calib_step", (GOOD, 64, 64, 16, GOOD, GOOD, GOOD, 1, -1.0, 0.9, 0.999, 1e-8, GOOD, 1, GOOD, None,
+                       GOOD, 1 << 30, None), kq.KQ_ERR_SHAPE),
+    ("kq_calib_step", (GOOD, 64, 64, 16, GOOD, None, GOOD, 1, 1e-3, 0.9, 0.999, 1e-8, GOOD, 1, GOOD, None,
+                       GOOD, 1 << 30, None), kq.KQ_ERR_NULL),
+    ("kq_calib_step", (GOOD, 64, 64, 16, GOOD, GOOD, GOOD, 1, 1e-3, 0.9, 0.999, 1e-8, GOOD, 1, GOOD, None,
+                       GOOD, 4096, None), kq.KQ_ERR_SHAPE),
 ])
 def test_host_argument_checks(L, fn, args, status):
     assert getattr(L, fn)(*args) == status
@@ -96,3 +115,13 @@ def test_factors_from_lu_matches_eq6(orc):
     bad[3, 2, 0] = 0.0
     with pytest.raises(kq.KQError):
         kq.factors_from_lu(bad)
+
+
+def test_calib_workspace_bytes(L):
+    n = ctypes.c_int64(0)
+    assert L.kq_calib_workspace_bytes(4096, 1152, 1152, ctypes.byref(n)) == kq.KQ_OK
+    floats = 4096 * 1152 * 6 + 1152 * 1152 * 3  # A, X, Q(X), grad (M x d); C0, E (M x o); Y, Q(Y), grad (o x d)
+    assert n.value >= floats * 4
+    assert L.kq_calib_workspace_bytes(4096, 1000, 16, ctypes.byref(n)) == kq.KQ_ERR_SHAPE
+    assert L.kq_calib_workspace_bytes(4096, 1024, 16, None) == kq.KQ_ERR_NULL
+    assert L.kq_calib_workspace_bytes(1 << 20, 4096, 16, ctypes.byref(n)) == kq.KQ_ERR_UNSUPPORTED
