@@ -132,3 +132,55 @@ def test_short_run_lowers_the_loss(torch_dev, kq):
     last = cal.step(lr=0.0).cpu().numpy()
     print("[calib] L_out %.4f -> %.4f, L_A %.4f -> %.4f" % (first[0], last[0], first[1], last[1]), flush=True)
     assert last[0] < 0.5 * first[0]
+
+
+def test_w4a4_calibrated_flux(torch_dev, kq, orc):
+    """Calibrate on the first 4096 rows of the FLUX 18432x3072 activations with the
+    3072x3072 weights, then run the whole W4A4 pipeline (fold, fp32 quantize, fused
+    transform + quantize, MXFP4 GEMM) with the learned factors and compare the layer
+    output error |Q(AT) Q(WT^-T)^T - A W^T| on held-out rows with T = I and with
+    the block-Hadamard start. The pipeline itself is checked against the oracle's
+    pipeline with the same learned factors."""
+    torch = torch_dev
+    case("w4a4 calibrated 18432x3072x3072")
+    w = synth.workload("flux_18432x3072")
+    W = synth.weights(3072, 3072, 1004)
+    Wd = torch.from_numpy(W).cuda()
+    A_dev = torch.from_numpy(w.A.view(np.int16)).cuda().view(torch.bfloat16)
+    cal = kq.Calibration(A_dev[:4096].contiguous(), Wd)
+    for _ in range(100):
+        cal.step(lr=1e-2)
+    losses = cal.step(lr=0.0).cpu().numpy()
+    fac = torch.from_numpy(cal.factors()).cuda()
+
+    def pipeline(f):
+        if f is None:
+            ca, sa = kq.quantize_mxfp4(A_dev)
+            cw, sw = kq.quantize_mxfp4_f32(Wd)
+        else:
+            ca, sa = kq.transform_quantize_mxfp4(A_dev, f)
+            cw, sw = kq.quantize_mxfp4_f32(kq.inverse_fold_weights(Wd, f))
+        return kq.mxfp4_gemm(ca, sa, cw, sw)
+
+    O_c = pipeline(fac)
+    O_h = pipeline(torch.from_numpy(synth.hadamard_factors(96)).cuda())
+    O_i = pipeline(None)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = np.sort(rng.choice(np.arange(4096, w.m), 256, replace=False))  # held out from calibration
+    idx = torch.from_numpy(rows).cuda()
+    exact = synth.bf16_bits_to_f32(w.A[rows]).astype(np.float64) @ W.astype(np.float64).T
+    err = {k: np.linalg.norm(O.index_select(0, idx).cpu().numpy().astype(np.float64) - exact)
+           for k, O in (("calibrated", O_c), ("hadamard", O_h), ("identity", O_i))}
+    # the GPU pipeline with the learned factors against the oracle's pipeline (same factors)
+    sub = rows[:64]
+    facn = cal.factors()
+    ca_r, sa_r, _ = orc.transform_quantize(w.A[sub], facn, want_y=False)
+    cw_r, sw_r = orc.quantize_f64(orc.inverse_fold(W, facn))
+    O_r = orc.gemm_dequant(ca_r, sa_r, cw_r, sw_r, 3072)
+    og = O_c.index_select(0, torch.from_numpy(sub).cuda()).cpu().numpy().astype(np.float64)
+    rel = np.linalg.norm(og - O_r) / np.linalg.norm(O_r)
+    print("[calib-w4a4] calibration losses %s; held-out |E|: calibrated %.1f, Hadamard %.1f, T=I %.1f; "
+          "pipeline vs oracle %.2e" % (losses, err["calibrated"], err["hadamard"], err["identity"], rel), flush=True)
+    assert rel <= 1e-3
+    assert err["calibrated"] < err["hadamard"] and err["calibrated"] < err["identity"]
