@@ -238,7 +238,40 @@ def extras(torch, kq, synth, flux_sets, reps=100, warmup=20):
                                          "TFLOPs": round(flops / (med * 1e-6) / 1e12, 1),
                                          "pct_fp4_peak": round(100 * flops / (med * 1e-6) / 10.1e15, 2)}
     log("weight side / gemm: %s %s" % (out["weight_fold_3072x3072"], out["w4a4_gemm_18432x3072x3072"]))
+    out["calibration_4096x3072x3072"] = calibration_timing(torch, kq, synth, A, W)
+    log("calibration: %s" % out["calibration_4096x3072x3072"])
     return out
+
+
+def calibration_timing(torch, kq, synth, A, W, steps=20):
+    """Layer-wise calibration (Sec. 3.3) on 4096 FLUX rows with the 3072 x 3072 weights:
+    GPU time per Adam step (three M x d x o GEMMs and the per-block chain), the fp32
+    GEMM alone, and one step of the float64 oracle on the host for scale."""
+    M = 4096
+    A4 = A[:M].contiguous()
+    cal = kq.Calibration(A4, W)
+    cal.step(lr=1e-2)  # sets lambda
+    d_step = _events_us(torch, lambda: cal.step(lr=1e-2), steps, 2)
+    Af = A4.float()
+    Cg = torch.empty((M, W.shape[0]), dtype=torch.float32, device="cuda")
+    d_gemm = _events_us(torch, lambda: kq.gemm_f32(Af, W, transb=True, out=Cg), 10, 2)
+    flops = 2.0 * M * W.shape[0] * W.shape[1]
+    res = {"gpu_ms_per_step": round(float(np.median(d_step)) / 1e3, 3),
+           "gemm_f32_4096x3072x3072_us": round(float(np.median(d_gemm)), 1),
+           "gemm_f32_TFLOPs": round(flops / (np.median(d_gemm) * 1e-6) / 1e12, 1),
+           "gemm_f32_frac_of_fp32_peak": round(flops / (np.median(d_gemm) * 1e-6) / 157.3e12, 3),
+           "losses_after": [round(float(x), 5) for x in cal.losses.cpu().numpy()]}
+    try:
+        from oracle import calib as ocalib
+        P = ocalib.Problem(synth.bf16_bits_to_f32(A4.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64),
+                           W.cpu().numpy().astype(np.float64))
+        th = ocalib.hadamard_theta(W.shape[1] // 32)
+        t0 = time.perf_counter()
+        P.gradient(th, 1.0, 1.0)
+        res["oracle_s_per_step"] = round(time.perf_counter() - t0, 2)
+    except Exception as e:  # the oracle is a reported baseline only
+        res["oracle_s_per_step"] = "unavailable: %s" % e
+    return res
 
 
 def kernel_table(torch, kq, synth, reps, warmup):
