@@ -384,10 +384,17 @@ __global__ __launch_bounds__(kThreads) void f32_kernel(
 // wave supplies row l % 16 and the 32 consecutive k of group l / 16 (16 code
 // bytes) with that group's E8M0 byte as its scale, which is exactly the MX
 // layout of the codes/scales arrays; it receives O rows 4 (l / 16) + t, column
-// l % 16. A workgroup of 4 waves computes a 64 x 64 tile, each wave 32 x 32
-// (2 x 2 MFMA tiles), walking k in steps of 128. Rows and columns past m or n
-// read zero codes and are not stored; k must be a multiple of 32, and k
-// groups past k read zero codes.
+// l % 16.
+//
+// A workgroup of 4 waves computes a 128 x 128 tile, each wave 64 x 64 (4 x 4
+// MFMA tiles), walking k in steps of 128 (64 code bytes and 4 scale bytes per
+// row). The A and W tiles of a step are staged through LDS, double-buffered:
+// every thread fetches its share of the next step's codes and scales into
+// registers before the MFMAs of the current step and stores them to the other
+// buffer after, one barrier per step. LDS rows are padded to 80 bytes so the 16
+// rows an operand read touches fall in distinct banks. Rows and columns past m
+// or n, and k groups past k, read zero codes (scale 2^0) and are not stored;
+// k must be a multiple of 32.
 // ---------------------------------------------------------------------------
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
@@ -395,57 +402,147 @@ struct GemmGeom {
     int64_t m, n, k, ldo, tiles_n;
 };
 
-__device__ __forceinline__ i32x8_t load_fp4_operand(const uint8_t *codes, int64_t row, int64_t nrows,
-                                                     int64_t kbytes, int64_t kbyte0, int &scale,
-                                                     const uint8_t *scales, int64_t kblocks, int64_t kblk) {
-    i32x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
-    scale = 127;
-    if (row < nrows && kbyte0 < kbytes) {
-        const uint4 q = *reinterpret_cast<const uint4 *>(codes + row * kbytes + kbyte0);
-        v[0] = (int)q.x; v[1] = (int)q.y; v[2] = (int)q.z; v[3] = (int)q.w;
-        scale = scales[row * kblocks + kblk];
+constexpr int kGemmTile = 128;
+
+// Staged rows of one operand tile: KS k blocks of 128 (64 code bytes each) per
+// stage, padded by 16 bytes so the 16 rows an operand read touches fall in
+// distinct banks.
+template <int KS>
+struct GemmStage {
+    static constexpr int kRow = KS * 64 + 16;
+    static constexpr int kLoads = KS * 2;  // 16-byte code loads per thread per operand
+};
+
+// This thread's share of one operand tile for the stage starting at code byte
+// kb0: rows (t >> 2) + 64 h, 16 bytes at column 16 (t & 3) + 64 c of each
+// 128-k block c, and, for threads below 128, row t's KS * 4 scale bytes.
+template <int KS>
+struct TileRegs {
+    uint4 code[KS][2];
+    uint32_t scl[KS];
+};
+
+template <int KS>
+__device__ __forceinline__ void fetch_tile(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                           int64_t row_base, int64_t nrows, int64_t kbytes, int64_t kblocks,
+                                           int64_t kb0, TileRegs<KS> &R) {
+    const int t = threadIdx.x;
+    const int r0 = t >> 2, c16 = (t & 3) * 16;
+#pragma unroll
+    for (int c = 0; c < KS; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t row = row_base + r0 + 64 * h, kb = kb0 + 64 * c + c16;
+            R.code[c][h] = make_uint4(0, 0, 0, 0);
+            if (row < nrows && kb < kbytes)
+                R.code[c][h] = *reinterpret_cast<const uint4 *>(codes + row * kbytes + kb);
+        }
+    if (t < kGemmTile) {
+        const int64_t row = row_base + t;
+#pragma unroll
+        for (int c = 0; c < KS; ++c) {
+            const int64_t g0 = kb0 / 16 + 4 * c;  // first 32-k group of this 128-k block
+            uint32_t v = 0x7F7F7F7Fu;             // 2^0 for rows and k groups past the ends
+            if (row < nrows) {
+                if ((kblocks & 3) == 0 && (reinterpret_cast<uintptr_t>(scales) & 3) == 0 && g0 + 4 <= kblocks) {
+                    v = *reinterpret_cast<const uint32_t *>(scales + row * kblocks + g0);
+                } else {
+                    v = 0;
+#pragma unroll
+                    for (int gi = 0; gi < 4; ++gi)
+                        v |= (g0 + gi < kblocks ? (uint32_t)scales[row * kblocks + g0 + gi] : 0x7Fu) << (8 * gi);
+                }
+            }
+            R.scl[c] = v;
+        }
     }
-    return v;
 }
 
+template <int KS>
+__device__ __forceinline__ void stash_tile(uint8_t *codes_lds, uint32_t *scales_lds, const TileRegs<KS> &R) {
+    const int t = threadIdx.x;
+    const int r0 = t >> 2, c16 = (t & 3) * 16;
+#pragma unroll
+    for (int c = 0; c < KS; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            *reinterpret_cast<uint4 *>(codes_lds + (r0 + 64 * h) * GemmStage<KS>::kRow + 64 * c + c16) = R.code[c][h];
+    if (t < kGemmTile)
+#pragma unroll
+        for (int c = 0; c < KS; ++c) scales_lds[c * kGemmTile + t] = R.scl[c];
+}
+
+template <int KS>
 __global__ __launch_bounds__(kThreads) void mxfp4_gemm_kernel(
     const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const uint8_t *__restrict__ cw,
     const uint8_t *__restrict__ sw, GemmGeom g, float *__restrict__ O) {
+    constexpr int ROW = GemmStage<KS>::kRow;
+    __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kGemmTile * ROW];
+    __shared__ __attribute__((aligned(16))) uint8_t b_lds[2][kGemmTile * ROW];
+    __shared__ uint32_t as_lds[2][KS * kGemmTile], bs_lds[2][KS * kGemmTile];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t tm = blockIdx.x / g.tiles_n, tn = blockIdx.x % g.tiles_n;
-    const int64_t row0 = tm * 64 + (wave >> 1) * 32, col0 = tn * 64 + (wave & 1) * 32;
+    const int64_t m0 = tm * kGemmTile, n0 = tn * kGemmTile;
+    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;  // this wave's 64 x 64 within the tile
     const int r = lane & 15, grp = lane >> 4;
     const int64_t kbytes = g.k / 2, kblocks = g.k / 32;
-    floatx4_t acc[2][2];
+    const int64_t stages = (g.k + 128 * KS - 1) / (128 * KS);
+
+    floatx4_t acc[4][4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    for (int64_t k0 = 0; k0 < g.k; k0 += 128) {
-        const int64_t kb0 = k0 / 2 + grp * 16, kblk = k0 / 32 + grp;
-        i32x8_t av[2], bv[2];
-        int as[2], bs[2];
+        for (int b = 0; b < 4; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    TileRegs<KS> ra, rb;
+    fetch_tile<KS>(ca, sa, m0, g.m, kbytes, kblocks, 0, ra);
+    fetch_tile<KS>(cw, sw, n0, g.n, kbytes, kblocks, 0, rb);
+    stash_tile<KS>(a_lds[0], as_lds[0], ra);
+    stash_tile<KS>(b_lds[0], bs_lds[0], rb);
+    __syncthreads();
+    for (int64_t s = 0; s < stages; ++s) {
+        const int cur = (int)(s & 1);
+        if (s + 1 < stages) {
+            fetch_tile<KS>(ca, sa, m0, g.m, kbytes, kblocks, (s + 1) * 64 * KS, ra);
+            fetch_tile<KS>(cw, sw, n0, g.n, kbytes, kblocks, (s + 1) * 64 * KS, rb);
+        }
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-            av[a] = load_fp4_operand(ca, row0 + a * 16 + r, g.m, kbytes, kb0, as[a], sa, kblocks, kblk);
+        for (int c = 0; c < KS; ++c) {
+            i32x8_t bv[4];
+            int bsc[4];
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-            bv[b] = load_fp4_operand(cw, col0 + b * 16 + r, g.n, kbytes, kb0, bs[b], sw, kblocks, kblk);
+            for (int b = 0; b < 4; ++b) {
+                const uint4 q =
+                    *reinterpret_cast<const uint4 *>(b_lds[cur] + (wc + b * 16 + r) * ROW + 64 * c + grp * 16);
+                bv[b] = i32x8_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+                bsc[b] = (int)((bs_lds[cur][c * kGemmTile + wc + b * 16 + r] >> (8 * grp)) & 0xFFu);
+            }
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+            for (int a = 0; a < 4; ++a) {
+                const uint4 q =
+                    *reinterpret_cast<const uint4 *>(a_lds[cur] + (wr + a * 16 + r) * ROW + 64 * c + grp * 16);
+                const i32x8_t av = i32x8_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+                const int asc = (int)((as_lds[cur][c * kGemmTile + wr + a * 16 + r] >> (8 * grp)) & 0xFFu);
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[a], bv[b], acc[a][b], 4, 4, 0,
-                                                                             as[a], 0, bs[b]);
+                for (int b = 0; b < 4; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv[b], acc[a][b], 4, 4, 0, asc,
+                                                                                 0, bsc[b]);
+            }
+        }
+        if (s + 1 < stages) {
+            stash_tile<KS>(a_lds[cur ^ 1], as_lds[cur ^ 1], ra);
+            stash_tile<KS>(b_lds[cur ^ 1], bs_lds[cur ^ 1], rb);
+        }
+        __syncthreads();
     }
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int64_t col = col0 + b * 16 + r;
+        for (int b = 0; b < 4; ++b) {
+            const int64_t col = n0 + wc + b * 16 + r;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const int64_t row = row0 + a * 16 + grp * 4 + t;
+                const int64_t row = m0 + wr + a * 16 + grp * 4 + t;
                 if (row < g.m && col < g.n) O[row * g.ldo + col] = acc[a][b][t];
             }
         }
@@ -718,10 +815,10 @@ kq_status kq_mxfp4_gemm(const uint8_t *codes_a, const uint8_t *scales_a, const u
     if (m == 0 || n == 0) return KQ_OK;
     if (!codes_a || !scales_a || !codes_w || !scales_w || !O) return KQ_ERR_NULL;
     if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || (k / 2) % 16 != 0) return KQ_ERR_ALIGN;
-    const int64_t tiles_m = (m + 63) / 64, tiles_n = (n + 63) / 64;
+    const int64_t tiles_m = (m + kq::kGemmTile - 1) / kq::kGemmTile, tiles_n = (n + kq::kGemmTile - 1) / kq::kGemmTile;
     if (tiles_m * tiles_n > 0x7FFFFFFF || m > INT64_MAX / 4 / (ldo > 0 ? ldo : 1)) return KQ_ERR_SHAPE;
     kq::GemmGeom g{m, n, k, ldo, tiles_n};
-    hipLaunchKernelGGL(kq::mxfp4_gemm_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kq::kThreads), 0,
+    hipLaunchKernelGGL(kq::mxfp4_gemm_kernel<2>, dim3((unsigned)(tiles_m * tiles_n)), dim3(kq::kThreads), 0,
                        (hipStream_t)stream, codes_a, scales_a, codes_w, scales_w, g, O);
     return launched();
 }
