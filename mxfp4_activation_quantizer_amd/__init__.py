@@ -326,9 +326,10 @@ class Calibration:
                lib().kq_calib_init(_p(A), self.M, self.d, _p(W), self.o, ctypes.c_void_p(self._ws_ptr),
                                    self.ws.numel() - 256, _stream_ptr(stream)))
 
-    def step(self, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, auto_lambda=None):
-        """One Adam step; the first step (at the starting point) sets lambda by Eq. 10
-        unless ``auto_lambda`` is False (then ``self.lambdas`` is used as set)."""
+    def step(self, lr=1e-2, beta1=0.9, beta2=0.999, eps=1e-8, auto_lambda=None):
+        """One Adam step (App. D.1: 100 steps at learning rate 1e-2); the first step (at
+        the starting point) sets lambda by Eq. 10 unless ``auto_lambda`` is False (then
+        ``self.lambdas`` is used as set)."""
         self.t += 1
         auto = (self.t == 1) if auto_lambda is None else bool(auto_lambda)
         _check("kq_calib_step",
