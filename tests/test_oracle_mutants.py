@@ -95,3 +95,28 @@ def test_calibration_pins_catch_planted_mistake(name, tmp_path, orc):
     spec.loader.exec_module(mod)
     with pytest.raises(AssertionError):
         cpins.check_gradient(orc, mod, 2)
+
+
+LOWRANK_SRC = os.path.join(os.path.dirname(oracle.__file__), "lowrank.py")
+LOWRANK_MUTANTS = {
+    "residual_sign": ("resid = Wt - L @ R", "resid = Wt + L @ R", "test_unquantized_layer_is_AW"),
+    "no_bf16_rounding": ("Z = round_bf16(X) @ qdq(R, orc).T", "Z = X @ qdq(R, orc).T",
+                         "test_grid_exact_branch_is_plain_product"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LOWRANK_MUTANTS))
+def test_lowrank_pins_catch_planted_mistake(name, tmp_path, orc, monkeypatch):
+    import tests.test_oracle_lowrank_pins as lpins
+    old, new, pin = LOWRANK_MUTANTS[name]
+    src = open(LOWRANK_SRC).read()
+    assert src.count(old) == 1, "mutation site not found: " + old
+    path = tmp_path / "lowrank_mutant.py"
+    path.write_text(src.replace(old, new).replace("from . import get as _get_oracle",
+                                                  "from oracle import get as _get_oracle"))
+    spec = importlib.util.spec_from_file_location("lowrank_mutant_" + name, str(path))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    monkeypatch.setattr(lpins, "lowrank", mod)
+    with pytest.raises(AssertionError):
+        getattr(lpins, pin)(orc)
