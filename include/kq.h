@@ -161,6 +161,42 @@ kq_status kq_hadamard_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, in
                                      kq_stream_t stream);
 
 /*
+ * As kq_transform_quantize_mxfp4, also writing y rounded to bf16 (nearest,
+ * ties to even): the 16-bit activation the low-rank branch of Sec. 3.4 Eq. 11
+ * consumes (App. D keeps that branch's activations at 16 bits).
+ *   y16  device, bf16 bits [m][d], 16-byte aligned (required)
+ */
+kq_status kq_transform_quantize_mxfp4_y16(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
+                                          const float *factors, uint8_t *codes, uint8_t *scales, uint16_t *y16,
+                                          kq_stream_t stream);
+
+/*
+ * Low-rank branch of Eq. 11, first product: Z = X16 . Q(R)^T, fp32 accumulation
+ * (bf16 matrix instructions; the decoded MXFP4 values are exact in bf16).
+ *   X16       device, bf16 bits [m][ldx], ldx >= d, ldx % 8 == 0, 16-byte aligned
+ *   codes_r   device, [r][d/2] (R in MXFP4, blocks along d), 16-byte aligned
+ *   scales_r  device, [r][d/32]
+ *   Z         device, fp32 [m][r], 16-byte aligned, written
+ * d % 32 == 0, r > 0, r % 32 == 0 (KQ_ERR_SHAPE).
+ */
+kq_status kq_lowrank_project(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint8_t *codes_r,
+                             const uint8_t *scales_r, int64_t r, float *Z, kq_stream_t stream);
+
+/*
+ * The W4A4 layer of Eq. 11: O = deq(A) deq(W)^T + Z deq(L)^T, the low-rank term
+ * added in the same kernel (Z split into two bf16 terms, exact to 2^-16
+ * relative; deq(L) exact in bf16), so O is written once.
+ *   codes_a ... ldo   as kq_mxfp4_gemm (W here is the residual W~ - L R)
+ *   Z                 device, fp32 [m][r], 16-byte aligned (kq_lowrank_project)
+ *   codes_l, scales_l device, L in MXFP4: [n][r/2] (16-byte aligned), [n][r/32]
+ * r > 0, r % 32 == 0 (KQ_ERR_SHAPE).
+ */
+kq_status kq_mxfp4_gemm_lowrank(const uint8_t *codes_a, const uint8_t *scales_a, const uint8_t *codes_w,
+                                const uint8_t *scales_w, int64_t m, int64_t n, int64_t k, const float *Z,
+                                const uint8_t *codes_l, const uint8_t *scales_l, int64_t r, float *O, int64_t ldo,
+                                kq_stream_t stream);
+
+/*
  * fp32 GEMM: D = alpha op(A) op(B) + beta C, row-major operands; op(A) is m x k
  * (A is m x k, or k x m when transa), op(B) is k x n (B is k x n, or n x k when
  * transb). C may be NULL when beta == 0; C and D use the row strides ldc, ldd.

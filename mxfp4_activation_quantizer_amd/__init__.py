@@ -29,6 +29,9 @@ EXPORTS = (
     "kq_inverse_fold_weights",
     "kq_mxfp4_gemm",
     "kq_hadamard_quantize_mxfp4",
+    "kq_transform_quantize_mxfp4_y16",
+    "kq_lowrank_project",
+    "kq_mxfp4_gemm_lowrank",
     "kq_gemm_f32",
     "kq_calib_workspace_bytes",
     "kq_calib_init",
@@ -67,6 +70,9 @@ def lib():
             "kq_factors_from_lu": [p, i64, p],
             "kq_mxfp4_gemm": [p, p, p, p, i64, i64, i64, p, i64, p],
             "kq_hadamard_quantize_mxfp4": [p, i64, i64, i64, i64, p, p, p, p],
+            "kq_transform_quantize_mxfp4_y16": [p, i64, i64, i64, p, p, p, p, p],
+            "kq_lowrank_project": [p, i64, i64, i64, p, p, i64, p, p],
+            "kq_mxfp4_gemm_lowrank": [p, p, p, p, i64, i64, i64, p, p, p, i64, p, i64, p],
             "kq_gemm_f32": [st, st, i64, i64, i64, ctypes.c_float, p, i64, p, i64, ctypes.c_float, p, i64, p,
                             i64, p],
             "kq_calib_workspace_bytes": [i64, i64, i64, p],
@@ -187,6 +193,77 @@ def hadamard_quantize_mxfp4(A, n, codes=None, scales=None, y_debug=None, stream=
            lib().kq_hadamard_quantize_mxfp4(_p(A), m, d, lda, int(n), _p(codes), _p(scales),
                                             _p(y_debug), _stream_ptr(stream)))
     return codes, scales
+
+
+def transform_quantize_mxfp4_y16(A, factors, codes=None, scales=None, y16=None, stream=None):
+    """Fused y = A T then MXFP4, also writing bf16(y) [m][d] (the 16-bit activation the
+    low-rank branch of Eq. 11 consumes). Returns codes, scales, y16."""
+    torch = _torch()
+    m, d, lda = _bf16_input(A)
+    _dev(factors, "factors", (torch.float32,))
+    if factors.numel() != (d // 32) * 20 or not factors.is_contiguous():
+        raise ValueError("factors must be contiguous fp32 [d/32][5][2][2]")
+    if y16 is None:
+        y16 = torch.empty((m, d), dtype=torch.bfloat16, device=A.device)
+    _dev(y16, "y16", (torch.bfloat16,))
+    if tuple(y16.shape) != (m, d) or not y16.is_contiguous():
+        raise ValueError("y16 must be a contiguous bf16 [m][d] tensor")
+    codes, scales = _outputs(m, d, A.device, codes, scales)
+    _check("kq_transform_quantize_mxfp4_y16",
+           lib().kq_transform_quantize_mxfp4_y16(_p(A), m, d, lda, _p(factors), _p(codes), _p(scales), _p(y16),
+                                                 _stream_ptr(stream)))
+    return codes, scales, y16
+
+
+def lowrank_project(X16, codes_r, scales_r, out=None, stream=None):
+    """Z = X16 Q(R)^T in fp32: X16 bf16 [m][d], R in MXFP4 (codes [r][d/2], scales [r][d/32])."""
+    torch = _torch()
+    _dev(X16, "X16", (torch.bfloat16, torch.int16, torch.uint16))
+    m, d, ldx = _rows(X16, "X16")
+    for t, nm in ((codes_r, "codes_r"), (scales_r, "scales_r")):
+        _dev(t, nm, (torch.uint8,))
+        if not t.is_contiguous():
+            raise ValueError(nm + " must be contiguous")
+    r = codes_r.shape[0]
+    if tuple(codes_r.shape) != (r, d // 2) or tuple(scales_r.shape) != (r, d // 32):
+        raise ValueError("R operand shapes do not match X16")
+    if out is None:
+        out = torch.empty((m, r), dtype=torch.float32, device=X16.device)
+    _dev(out, "out", (torch.float32,))
+    if tuple(out.shape) != (m, r) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [m][r] tensor")
+    _check("kq_lowrank_project",
+           lib().kq_lowrank_project(_p(X16), m, d, ldx, _p(codes_r), _p(scales_r), r, _p(out), _stream_ptr(stream)))
+    return out
+
+
+def mxfp4_gemm_lowrank(codes_a, scales_a, codes_w, scales_w, Z, codes_l, scales_l, out=None, stream=None):
+    """O = deq(A) deq(W)^T + Z deq(L)^T (Eq. 11's two terms): Z fp32 [m][r], L in MXFP4
+    (codes [n][r/2], scales [n][r/32])."""
+    torch = _torch()
+    for t, nm in ((codes_a, "codes_a"), (scales_a, "scales_a"), (codes_w, "codes_w"), (scales_w, "scales_w"),
+                  (codes_l, "codes_l"), (scales_l, "scales_l")):
+        _dev(t, nm, (torch.uint8,))
+        if not t.is_contiguous():
+            raise ValueError(nm + " must be contiguous")
+    _dev(Z, "Z", (torch.float32,))
+    m, kb = codes_a.shape
+    n = codes_w.shape[0]
+    k = kb * 2
+    r = Z.shape[1]
+    if tuple(codes_w.shape) != (n, kb) or tuple(scales_a.shape) != (m, k // 32) or \
+            tuple(scales_w.shape) != (n, k // 32) or Z.shape[0] != m or not Z.is_contiguous() or \
+            tuple(codes_l.shape) != (n, r // 2) or tuple(scales_l.shape) != (n, r // 32):
+        raise ValueError("operand shapes do not match")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=codes_a.device)
+    _dev(out, "out", (torch.float32,))
+    if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
+        raise ValueError("out must be fp32 [m][n] with unit column stride")
+    _check("kq_mxfp4_gemm_lowrank",
+           lib().kq_mxfp4_gemm_lowrank(_p(codes_a), _p(scales_a), _p(codes_w), _p(scales_w), m, n, k, _p(Z),
+                                       _p(codes_l), _p(scales_l), r, _p(out), out.stride(0), _stream_ptr(stream)))
+    return out
 
 
 def smoothquant_quantize_mxfp4(A, inv_scale, codes=None, scales=None, stream=None):

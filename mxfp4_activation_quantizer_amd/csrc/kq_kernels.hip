@@ -97,16 +97,26 @@ __device__ __forceinline__ void for_rows(const Geom &g, const uint16_t *__restri
     }
 }
 
-// Quantize fp32 values of a quad-held block and store codes and scale
-// (and y itself in check mode).
-template <bool DEBUG>
+// What a quad kernel writes besides codes and scales: nothing, the fp32
+// transform result (check mode), or that result rounded to bf16 (the 16-bit
+// activation a low-rank branch consumes).
+enum YOut { kYNone = 0, kYF32 = 1, kYBF16 = 2 };
+
+// Quantize fp32 values of a quad-held block and store codes and scale, and y
+// as YOUT asks (fp32 or bf16 [m][d]).
+template <int YOUT>
 __device__ __forceinline__ void finish_f32(const float y[8], const Geom &g, int64_t row, int j, int sub,
                                            int64_t c0, uint8_t *__restrict__ codes,
-                                           uint8_t *__restrict__ scales, float *__restrict__ ydbg) {
-    if (DEBUG) {
-        float4 *o = reinterpret_cast<float4 *>(ydbg + row * g.d + c0);
+                                           uint8_t *__restrict__ scales, void *__restrict__ yout) {
+    if (YOUT == kYF32) {
+        float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(yout) + row * g.d + c0);
         o[0] = make_float4(y[0], y[1], y[2], y[3]);
         o[1] = make_float4(y[4], y[5], y[6], y[7]);
+    } else if (YOUT == kYBF16) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (uint32_t)bf16_rne_bits(y[2 * i]) | ((uint32_t)bf16_rne_bits(y[2 * i + 1]) << 16);
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(yout) + row * g.d + c0) = make_uint4(w[0], w[1], w[2], w[3]);
     }
     uint32_t sbyte;
     const uint32_t packed = quantize_quad_f32(y, sbyte);
@@ -117,10 +127,10 @@ __device__ __forceinline__ void finish_f32(const float y[8], const Geom &g, int6
 // bf16 input, quad layout: SmoothQuant (T = diag(inv_scale)) or the Kronecker
 // transform (shear form, or the general stages for blocks that do not admit
 // it). Quantize-only runs on the flat tiles of kq_flat.hip.
-template <int MODE, bool DEBUG, int U, bool NT, int MAP, bool PRE>
+template <int MODE, int YOUT, int U, bool NT, int MAP, bool PRE>
 __global__ __launch_bounds__(kThreads) void bf16_quad_kernel(
     const uint16_t *__restrict__ A, Geom g, const float *__restrict__ params,
-    uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ ydbg) {
+    uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, void *__restrict__ ydbg) {
     static_assert(MODE == kSmooth || MODE == kKron, "quantize-only runs on the flat kernel");
     int j, sub;
     int64_t row0;
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void bf16_quad_kernel(
             widen8(x, y);
 #pragma unroll
             for (int i = 0; i < 8; ++i) y[i] = y[i] * sq[i];
-            finish_f32<DEBUG>(y, g, row, j, sub, c0, codes, scales, ydbg);
+            finish_f32<YOUT>(y, g, row, j, sub, c0, codes, scales, ydbg);
         });
     } else {
         // Per-block setup is shared through LDS when the workgroup's first row
@@ -168,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void bf16_quad_kernel(
                 float y[8];
                 widen8(x, y);
                 shear_apply8(y, S);
-                finish_f32<DEBUG>(y, g, row, j, sub, c0, codes, scales, ydbg);
+                finish_f32<YOUT>(y, g, row, j, sub, c0, codes, scales, ydbg);
             });
         } else {
             float f[20];
@@ -179,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void bf16_quad_kernel(
                 float y[8];
                 widen8(x, y);
                 kron_apply8(y, L);
-                finish_f32<DEBUG>(y, g, row, j, sub, c0, codes, scales, ydbg);
+                finish_f32<YOUT>(y, g, row, j, sub, c0, codes, scales, ydbg);
             });
         }
     }
@@ -377,177 +387,6 @@ __global__ __launch_bounds__(kThreads) void f32_kernel(
     }
 }
 
-// ---------------------------------------------------------------------------
-// W4A4 GEMM on MXFP4 operands: O[i][j] = sum_k deq(A)[i][k] deq(W)[j][k]
-// (Eq. 2's Q(A T) Q(W T^{-T})^T), fp32 accumulation on
-// v_mfma_scale_f32_16x16x128_f8f6f4 with both operands in E2M1. Lane l of a
-// wave supplies row l % 16 and the 32 consecutive k of group l / 16 (16 code
-// bytes) with that group's E8M0 byte as its scale, which is exactly the MX
-// layout of the codes/scales arrays; it receives O rows 4 (l / 16) + t, column
-// l % 16.
-//
-// A workgroup of 4 waves computes a 128 x 128 tile, each wave 64 x 64 (4 x 4
-// MFMA tiles), walking k in steps of 128 (64 code bytes and 4 scale bytes per
-// row). The A and W tiles of a step are staged through LDS, double-buffered:
-// every thread fetches its share of the next step's codes and scales into
-// registers before the MFMAs of the current step and stores them to the other
-// buffer after, one barrier per step. LDS rows are padded to 80 bytes so the 16
-// rows an operand read touches fall in distinct banks. Rows and columns past m
-// or n, and k groups past k, read zero codes (scale 2^0) and are not stored;
-// k must be a multiple of 32.
-// ---------------------------------------------------------------------------
-typedef int i32x8_t __attribute__((ext_vector_type(8)));
-
-struct GemmGeom {
-    int64_t m, n, k, ldo, tiles_n;
-};
-
-constexpr int kGemmTile = 128;
-
-// Staged rows of one operand tile: KS k blocks of 128 (64 code bytes each) per
-// stage, padded by 16 bytes so the 16 rows an operand read touches fall in
-// distinct banks.
-template <int KS>
-struct GemmStage {
-    static constexpr int kRow = KS * 64 + 16;
-    static constexpr int kLoads = KS * 2;  // 16-byte code loads per thread per operand
-};
-
-// This thread's share of one operand tile for the stage starting at code byte
-// kb0: rows (t >> 2) + 64 h, 16 bytes at column 16 (t & 3) + 64 c of each
-// 128-k block c, and, for threads below 128, row t's KS * 4 scale bytes.
-template <int KS>
-struct TileRegs {
-    uint4 code[KS][2];
-    uint32_t scl[KS];
-};
-
-template <int KS>
-__device__ __forceinline__ void fetch_tile(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
-                                           int64_t row_base, int64_t nrows, int64_t kbytes, int64_t kblocks,
-                                           int64_t kb0, TileRegs<KS> &R) {
-    const int t = threadIdx.x;
-    const int r0 = t >> 2, c16 = (t & 3) * 16;
-#pragma unroll
-    for (int c = 0; c < KS; ++c)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int64_t row = row_base + r0 + 64 * h, kb = kb0 + 64 * c + c16;
-            R.code[c][h] = make_uint4(0, 0, 0, 0);
-            if (row < nrows && kb < kbytes)
-                R.code[c][h] = *reinterpret_cast<const uint4 *>(codes + row * kbytes + kb);
-        }
-    if (t < kGemmTile) {
-        const int64_t row = row_base + t;
-#pragma unroll
-        for (int c = 0; c < KS; ++c) {
-            const int64_t g0 = kb0 / 16 + 4 * c;  // first 32-k group of this 128-k block
-            uint32_t v = 0x7F7F7F7Fu;             // 2^0 for rows and k groups past the ends
-            if (row < nrows) {
-                if ((kblocks & 3) == 0 && (reinterpret_cast<uintptr_t>(scales) & 3) == 0 && g0 + 4 <= kblocks) {
-                    v = *reinterpret_cast<const uint32_t *>(scales + row * kblocks + g0);
-                } else {
-                    v = 0;
-#pragma unroll
-                    for (int gi = 0; gi < 4; ++gi)
-                        v |= (g0 + gi < kblocks ? (uint32_t)scales[row * kblocks + g0 + gi] : 0x7Fu) << (8 * gi);
-                }
-            }
-            R.scl[c] = v;
-        }
-    }
-}
-
-template <int KS>
-__device__ __forceinline__ void stash_tile(uint8_t *codes_lds, uint32_t *scales_lds, const TileRegs<KS> &R) {
-    const int t = threadIdx.x;
-    const int r0 = t >> 2, c16 = (t & 3) * 16;
-#pragma unroll
-    for (int c = 0; c < KS; ++c)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-            *reinterpret_cast<uint4 *>(codes_lds + (r0 + 64 * h) * GemmStage<KS>::kRow + 64 * c + c16) = R.code[c][h];
-    if (t < kGemmTile)
-#pragma unroll
-        for (int c = 0; c < KS; ++c) scales_lds[c * kGemmTile + t] = R.scl[c];
-}
-
-template <int KS>
-__global__ __launch_bounds__(kThreads) void mxfp4_gemm_kernel(
-    const uint8_t *__restrict__ ca, const uint8_t *__restrict__ sa, const uint8_t *__restrict__ cw,
-    const uint8_t *__restrict__ sw, GemmGeom g, float *__restrict__ O) {
-    constexpr int ROW = GemmStage<KS>::kRow;
-    __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kGemmTile * ROW];
-    __shared__ __attribute__((aligned(16))) uint8_t b_lds[2][kGemmTile * ROW];
-    __shared__ uint32_t as_lds[2][KS * kGemmTile], bs_lds[2][KS * kGemmTile];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t tm = blockIdx.x / g.tiles_n, tn = blockIdx.x % g.tiles_n;
-    const int64_t m0 = tm * kGemmTile, n0 = tn * kGemmTile;
-    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;  // this wave's 64 x 64 within the tile
-    const int r = lane & 15, grp = lane >> 4;
-    const int64_t kbytes = g.k / 2, kblocks = g.k / 32;
-    const int64_t stages = (g.k + 128 * KS - 1) / (128 * KS);
-
-    floatx4_t acc[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-    TileRegs<KS> ra, rb;
-    fetch_tile<KS>(ca, sa, m0, g.m, kbytes, kblocks, 0, ra);
-    fetch_tile<KS>(cw, sw, n0, g.n, kbytes, kblocks, 0, rb);
-    stash_tile<KS>(a_lds[0], as_lds[0], ra);
-    stash_tile<KS>(b_lds[0], bs_lds[0], rb);
-    __syncthreads();
-    for (int64_t s = 0; s < stages; ++s) {
-        const int cur = (int)(s & 1);
-        if (s + 1 < stages) {
-            fetch_tile<KS>(ca, sa, m0, g.m, kbytes, kblocks, (s + 1) * 64 * KS, ra);
-            fetch_tile<KS>(cw, sw, n0, g.n, kbytes, kblocks, (s + 1) * 64 * KS, rb);
-        }
-#pragma unroll
-        for (int c = 0; c < KS; ++c) {
-            i32x8_t bv[4];
-            int bsc[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const uint4 q =
-                    *reinterpret_cast<const uint4 *>(b_lds[cur] + (wc + b * 16 + r) * ROW + 64 * c + grp * 16);
-                bv[b] = i32x8_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-                bsc[b] = (int)((bs_lds[cur][c * kGemmTile + wc + b * 16 + r] >> (8 * grp)) & 0xFFu);
-            }
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const uint4 q =
-                    *reinterpret_cast<const uint4 *>(a_lds[cur] + (wr + a * 16 + r) * ROW + 64 * c + grp * 16);
-                const i32x8_t av = i32x8_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-                const int asc = (int)((as_lds[cur][c * kGemmTile + wr + a * 16 + r] >> (8 * grp)) & 0xFFu);
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv[b], acc[a][b], 4, 4, 0, asc,
-                                                                                 0, bsc[b]);
-            }
-        }
-        if (s + 1 < stages) {
-            stash_tile<KS>(a_lds[cur ^ 1], as_lds[cur ^ 1], ra);
-            stash_tile<KS>(b_lds[cur ^ 1], bs_lds[cur ^ 1], rb);
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int64_t col = n0 + wc + b * 16 + r;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int64_t row = m0 + wr + a * 16 + grp * 4 + t;
-                if (row < g.m && col < g.n) O[row * g.ldo + col] = acc[a][b][t];
-            }
-        }
-}
-
 }  // namespace kq
 
 // ===========================================================================
@@ -656,9 +495,9 @@ bool make_mgeom(int64_t m, int64_t d, int64_t lda, int nb, int unroll, kq::MGeom
 // more rows, and the first 4 rows' loads are issued before the setup). Chosen
 // by sweeping tile counts, unroll depth, prefetching and the strip, flat and
 // column-per-wave mappings on the 18432 x 3072 and 18432 x 12288 shapes.
-template <int MODE, bool DEBUG>
+template <int MODE, int YOUT>
 kq_status launch_quad(const uint16_t *A, int64_t m, int64_t d, int64_t lda, const float *params,
-                      uint8_t *codes, uint8_t *scales, float *ydbg, kq_stream_t stream) {
+                      uint8_t *codes, uint8_t *scales, void *ydbg, kq_stream_t stream) {
     kq::Geom g;
     unsigned nwg;
     if (MODE == kq::kKron) {
@@ -667,17 +506,17 @@ kq_status launch_quad(const uint16_t *A, int64_t m, int64_t d, int64_t lda, cons
         // small inputs need the parallelism more than the amortized setup.
         if (!make_geom_strip(m, d, lda, 4, 8, g, nwg)) return KQ_ERR_SHAPE;
         if (nwg >= 1024) {
-            hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, DEBUG, 4, true, kq::kStrip, true>), dim3(nwg),
+            hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, YOUT, 4, true, kq::kStrip, true>), dim3(nwg),
                                dim3(kq::kThreads), 0, (hipStream_t)stream, A, g, params, codes, scales, ydbg);
             return launched();
         }
         if (!make_geom_strip(m, d, lda, 2, 2, g, nwg)) return KQ_ERR_SHAPE;
-        hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, DEBUG, 2, true, kq::kStrip, true>), dim3(nwg),
+        hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, YOUT, 2, true, kq::kStrip, true>), dim3(nwg),
                            dim3(kq::kThreads), 0, (hipStream_t)stream, A, g, params, codes, scales, ydbg);
         return launched();
     }
     if (!make_geom_strip(m, d, lda, 2, 2, g, nwg)) return KQ_ERR_SHAPE;
-    hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, DEBUG, 2, true, kq::kStrip, false>), dim3(nwg),
+    hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, YOUT, 2, true, kq::kStrip, false>), dim3(nwg),
                        dim3(kq::kThreads), 0, (hipStream_t)stream, A, g, params, codes, scales, ydbg);
     return launched();
 }
@@ -743,7 +582,9 @@ kq_status launch_fused(const uint16_t *A, int64_t m, int64_t d, int64_t lda, con
     const Form f = transform_form();
     if (f == kFormMfmaLds && (d / 32) % 16 == 0)
         return launch_mfma_lds<DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
-    if (f != kFormMfma) return launch_quad<kq::kKron, DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
+    if (f != kFormMfma)
+        return launch_quad<kq::kKron, DEBUG ? kq::kYF32 : kq::kYNone>(A, m, d, lda, factors, codes, scales, ydbg,
+                                                                       stream);
     if ((d / 32) % 2 == 0)
         return launch_mfma<2, DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
     return launch_mfma<1, DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
@@ -766,6 +607,18 @@ kq_status kq_transform_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, i
     return launch_fused<false>(A, m, d, lda, factors, codes, scales, nullptr, stream);
 }
 
+kq_status kq_transform_quantize_mxfp4_y16(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
+                                          const float *factors, uint8_t *codes, uint8_t *scales, uint16_t *y16,
+                                          kq_stream_t stream) {
+    kq_status s = check_shape(m, d, lda);
+    if (s != KQ_OK) return s;
+    if (m == 0 || d == 0) return KQ_OK;
+    if ((s = check_bf16_io(A, lda, codes, scales)) != KQ_OK) return s;
+    if (!factors || !y16) return KQ_ERR_NULL;
+    if (!aligned(factors, 16) || !aligned(y16, 16)) return KQ_ERR_ALIGN;
+    return launch_quad<kq::kKron, kq::kYBF16>(A, m, d, lda, factors, codes, scales, y16, stream);
+}
+
 kq_status kq_smoothquant_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
                                         const float *inv_scale, uint8_t *codes, uint8_t *scales,
                                         kq_stream_t stream) {
@@ -775,7 +628,7 @@ kq_status kq_smoothquant_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d,
     if ((s = check_bf16_io(A, lda, codes, scales)) != KQ_OK) return s;
     if (!inv_scale) return KQ_ERR_NULL;
     if (!aligned(inv_scale, 16)) return KQ_ERR_ALIGN;
-    return launch_quad<kq::kSmooth, false>(A, m, d, lda, inv_scale, codes, scales, nullptr, stream);
+    return launch_quad<kq::kSmooth, kq::kYNone>(A, m, d, lda, inv_scale, codes, scales, nullptr, stream);
 }
 
 kq_status kq_quantize_mxfp4_f32(const float *X, int64_t m, int64_t d, int64_t ldx, uint8_t *codes,
@@ -805,21 +658,6 @@ kq_status kq_inverse_fold_weights(const float *W, int64_t o, int64_t d, const fl
     if (!make_geom_flat(o, d, d, 1, 256 * 8, g, nwg)) return KQ_ERR_SHAPE;
     hipLaunchKernelGGL((kq::f32_kernel<kq::kKron>), dim3(nwg), dim3(kq::kThreads), 0,
                        (hipStream_t)stream, W, g, factors, nullptr, nullptr, W_folded);
-    return launched();
-}
-
-kq_status kq_mxfp4_gemm(const uint8_t *codes_a, const uint8_t *scales_a, const uint8_t *codes_w,
-                        const uint8_t *scales_w, int64_t m, int64_t n, int64_t k, float *O, int64_t ldo,
-                        kq_stream_t stream) {
-    if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || ldo < n) return KQ_ERR_SHAPE;
-    if (m == 0 || n == 0) return KQ_OK;
-    if (!codes_a || !scales_a || !codes_w || !scales_w || !O) return KQ_ERR_NULL;
-    if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || (k / 2) % 16 != 0) return KQ_ERR_ALIGN;
-    const int64_t tiles_m = (m + kq::kGemmTile - 1) / kq::kGemmTile, tiles_n = (n + kq::kGemmTile - 1) / kq::kGemmTile;
-    if (tiles_m * tiles_n > 0x7FFFFFFF || m > INT64_MAX / 4 / (ldo > 0 ? ldo : 1)) return KQ_ERR_SHAPE;
-    kq::GemmGeom g{m, n, k, ldo, tiles_n};
-    hipLaunchKernelGGL(kq::mxfp4_gemm_kernel<2>, dim3((unsigned)(tiles_m * tiles_n)), dim3(kq::kThreads), 0,
-                       (hipStream_t)stream, codes_a, scales_a, codes_w, scales_w, g, O);
     return launched();
 }
 

@@ -74,6 +74,18 @@ GOOD = P(0x10000)  # never dereferenced: every case below fails before a launch
     ("kq_hadamard_quantize_mxfp4", (GOOD, 4, 64, 64, 64, GOOD, GOOD, P(0x10004), None), kq.KQ_ERR_ALIGN),
     ("kq_hadamard_quantize_mxfp4", (GOOD, 4, 64, 68, 64, GOOD, GOOD, None, None), kq.KQ_ERR_ALIGN),
     ("kq_hadamard_quantize_mxfp4", (None, 0, 1024, 1024, 1024, None, None, None, None), kq.KQ_OK),
+    ("kq_transform_quantize_mxfp4_y16", (GOOD, 4, 64, 64, GOOD, GOOD, GOOD, None, None), kq.KQ_ERR_NULL),
+    ("kq_transform_quantize_mxfp4_y16", (GOOD, 4, 64, 64, GOOD, GOOD, GOOD, P(0x10008), None), kq.KQ_ERR_ALIGN),
+    ("kq_lowrank_project", (GOOD, 4, 64, 64, GOOD, GOOD, 48, GOOD, None), kq.KQ_ERR_SHAPE),
+    ("kq_lowrank_project", (GOOD, 4, 64, 60, GOOD, GOOD, 32, GOOD, None), kq.KQ_ERR_SHAPE),
+    ("kq_lowrank_project", (GOOD, 4, 64, 72, GOOD, GOOD, 32, P(0x10004), None), kq.KQ_ERR_ALIGN),
+    ("kq_lowrank_project", (None, 4, 64, 64, GOOD, GOOD, 32, GOOD, None), kq.KQ_ERR_NULL),
+    ("kq_mxfp4_gemm_lowrank", (GOOD, GOOD, GOOD, GOOD, 4, 4, 64, GOOD, GOOD, GOOD, 0, GOOD, 4, None),
+     kq.KQ_ERR_SHAPE),
+    ("kq_mxfp4_gemm_lowrank", (GOOD, GOOD, GOOD, GOOD, 4, 4, 64, None, GOOD, GOOD, 32, GOOD, 4, None),
+     kq.KQ_ERR_NULL),
+    ("kq_mxfp4_gemm_lowrank", (GOOD, GOOD, GOOD, GOOD, 4, 4, 64, P(0x10004), GOOD, GOOD, 32, GOOD, 4, None),
+     kq.KQ_ERR_ALIGN),
     ("kq_gemm_f32", (0, 0, 4, 4, 4, 1.0, None, 4, GOOD, 4, 0.0, None, 4, GOOD, 4, None), kq.KQ_ERR_NULL),
     ("kq_gemm_f32", (0, 0, 4, 4, 8, 1.0, GOOD, 4, GOOD, 4, 0.0, None, 4, GOOD, 4, None), kq.KQ_ERR_SHAPE),
     ("kq_gemm_f32", (0, 0, 4, 4, 4, 1.0, GOOD, 4, GOOD, 4, 1.0, None, 4, GOOD, 4, None), kq.KQ_ERR_NULL),

@@ -1,0 +1,141 @@
+"""GPU parity of the W4A4 layer with its low-rank branch (Sec. 3.4 Eq. 11, App. D):
+the fused quantizer's bf16 activation output, the projection Z = X16 Q(R)^T, the
+GEMM with the low-rank epilogue, and the whole layer on the FLUX 18432x3072x3072
+config against the oracle (oracle/lowrank.py) on sampled rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import lowrank
+
+pytestmark = pytest.mark.gpu
+
+
+def case(msg):
+    print("[case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch
+
+
+@pytest.fixture(scope="module")
+def kq():
+    import mxfp4_activation_quantizer_amd as kq
+    kq.lib()
+    return kq
+
+
+def dev_bf16(torch, A):
+    return torch.from_numpy(np.ascontiguousarray(A).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("m,d", [(70, 96), (256, 3072)])
+def test_y16_is_rounded_y(torch_dev, kq, m, d):
+    torch = torch_dev
+    case("y16 %dx%d" % (m, d))
+    A = synth.random_bf16_matrix(m, d, seed=m + d, scale=4.0)
+    fac = torch.from_numpy(synth.lu_perturbed_factors(d // 32, 3)).cuda()
+    Ad = dev_bf16(torch, A)
+    y = torch.empty((m, d), dtype=torch.float32, device="cuda")
+    c1, s1 = kq.transform_quantize_mxfp4(Ad, fac, y_debug=y)
+    c2, s2, y16 = kq.transform_quantize_mxfp4_y16(Ad, fac)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(s1, s2)
+    assert torch.equal(y16.view(torch.int16), y.to(torch.bfloat16).view(torch.int16))
+
+
+def quantize_host(orc, X):
+    codes, scales = orc.quantize_f64(np.asarray(X, dtype=np.float64))
+    return codes, scales
+
+
+@pytest.mark.parametrize("m,d,r", [(100, 96, 32), (300, 3072, 128), (64, 512, 160)])
+def test_lowrank_project(torch_dev, kq, orc, m, d, r):
+    torch = torch_dev
+    case("project %dx%d r=%d" % (m, d, r))
+    X = synth.random_bf16_matrix(m, d, seed=d + r)
+    R = np.random.default_rng(r).standard_normal((r, d)) / np.sqrt(d)
+    cr, sr = quantize_host(orc, R)
+    Z = kq.lowrank_project(dev_bf16(torch, X), torch.from_numpy(cr).cuda(), torch.from_numpy(sr).cuda())
+    torch.cuda.synchronize()
+    Xf = synth.bf16_bits_to_f32(X).astype(np.float64)
+    Rq = orc.dequantize(cr, sr, d)
+    ref = Xf @ Rq.T
+    bound = 2.0 ** -22 * d * (np.abs(Xf) @ np.abs(Rq).T) + 1e-30
+    assert (np.abs(Z.cpu().numpy() - ref) <= bound).all()
+
+
+@pytest.mark.parametrize("m,n,k,r", [(130, 70, 96, 32), (256, 256, 512, 128)])
+def test_gemm_lowrank_epilogue(torch_dev, kq, orc, m, n, k, r):
+    torch = torch_dev
+    case("gemm lowrank %dx%dx%d r=%d" % (m, n, k, r))
+    rng = np.random.default_rng(m + n + k + r)
+    ca, sa = quantize_host(orc, rng.standard_normal((m, k)))
+    cw, sw = quantize_host(orc, rng.standard_normal((n, k)) / np.sqrt(k))
+    cl, sl = quantize_host(orc, rng.standard_normal((n, r)) / np.sqrt(r))
+    Z = (rng.standard_normal((m, r)) * 3.0).astype(np.float32)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    O = kq.mxfp4_gemm_lowrank(t(ca), t(sa), t(cw), t(sw), t(Z), t(cl), t(sl))
+    O0 = kq.mxfp4_gemm(t(ca), t(sa), t(cw), t(sw))
+    torch.cuda.synchronize()
+    Lq = orc.dequantize(cl, sl, r)
+    low = Z.astype(np.float64) @ Lq.T
+    ref = orc.gemm_dequant(ca, sa, cw, sw, k) + low
+    # the split of Z is exact to 2^-16 relative; fp32 sums add a few 2^-24 per term
+    bound = (2.0 ** -15 + r * 2.0 ** -23) * (np.abs(Z.astype(np.float64)) @ np.abs(Lq).T) + \
+        2.0 ** -20 * np.abs(ref) + 1e-30
+    assert (np.abs(O.cpu().numpy() - ref) <= bound).all()
+    # without the branch the epilogue kernel is the plain GEMM
+    assert np.allclose(O.cpu().numpy() - low, O0.cpu().numpy(), rtol=0, atol=1e-4 * np.abs(low).max())
+
+
+def test_lowrank_layer_flux(torch_dev, kq, orc):
+    """Eq. 11 on the FLUX 18432x3072 activations with the 3072x3072 weights and the
+    workload's factors; L, R (rank 128) are the top singular pairs of W T^{-T},
+    computed offline on the host. GPU: fold, residual W~ - L R (fp32 GEMM),
+    quantize residual, L and R, fused transform + quantize with the bf16 output,
+    projection, GEMM with the low-rank epilogue. Checked against the oracle's layer
+    on sampled rows; the output error with and without the branch is reported."""
+    torch = torch_dev
+    case("lowrank layer 18432x3072x3072 r=128")
+    w = synth.workload("flux_18432x3072")
+    W = synth.weights(3072, 3072, 1004)
+    fac = w.factors
+    r = 128
+    Wt = orc.inverse_fold(W, fac)
+    U, S, Vt = np.linalg.svd(Wt, full_matrices=False)
+    L = (U[:, :r] * S[:r]).astype(np.float32)
+    R = Vt[:r].astype(np.float32)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    facd, Ld, Rd = t(fac), t(L), t(R)
+    A = dev_bf16(torch, w.A)
+    Wtd = kq.inverse_fold_weights(t(W), facd)
+    resid = kq.gemm_f32(Ld, Rd, alpha=-1.0, beta=1.0, C=Wtd)
+    cw, sw = kq.quantize_mxfp4_f32(resid)
+    cr, sr = kq.quantize_mxfp4_f32(Rd)
+    cl, sl = kq.quantize_mxfp4_f32(Ld)
+    ca, sa, y16 = kq.transform_quantize_mxfp4_y16(A, facd)
+    Z = kq.lowrank_project(y16, cr, sr)
+    O = kq.mxfp4_gemm_lowrank(ca, sa, cw, sw, Z, cl, sl)
+    cw0, sw0 = kq.quantize_mxfp4_f32(Wtd)
+    O0 = kq.mxfp4_gemm(ca, sa, cw0, sw0)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(13).choice(w.m, 96, replace=False))
+    idx = torch.from_numpy(rows).cuda()
+    og = O.index_select(0, idx).cpu().numpy().astype(np.float64)
+    ref, _ = lowrank.layer(w.A[rows], W, fac, L.astype(np.float64), R.astype(np.float64), orc)
+    rel = np.linalg.norm(og - ref) / np.linalg.norm(ref)
+    exact = synth.bf16_bits_to_f32(w.A[rows]).astype(np.float64) @ W.astype(np.float64).T
+    e_lr = np.linalg.norm(og - exact)
+    e_plain = np.linalg.norm(O0.index_select(0, idx).cpu().numpy().astype(np.float64) - exact)
+    print("[lowrank] rel(gpu layer vs oracle) %.2e; |O - A W^T|: with the rank-%d branch %.2f, "
+          "without %.2f" % (rel, r, e_lr, e_plain), flush=True)
+    assert rel <= 1e-3
