@@ -238,9 +238,35 @@ def extras(torch, kq, synth, flux_sets, reps=100, warmup=20):
                                          "TFLOPs": round(flops / (med * 1e-6) / 1e12, 1),
                                          "pct_fp4_peak": round(100 * flops / (med * 1e-6) / 10.1e15, 2)}
     log("weight side / gemm: %s %s" % (out["weight_fold_3072x3072"], out["w4a4_gemm_18432x3072x3072"]))
+    out["w4a4_layer_lowrank_18432x3072x3072_r128"] = lowrank_layer_timing(torch, kq, A, fac, cw, sw, W)
+    log("low-rank layer: %s" % out["w4a4_layer_lowrank_18432x3072x3072_r128"])
     out["calibration_4096x3072x3072"] = calibration_timing(torch, kq, synth, A, W)
     log("calibration: %s" % out["calibration_4096x3072x3072"])
     return out
+
+
+def lowrank_layer_timing(torch, kq, A, fac, cw, sw, W, r=128, reps=20):
+    """Eq. 11 at inference on the FLUX 18432x3072 input with 3072x3072 weights and a
+    rank-128 branch (random L, R; timing only): fused quantizer with the bf16 output,
+    projection Z = X16 Q(R)^T, GEMM with the low-rank epilogue; against the plain
+    quantizer + W4A4 GEMM."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    L = torch.randn((W.shape[0], r), device="cuda", generator=g) / r ** 0.5
+    R = torch.randn((r, W.shape[1]), device="cuda", generator=g) / W.shape[1] ** 0.5
+    cr, sr = kq.quantize_mxfp4_f32(R)
+    cl, sl = kq.quantize_mxfp4_f32(L)
+    ca, sa, y16 = kq.transform_quantize_mxfp4_y16(A, fac)
+    Z = kq.lowrank_project(y16, cr, sr)
+    O = kq.mxfp4_gemm_lowrank(ca, sa, cw, sw, Z, cl, sl)
+    med = lambda f: round(float(np.median(_events_us(torch, f, reps, 3))), 1)
+    res = {"quantize_y16_us": med(lambda: kq.transform_quantize_mxfp4_y16(A, fac, codes=ca, scales=sa, y16=y16)),
+           "project_us": med(lambda: kq.lowrank_project(y16, cr, sr, out=Z)),
+           "gemm_lowrank_us": med(lambda: kq.mxfp4_gemm_lowrank(ca, sa, cw, sw, Z, cl, sl, out=O)),
+           "quantize_us": med(lambda: kq.transform_quantize_mxfp4(A, fac, codes=ca, scales=sa)),
+           "gemm_us": med(lambda: kq.mxfp4_gemm(ca, sa, cw, sw, out=O))}
+    res["layer_with_branch_us"] = round(res["quantize_y16_us"] + res["project_us"] + res["gemm_lowrank_us"], 1)
+    res["layer_plain_us"] = round(res["quantize_us"] + res["gemm_us"], 1)
+    return res
 
 
 def calibration_timing(torch, kq, synth, A, W, steps=20):

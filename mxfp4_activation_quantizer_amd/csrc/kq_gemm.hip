@@ -50,64 +50,110 @@ __device__ __forceinline__ void split_bf16x8(const float x[8], bf16x8_t &hi, bf1
 
 // Z = X Q(R)^T: X bf16 [m][ldx] (the branch's 16-bit activations), R MXFP4
 // [r][d] (codes [r][d/2], scales [r][d/32]), Z fp32 [m][r]. A workgroup
-// computes 64 rows x 128 columns of Z (each wave 32 x 64 = 2 x 4 MFMA tiles),
-// walking d in steps of 32 with v_mfma_f32_16x16x32_bf16: lane l supplies row
-// l % 16 and k = 8 (l / 16) .. +7 of X (one 16-byte load) and of the decoded R
-// row; it receives rows 4 (l / 16) + t, column l % 16.
+// computes 64 rows x 128 columns of Z, each wave 16 rows x 128 columns (8 MFMA
+// tiles), walking d in steps of 128 with v_mfma_f32_16x16x32_bf16 (four k
+// sub-steps of 32 per step): lane l supplies row l % 16 and k = 8 (l / 16) .. +7
+// of each sub-step of X (four 16-byte loads, fetched one step ahead) and of the
+// decoded R column; it receives rows 4 (l / 16) + t, column l % 16. The
+// workgroup decodes each step's 128 x 128 slice of R once into LDS (thread t:
+// column t / 2, 64 k), double-buffered, one barrier per step; staged columns are
+// padded by 16 bytes so operand reads hit distinct banks. d must be a multiple
+// of 32; a step past d reads zero codes.
 struct ProjGeom {
     int64_t m, d, ldx, r, tiles_r;
 };
+
+constexpr int kProjRow = 128 * 2 + 16;  // bytes per staged R column: 128 bf16 + 16 of padding
 
 __global__ __launch_bounds__(kThreads) void lowrank_project_kernel(const uint16_t *__restrict__ X, ProjGeom g,
                                                                    const uint8_t *__restrict__ cr,
                                                                    const uint8_t *__restrict__ sr,
                                                                    float *__restrict__ Z) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) uint8_t rl[2][128 * kProjRow];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int64_t tm = blockIdx.x / g.tiles_r, tr = blockIdx.x % g.tiles_r;
-    const int64_t row0 = tm * 64 + (wave >> 1) * 32, col0 = tr * 128 + (wave & 1) * 64;
-    const int r = lane & 15, grp = lane >> 4;
-    floatx4_t acc[2][4];
+    const int64_t row = tm * 64 + wave * 16 + (lane & 15), col0 = tr * 128;
+    const int grp = lane >> 4;
+    // this thread's share of an R slice: column dc, k half dh (64 k = 32 code bytes, 2 scales)
+    const int dc = t >> 1, dh = t & 1;
+    const int64_t rn = col0 + dc;
+    struct RRegs {
+        uint4 c[2];
+        uint32_t s[2];
+    };
+    auto fetch_r = [&](int64_t k0, RRegs &R) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    for (int64_t k0 = 0; k0 < g.d; k0 += 32) {
-        const int64_t k = k0 + 8 * grp;
-        bf16x8_t xa[2], rb[4];
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-            const int64_t row = row0 + a * 16 + r;
-            uint4 q = make_uint4(0, 0, 0, 0);
-            if (row < g.m) q = load_stream(reinterpret_cast<const uint4 *>(X + row * g.ldx + k), true);
-            xa[a] = as_bf16x8(q);
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int64_t n = col0 + b * 16 + r;
-            uint32_t c8 = 0, s = 127;
-            if (n < g.r) {
-                c8 = *reinterpret_cast<const uint32_t *>(cr + n * (g.d / 2) + k / 2);
-                s = sr[n * (g.d / 32) + k0 / 32];
+        for (int h = 0; h < 2; ++h) {
+            const int64_t k = k0 + 64 * dh + 32 * h;  // a 32-k group
+            R.c[h] = make_uint4(0, 0, 0, 0);
+            R.s[h] = 127;
+            if (rn < g.r && k < g.d) {
+                R.c[h] = *reinterpret_cast<const uint4 *>(cr + rn * (g.d / 2) + k / 2);
+                R.s[h] = sr[rn * (g.d / 32) + k / 32];
             }
-            rb[b] = decode_fp4x8_bf16(c8, s);
+        }
+    };
+    auto stash_r = [&](uint8_t *buf, const RRegs &R) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint8_t *dst = buf + dc * kProjRow + 128 * dh + 64 * h;
+            *reinterpret_cast<bf16x8_t *>(dst) = decode_fp4x8_bf16(R.c[h].x, R.s[h]);
+            *reinterpret_cast<bf16x8_t *>(dst + 16) = decode_fp4x8_bf16(R.c[h].y, R.s[h]);
+            *reinterpret_cast<bf16x8_t *>(dst + 32) = decode_fp4x8_bf16(R.c[h].z, R.s[h]);
+            *reinterpret_cast<bf16x8_t *>(dst + 48) = decode_fp4x8_bf16(R.c[h].w, R.s[h]);
+        }
+    };
+    auto fetch_x = [&](int64_t k0, uint4 q[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t k = k0 + 32 * u + 8 * grp;
+            q[u] = make_uint4(0, 0, 0, 0);
+            if (row < g.m && k < g.d) q[u] = load_stream(reinterpret_cast<const uint4 *>(X + row * g.ldx + k), true);
+        }
+    };
+    floatx4_t acc[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    RRegs R;
+    uint4 xq[4], xn[4];
+    fetch_r(0, R);
+    fetch_x(0, xq);
+    stash_r(rl[0], R);
+    __syncthreads();
+    const int64_t steps = (g.d + 127) / 128;
+    for (int64_t st = 0; st < steps; ++st) {
+        const int cur = (int)(st & 1);
+        if (st + 1 < steps) {
+            fetch_r((st + 1) * 128, R);
+            fetch_x((st + 1) * 128, xn);
         }
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int u = 0; u < 4; ++u) {
+            const bf16x8_t xa = as_bf16x8(xq[u]);
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[a], rb[b], acc[a][b], 0, 0, 0);
+            for (int b = 0; b < 8; ++b) {
+                const bf16x8_t rb = *reinterpret_cast<const bf16x8_t *>(rl[cur] + (b * 16 + (lane & 15)) * kProjRow +
+                                                                        64 * u + 16 * grp);
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, rb, acc[b], 0, 0, 0);
+            }
+        }
+        if (st + 1 < steps) {
+            stash_r(rl[cur ^ 1], R);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) xq[u] = xn[u];
+        }
+        __syncthreads();
     }
+    const int64_t orow0 = tm * 64 + wave * 16 + grp * 4;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < 8; ++b) {
+        const int64_t col = col0 + b * 16 + (lane & 15);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int64_t col = col0 + b * 16 + r;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int64_t row = row0 + a * 16 + grp * 4 + t;
-                if (row < g.m && col < g.r) Z[row * g.r + col] = acc[a][b][t];
-            }
+        for (int tt = 0; tt < 4; ++tt) {
+            const int64_t orow = orow0 + tt;
+            if (orow < g.m && col < g.r) Z[orow * g.r + col] = acc[b][tt];
         }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -271,39 +317,67 @@ __global__ __launch_bounds__(kThreads) void mxfp4_gemm_kernel(
         __syncthreads();
     }
     if (LR) {
-        // Low-rank term Z Q(L)^T into the same accumulators: Z fp32 [m][r] split
-        // as hi + lo bf16 (exact to 2^-16 relative), Q(L) decoded to bf16 (exact),
-        // two v_mfma_f32_16x16x32_bf16 per tile pair and 32 k of r.
-        for (int64_t kk = 0; kk < g.r; kk += 32) {
-            const int64_t k = kk + 8 * grp;
-            bf16x8_t lb[4];
+        // Low-rank term Z Q(L)^T into the same accumulators, 64 of r at a time:
+        // the workgroup stages the tile's Z rows split as hi + lo bf16 (exact to
+        // 2^-16 relative) in the free A buffers and its decoded L rows (exact in
+        // bf16) in a B buffer, all loads issued at once (thread t: row or column
+        // t / 2, 32 of r), then each wave runs two v_mfma_f32_16x16x32_bf16 per
+        // tile pair and 32 of r from LDS. Rows 144 bytes apart, as above.
+        static_assert(GemmStage<KS>::kRow >= 144, "staged rows must hold 64 bf16");
+        constexpr int SR = GemmStage<KS>::kRow;
+        uint8_t *zh_lds = a_lds[0], *zl_lds = a_lds[1], *l_lds = b_lds[0];
+        const int t = threadIdx.x, sr_ = t >> 1, sh = t & 1;
+        for (int64_t r0 = 0; r0 < g.r; r0 += 64) {
+            const int64_t rc = r0 + 32 * sh;  // this thread's 32 of r
+            float4 zv[8];
+            const int64_t zrow = m0 + sr_;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int64_t nrow = n0 + wc + b * 16 + r;
-                uint32_t c8 = 0, s = 127;
-                if (nrow < g.n) {
-                    c8 = *reinterpret_cast<const uint32_t *>(cl + nrow * (g.r / 2) + k / 2);
-                    s = sl[nrow * (g.r / 32) + kk / 32];
-                }
-                lb[b] = decode_fp4x8_bf16(c8, s);
+            for (int q = 0; q < 8; ++q) zv[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (zrow < g.m && rc < g.r) {
+                const float4 *p = reinterpret_cast<const float4 *>(Z + zrow * g.r + rc);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) zv[q] = p[q];
+            }
+            const int64_t lrow = n0 + sr_;
+            uint4 lc = make_uint4(0, 0, 0, 0);
+            uint32_t ls = 127;
+            if (lrow < g.n && rc < g.r) {
+                lc = *reinterpret_cast<const uint4 *>(cl + lrow * (g.r / 2) + rc / 2);
+                ls = sl[lrow * (g.r / 32) + rc / 32];
             }
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int64_t row = m0 + wr + a * 16 + r;
-                float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                if (row < g.m) {
-                    const float4 *p = reinterpret_cast<const float4 *>(Z + row * g.r + k);
-                    const float4 u = p[0], v = p[1];
-                    z[0] = u.x; z[1] = u.y; z[2] = u.z; z[3] = u.w; z[4] = v.x; z[5] = v.y; z[6] = v.z; z[7] = v.w;
-                }
-                bf16x8_t zh, zl;
-                split_bf16x8(z, zh, zl);
+            for (int q = 0; q < 4; ++q) {
+                const float z8[8] = {zv[2 * q].x, zv[2 * q].y, zv[2 * q].z, zv[2 * q].w,
+                                     zv[2 * q + 1].x, zv[2 * q + 1].y, zv[2 * q + 1].z, zv[2 * q + 1].w};
+                bf16x8_t h, l;
+                split_bf16x8(z8, h, l);
+                *reinterpret_cast<bf16x8_t *>(zh_lds + sr_ * SR + 64 * sh + 16 * q) = h;
+                *reinterpret_cast<bf16x8_t *>(zl_lds + sr_ * SR + 64 * sh + 16 * q) = l;
+            }
+            const uint32_t lw[4] = {lc.x, lc.y, lc.z, lc.w};
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zh, lb[b], acc[a][b], 0, 0, 0);
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zl, lb[b], acc[a][b], 0, 0, 0);
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<bf16x8_t *>(l_lds + sr_ * SR + 64 * sh + 16 * q) = decode_fp4x8_bf16(lw[q], ls);
+            __syncthreads();
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                bf16x8_t lb[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    lb[b] = *reinterpret_cast<const bf16x8_t *>(l_lds + (wc + b * 16 + r) * SR + 64 * kk + 16 * grp);
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int off = (wr + a * 16 + r) * SR + 64 * kk + 16 * grp;
+                    const bf16x8_t zh = *reinterpret_cast<const bf16x8_t *>(zh_lds + off);
+                    const bf16x8_t zl = *reinterpret_cast<const bf16x8_t *>(zl_lds + off);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zh, lb[b], acc[a][b], 0, 0, 0);
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zl, lb[b], acc[a][b], 0, 0, 0);
+                    }
                 }
             }
+            __syncthreads();
         }
     }
 #pragma unroll

@@ -73,7 +73,7 @@ def test_lowrank_project(torch_dev, kq, orc, m, d, r):
     assert (np.abs(Z.cpu().numpy() - ref) <= bound).all()
 
 
-@pytest.mark.parametrize("m,n,k,r", [(130, 70, 96, 32), (256, 256, 512, 128)])
+@pytest.mark.parametrize("m,n,k,r", [(130, 70, 96, 32), (256, 256, 512, 128), (200, 130, 256, 160)])
 def test_gemm_lowrank_epilogue(torch_dev, kq, orc, m, n, k, r):
     torch = torch_dev
     case("gemm lowrank %dx%dx%d r=%d" % (m, n, k, r))
