@@ -202,52 +202,10 @@ __device__ __forceinline__ void kron_apply8(float x[8], const KronLane &L) {
 }
 
 // ---------------------------------------------------------------------------
-// Shear form of the same butterfly. Each factor splits exactly as
-//   G = S D,  S = [[1, G01/G11], [G10/G00, 1]],  D = diag(G00, G11),
-// and by the mixed-product rule of Kronecker products
-//   K = (S1 D1) (x) ... (x) (S5 D5) = (S1 (x) ... (x) S5) (D1 (x) ... (x) D5).
-// So the five stages become unit-diagonal shears, one fma per element each,
-// (x0, x1) -> (x0 + q x1, x1 + p x0) with p = G01/G11, q = G10/G00, followed by
-// one multiply per channel with the product of the five diagonal entries that
-// belong to it. Every intermediate is the direct butterfly's intermediate
-// divided by a per-channel constant, so rounding errors stay relative to the
-// same quantities. A block takes this path only if every G00 and G11 is
-// nonzero and the ratios stay below 2^20 in magnitude; otherwise (a swap
-// factor, say) it runs the general stages above.
+// Unit-diagonal shear stages (the kernels' shear form of the butterfly):
+// (x0, x1) -> (x0 + q x1, x1 + p x0) for each pair of channels that differ in
+// the stage's bit.
 // ---------------------------------------------------------------------------
-struct ShearLane {
-    float c1, c2;                  // cross-lane: y_self = x_self + c * x_partner
-    float p3, q3, p4, q4, p5, q5;  // in-lane stages
-    float dscale[8];               // per-channel product of the diagonal entries
-    bool ok;
-};
-
-// The ratios use the hardware reciprocal (about 1 ulp); they are coefficients
-// of an exact refactoring, so a last-bit difference only moves y by rounding.
-__device__ __forceinline__ void shear_lane_setup(const float *f20, int sub, ShearLane &S) {
-    float p[5], q[5];
-    bool ok = true;
-#pragma unroll
-    for (int k = 0; k < 5; ++k) {
-        const float g00 = f20[4 * k], g01 = f20[4 * k + 1], g10 = f20[4 * k + 2], g11 = f20[4 * k + 3];
-        const float lim = 0x1.0p20f;
-        ok = ok && fabsf(g01) <= lim * fabsf(g11) && fabsf(g10) <= lim * fabsf(g00) && g00 != 0.f && g11 != 0.f;
-        p[k] = g01 * __builtin_amdgcn_rcpf(g11);
-        q[k] = g10 * __builtin_amdgcn_rcpf(g00);
-    }
-    const int b4 = (sub >> 1) & 1, b3 = sub & 1;
-    S.c1 = b4 ? p[0] : q[0];
-    S.c2 = b3 ? p[1] : q[1];
-    S.p3 = p[2]; S.q3 = q[2];
-    S.p4 = p[3]; S.q4 = q[3];
-    S.p5 = p[4]; S.q5 = q[4];
-    const float d12 = f20[0 + 3 * b4] * f20[4 + 3 * b3];  // G1[b4][b4] G2[b3][b3]
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        S.dscale[i] = d12 * f20[8 + 3 * ((i >> 2) & 1)] * f20[12 + 3 * ((i >> 1) & 1)] * f20[16 + 3 * (i & 1)];
-    S.ok = ok;
-}
-
 // The block's 20 factor entries with five 16-byte loads (factors are 16-byte aligned).
 __device__ __forceinline__ void load_factors20(const float *p, float f[20]) {
 #pragma unroll
@@ -289,16 +247,6 @@ __device__ __forceinline__ void shear_stage(float x[8], float p, float q) {
 
 __device__ __forceinline__ void fmac_partner_xor2(float x[8], float c) { KQ_FMAC_DPP8("quad_perm:[2,3,0,1]"); }
 __device__ __forceinline__ void fmac_partner_xor1(float x[8], float c) { KQ_FMAC_DPP8("quad_perm:[1,0,3,2]"); }
-
-__device__ __forceinline__ void shear_apply8(float x[8], const ShearLane &S) {
-    fmac_partner_xor2(x, S.c1);  // G1: channel bit 4 = bit 1 of sub
-    fmac_partner_xor1(x, S.c2);  // G2: channel bit 3 = bit 0 of sub
-    shear_stage<4>(x, S.p3, S.q3);
-    shear_stage<2>(x, S.p4, S.q4);
-    shear_stage<1>(x, S.p5, S.q5);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = x[i] * S.dscale[i];
-}
 
 // ---------------------------------------------------------------------------
 // Materialized form on MFMA: per block, D = K^T X^T with

@@ -5,15 +5,17 @@
 // j, y = a . K^(j) with K^(j) = G1 (x) G2 (x) G3 (x) G4 (x) G5 (Sec. 3.2 Eq. 5,
 // Sec. 3.5.1 Eq. 12), then MXFP4 (Sec. 3.1; Sec. 4.1 "Data format", App. D).
 //
-// Work mapping (the strip kernels here: SmoothQuant and the fused transform;
+// Work mapping of the bf16 kernels here (SmoothQuant and the fused transform;
 // quantize-only and the Hadamard baselines use the flat tiles of kq_flat.hip):
-// a workgroup of 256 lanes = 64 quads; a quad
-// owns one 32-channel block of one row (16 bytes per lane). The 64 quads cover
-// CB = 2^cb_log2 consecutive blocks of R = 64 / CB consecutive rows, so every
-// row segment a workgroup touches is CB * 64 contiguous bytes. A workgroup
-// stays on one column group (its per-block parameters load once into
-// registers) and walks `iters` row tiles of one slab. The op is HBM-bound:
-// 2 bytes in, 0.5 + 1/32 bytes out per element.
+// row-wave strips. A quad of lanes owns one 32-channel block of one row (16
+// bytes per lane), a wave 16 consecutive blocks (one 1 KB segment) of one row,
+// and a workgroup NW waves on NW consecutive rows of the same segment, walking
+// `iters` such row groups. Rows are therefore wave-uniform: every address is a
+// per-row scalar base (a buffer resource) plus a per-lane offset that never
+// changes, so the vector ALU spends nothing on addressing. The op is HBM-bound
+// in principle (2 bytes in, 0.5 + 1/32 bytes out per element), but the
+// transform's arithmetic is close to the VALU budget, which is why the loop
+// carries nothing else.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -28,170 +30,302 @@ namespace kq {
 constexpr int kThreads = 256;
 
 
-// Workgroup -> work mapping of the quad kernels (a workgroup is 64 quads, a
-// quad owns one 32-channel block of one row at a time).
-//  kStrip: the 64 quads cover CB = 2^cb_log2 consecutive blocks of R = 64 / CB
-//          consecutive rows; workgroup w takes column group w % ncg and row
-//          slab w / ncg and walks `iters` row tiles of that slab (rstep = R).
-//  kFlat:  blocks are numbered row-major (b = row * nblk + j); workgroup w,
-//          quad q starts at block 64 w + q and advances by the whole grid
-//          (64 gridDim.x blocks, a multiple of nblk, so j stays fixed) per
-//          sweep, i.e. by rstep = 64 gridDim.x / nblk rows.
-// In both, a quad keeps one block column for its whole life, so per-block
-// parameters load once.
-enum Map { kStrip = 0, kFlat = 1 };
-
+// Grid-stride mapping of the fp32 kernels (fold, fp32 quantize): blocks are
+// numbered row-major (b = row * nblk + j); workgroup w, quad q starts at block
+// 64 w + q and advances by the whole grid (64 gridDim.x blocks, a multiple of
+// nblk, so j stays fixed) per sweep, i.e. by rstep = 64 gridDim.x / nblk rows.
+// A quad keeps one block column for its whole life, so per-block parameters
+// load once.
 struct Geom {
     int64_t m, lda, d, rstep;
-    int nblk, iters, cb_log2, ncg;
+    int nblk, iters;
 };
 
-template <int MAP>
-__device__ __forceinline__ void lane_coords(const Geom &g, int &j, int &sub, int64_t &row0) {
+__device__ __forceinline__ void flat_coords(const Geom &g, int &j, int &sub, int64_t &row0) {
     sub = threadIdx.x & 3;
-    const int quad = threadIdx.x >> 2;
-    if (MAP == kFlat) {
-        const int64_t b0 = (int64_t)blockIdx.x * 64 + quad;
-        j = (int)(b0 % g.nblk);
-        row0 = b0 / g.nblk;
-    } else {
-        const int cg = (int)(blockIdx.x % (unsigned)g.ncg);
-        const int64_t slab = blockIdx.x / (unsigned)g.ncg;
-        j = (cg << g.cb_log2) + (quad & ((1 << g.cb_log2) - 1));
-        row0 = slab * g.rstep * g.iters + (quad >> g.cb_log2);
-    }
+    const int64_t b0 = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+    j = (int)(b0 % g.nblk);
+    row0 = b0 / g.nblk;
 }
 
-// Loads of this quad's rows row0 + (it + u) rstep, u < U (zeros past m).
-template <int U, bool NT>
-__device__ __forceinline__ void load_rows(const Geom &g, const uint16_t *__restrict__ A, int64_t row0,
-                                          int64_t c0, int it, uint4 q[U]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t row = row0 + (int64_t)(it + u) * g.rstep;
-        q[u] = row < g.m ? load_stream(reinterpret_cast<const uint4 *>(A + row * g.lda + c0), NT)
-                         : make_uint4(0, 0, 0, 0);
-    }
-}
-
-// Walks this quad's rows row0 + k rstep (k < iters), U rows' loads at a time,
-// and calls body(q, row) for each row below m. `q` holds the first group's
-// loads already when `preloaded` (issued before the per-block setup, so their
-// latency overlaps it). The row test is uniform within a quad, so DPP inside
-// `body` sees all four lanes. (Issuing the next group's loads before
-// processing this one, with or without raised wave priority, measured slower
-// on the FLUX shapes: it costs registers and occupancy.)
-template <int U, bool NT, typename Body>
-__device__ __forceinline__ void for_rows(const Geom &g, const uint16_t *__restrict__ A, int64_t row0,
-                                         int64_t c0, uint4 q[U], bool preloaded, Body body) {
-    const int64_t R = g.rstep;
-    for (int it = 0; it < g.iters; it += U) {
-        if (row0 + (int64_t)it * R >= g.m) break;
-        if (it > 0 || !preloaded) load_rows<U, NT>(g, A, row0, c0, it, q);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t row = row0 + (int64_t)(it + u) * R;
-            if (row >= g.m) break;
-            body(q[u], row);
-        }
-    }
-}
-
-// What a quad kernel writes besides codes and scales: nothing, the fp32
+// What a row-wave kernel writes besides codes and scales: nothing, the fp32
 // transform result (check mode), or that result rounded to bf16 (the 16-bit
 // activation a low-rank branch consumes).
 enum YOut { kYNone = 0, kYF32 = 1, kYBF16 = 2 };
 
-// Quantize fp32 values of a quad-held block and store codes and scale, and y
-// as YOUT asks (fp32 or bf16 [m][d]).
+// Row-wave strips (see the file header). Workgroup b takes segment b % nseg
+// (blocks 16 seg .. 16 seg + 15) and rows NW iters (b / nseg) + w + NW k for
+// its waves w and k < iters. The last segment of a row may be partial (nblk %
+// 16 != 0): each buffer resource's record count is the valid bytes from the
+// segment start to the end of the row's d channels, so lanes past the last
+// block read zeros and their stores are dropped by the hardware range check.
+struct RGeom {
+    int64_t m, lda, d;  // elements
+    int nblk, nseg, iters;
+};
+
+// Buffer resource over `bytes` bytes from `base` (raw addressing, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// The per-row output pointers of a wave, advanced by NW rows after each store.
+struct RowOut {
+    char *codes, *scales, *y;
+    int64_t codes_step, scales_step, y_step;
+    uint32_t codes_bytes, scales_bytes, y_bytes;
+};
+
+// Quantize the quad-held fp32 block and store codes, scale and y as YOUT asks.
 template <int YOUT>
-__device__ __forceinline__ void finish_f32(const float y[8], const Geom &g, int64_t row, int j, int sub,
-                                           int64_t c0, uint8_t *__restrict__ codes,
-                                           uint8_t *__restrict__ scales, void *__restrict__ yout) {
+__device__ __forceinline__ void store_row(const float y[8], RowOut &o, int lane) {
     if (YOUT == kYF32) {
-        float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(yout) + row * g.d + c0);
-        o[0] = make_float4(y[0], y[1], y[2], y[3]);
-        o[1] = make_float4(y[4], y[5], y[6], y[7]);
+        const auto r = buf_rsrc(o.y, o.y_bytes);
+        const uint32_t off = (uint32_t)lane * 32;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            (u32x4_t){__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])}, r,
+            off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            (u32x4_t){__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]), __float_as_uint(y[7])}, r,
+            off + 16, 0, 0);
     } else if (YOUT == kYBF16) {
-        uint32_t w[4];
+        u32x4_t w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = (uint32_t)bf16_rne_bits(y[2 * i]) | ((uint32_t)bf16_rne_bits(y[2 * i + 1]) << 16);
-        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(yout) + row * g.d + c0) = make_uint4(w[0], w[1], w[2], w[3]);
+        for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)bf16_rne_bits(y[2 * i]) | ((uint32_t)bf16_rne_bits(y[2 * i + 1]) << 16);
+        __builtin_amdgcn_raw_buffer_store_b128(w, buf_rsrc(o.y, o.y_bytes), (uint32_t)lane * 16, 0, 0);
     }
     uint32_t sbyte;
     const uint32_t packed = quantize_quad_f32(y, sbyte);
-    *reinterpret_cast<uint32_t *>(codes + row * (g.d / 2) + (int64_t)j * 16 + sub * 4) = packed;
-    if (sub == 0) scales[row * g.nblk + j] = (uint8_t)sbyte;
+    __builtin_amdgcn_raw_buffer_store_b32(packed, buf_rsrc(o.codes, o.codes_bytes), (uint32_t)lane * 4, 0, 0);
+    if ((lane & 3) == 0)
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, buf_rsrc(o.scales, o.scales_bytes), (uint32_t)lane >> 2,
+                                             0, 0);
+    o.codes += o.codes_step;
+    o.scales += o.scales_step;
+    o.y += o.y_step;
 }
 
-// bf16 input, quad layout: SmoothQuant (T = diag(inv_scale)) or the Kronecker
-// transform (shear form, or the general stages for blocks that do not admit
-// it). Quantize-only runs on the flat tiles of kq_flat.hip.
-template <int MODE, int YOUT, int U, bool NT, int MAP, bool PRE>
-__global__ __launch_bounds__(kThreads) void bf16_quad_kernel(
-    const uint16_t *__restrict__ A, Geom g, const float *__restrict__ params,
-    uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, void *__restrict__ ydbg) {
-    static_assert(MODE == kSmooth || MODE == kKron, "quantize-only runs on the flat kernel");
-    int j, sub;
-    int64_t row0;
-    lane_coords<MAP>(g, j, sub, row0);
-    const int64_t c0 = (int64_t)j * 32 + sub * 8;
-    uint4 q[U];
+// The block's 16 per-lane coefficients, written to LDS by wave 0.
+//
+// Shear form. Each factor splits exactly as G = S D with S = [[1, p], [q, 1]],
+// p = G01 / G11, q = G10 / G00, D = diag(G00, G11), and by the mixed-product
+// rule K = (S1 (x) ... (x) S5)(D1 (x) ... (x) D5): five unit-diagonal shear
+// stages, (x0, x1) -> (x0 + q x1, x1 + p x0), one fma per element each, then
+// one multiply per channel by the product of its five diagonal entries. Every
+// intermediate is the direct butterfly's intermediate divided by a
+// per-channel constant, so rounding errors stay relative to the same
+// quantities. The ratios use the hardware reciprocal (about 1 ulp): they are
+// coefficients of an exact refactoring, so a last-bit difference only moves y
+// by rounding. A block admits the form when every |p|, |q| <= 2^20 (a zero or
+// tiny diagonal entry, a swap say, gives an infinite, NaN or huge ratio).
+// Lane coefficients: c1 (G1, channel bit 4 = bit 1 of sub: this lane's
+// partner weight, q for bit 0 and p for bit 1), c2 (G2, bit 3), p3, q3, p4,
+// q4, p5, q5, then the 8 per-channel diagonal products.
+//
+// General form (any block of the segment without the shear form): the 2x2
+// stages y = x_self G[b][b] + x_partner G[1-b][b] (KronLane layout: s1, o1,
+// s2, o2, then G3, G4, G5 as 4 entries each).
+//
+// Every lane-dependent choice is an explicit select: a lane-dependent index
+// into the factor array would become a chain of compares and selects.
+struct SetupLane {
+    float p[5], q[5];
+    bool shear;
+};
 
+__device__ __forceinline__ void setup_ratios(const float f[20], SetupLane &S) {
+    const float lim = 0x1.0p20f;
+    S.shear = true;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+        S.p[k] = f[4 * k + 1] * __builtin_amdgcn_rcpf(f[4 * k + 3]);
+        S.q[k] = f[4 * k + 2] * __builtin_amdgcn_rcpf(f[4 * k]);
+        S.shear = S.shear & (fabsf(S.p[k]) <= lim) & (fabsf(S.q[k]) <= lim);  // false for inf and NaN
+    }
+}
+
+__device__ __forceinline__ void write_shear_coefs(const float f[20], const SetupLane &S, int sub, float *dst) {
+    const bool b4 = (sub >> 1) & 1, b3 = sub & 1;
+    dst[0] = b4 ? S.p[0] : S.q[0];
+    dst[1] = b3 ? S.p[1] : S.q[1];
+#pragma unroll
+    for (int k = 2; k < 5; ++k) {
+        dst[2 * k - 2] = S.p[k];
+        dst[2 * k - 1] = S.q[k];
+    }
+    // diagonal product of channel (b4, b3, i2, i1, i0): ((d12 G3[i2][i2]) G4[i1][i1]) G5[i0][i0]
+    const float d12 = (b4 ? f[3] : f[0]) * (b3 ? f[7] : f[4]);
+    float t3[2], t4[4];
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2) t3[i2] = d12 * f[8 + 3 * i2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t4[i] = t3[i >> 1] * f[12 + 3 * (i & 1)];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[8 + i] = t4[i >> 1] * f[16 + 3 * (i & 1)];
+}
+
+__device__ __forceinline__ void write_general_coefs(const float f[20], int sub, float *dst) {
+    const bool b4 = (sub >> 1) & 1, b3 = sub & 1;
+    dst[0] = b4 ? f[3] : f[0];  // G1[b4][b4]
+    dst[1] = b4 ? f[1] : f[2];  // G1[1-b4][b4]
+    dst[2] = b3 ? f[7] : f[4];  // G2[b3][b3]
+    dst[3] = b3 ? f[5] : f[6];  // G2[1-b3][b3]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        dst[4 + i] = f[8 + i];
+        dst[8 + i] = f[12 + i];
+        dst[12 + i] = f[16 + i];
+    }
+}
+
+template <bool SHEAR>
+__device__ __forceinline__ void apply_coefs(float y[8], const float c[16]) {
+    if (SHEAR) {
+        fmac_partner_xor2(y, c[0]);  // G1: channel bit 4 = bit 1 of sub
+        fmac_partner_xor1(y, c[1]);  // G2: channel bit 3 = bit 0 of sub
+        shear_stage<4>(y, c[2], c[3]);
+        shear_stage<2>(y, c[4], c[5]);
+        shear_stage<1>(y, c[6], c[7]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = y[i] * c[8 + i];
+    } else {
+        KronLane L;
+        L.s1 = c[0]; L.o1 = c[1]; L.s2 = c[2]; L.o2 = c[3];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            L.g3[i] = c[4 + i];
+            L.g4[i] = c[8 + i];
+            L.g5[i] = c[12 + i];
+        }
+        kron_apply8(y, L);
+    }
+}
+
+// bf16 input, row-wave strips: SmoothQuant (T = diag(inv_scale)) or the
+// Kronecker transform. U rows' loads are issued at once; for the transform the
+// first U rows' loads are in flight while wave 0 derives the segment's
+// coefficients (factor loads, reciprocals, LDS writes, barrier).
+template <int MODE, int YOUT, int NW, int U>
+__global__ __launch_bounds__(NW * 64) void rowwave_kernel(const uint16_t *__restrict__ A, RGeom g,
+                                                          const float *__restrict__ params,
+                                                          uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                          void *__restrict__ yout) {
+    static_assert(MODE == kSmooth || MODE == kKron, "quantize-only runs on the flat kernel");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sub = lane & 3;
+    const int seg = (int)(blockIdx.x % (unsigned)g.nseg);
+    const int64_t row0 = (int64_t)(blockIdx.x / (unsigned)g.nseg) * NW * g.iters + wave;
+    const int j = seg * 16 + (lane >> 2);
+    const bool active = j < g.nblk;
+    const int64_t c_seg = (int64_t)seg * 512;  // first channel of the segment
+    // rows of this wave: row0 + NW k for k < nr
+    const int64_t left = row0 < g.m ? (g.m - row0 + NW - 1) / NW : 0;
+    const int nr = (int)(left < g.iters ? left : g.iters);
+
+    const char *a_row = reinterpret_cast<const char *>(A + row0 * g.lda + c_seg);
+    const int64_t a_step = (int64_t)NW * g.lda * 2;
+    const uint32_t a_bytes = (uint32_t)((g.d - c_seg) * 2);
+    const uint32_t a_off = (uint32_t)lane * 16;
+    RowOut o;
+    o.codes = reinterpret_cast<char *>(codes + row0 * (g.d / 2) + c_seg / 2);
+    o.scales = reinterpret_cast<char *>(scales + row0 * g.nblk + seg * 16);
+    o.codes_step = (int64_t)NW * (g.d / 2);
+    o.scales_step = (int64_t)NW * g.nblk;
+    o.codes_bytes = (uint32_t)((g.d - c_seg) / 2);
+    o.scales_bytes = (uint32_t)(g.nblk - seg * 16);
+    const int ysize = YOUT == kYF32 ? 4 : 2;
+    o.y = YOUT == kYNone ? nullptr : static_cast<char *>(yout) + (row0 * g.d + c_seg) * ysize;
+    o.y_step = (int64_t)NW * g.d * ysize;
+    o.y_bytes = (uint32_t)((g.d - c_seg) * ysize);
+
+    // Every load of a group is issued; a row past the wave's last one gets a
+    // buffer of zero records, so it reads zeros without touching memory (and
+    // the compiler's wait counts stay exact).
+    uint4 q[U];
+    auto load_group = [&](int k0) {
+        const char *p = a_row + (int64_t)k0 * a_step;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const u32x4_t v =
+                __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(p, k0 + u < nr ? a_bytes : 0u), a_off, 0, 2);
+            q[u] = make_uint4(v[0], v[1], v[2], v[3]);
+            p += a_step;
+        }
+    };
+    // A group consumes all of its loads at once, before its first store:
+    // stores count in the same vector-memory counter as loads, so a wait for
+    // row u > 1 issued after the stores of earlier rows would also wait for
+    // those stores to be acknowledged. The empty asm statement reads every
+    // loaded register of the group, so the compiler places one wait for all of
+    // them before it and none inside the group. The first group is peeled off
+    // the row loop; with 4 rows per wave it is the only one.
+    auto group = [&](int k, auto per_row) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) asm volatile("" : "+v"(q[u].x), "+v"(q[u].y), "+v"(q[u].z), "+v"(q[u].w));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (k + u >= nr) break;
+            float y[8];
+            widen8(q[u], y);
+            per_row(y);
+            store_row<YOUT>(y, o, lane);
+        }
+    };
+    auto rows = [&](auto per_row, bool preloaded) {
+        if (!preloaded) load_group(0);
+        group(0, per_row);
+        for (int k = U; k < nr; k += U) {
+            load_group(k);
+            group(k, per_row);
+        }
+    };
     if (MODE == kSmooth) {
         float sq[8];
-        const float4 a = *reinterpret_cast<const float4 *>(params + c0);
-        const float4 b = *reinterpret_cast<const float4 *>(params + c0 + 4);
-        sq[0] = a.x; sq[1] = a.y; sq[2] = a.z; sq[3] = a.w;
-        sq[4] = b.x; sq[5] = b.y; sq[6] = b.z; sq[7] = b.w;
-        for_rows<U, NT>(g, A, row0, c0, q, false, [&](const uint4 &x, int64_t row) {
-            float y[8];
-            widen8(x, y);
+        const float4 lo = active ? *reinterpret_cast<const float4 *>(params + j * 32 + sub * 8) : make_float4(0, 0, 0, 0);
+        const float4 hi = active ? *reinterpret_cast<const float4 *>(params + j * 32 + sub * 8 + 4) : make_float4(0, 0, 0, 0);
+        sq[0] = lo.x; sq[1] = lo.y; sq[2] = lo.z; sq[3] = lo.w;
+        sq[4] = hi.x; sq[5] = hi.y; sq[6] = hi.z; sq[7] = hi.w;
+        rows([&](float y[8]) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) y[i] = y[i] * sq[i];
-            finish_f32<YOUT>(y, g, row, j, sub, c0, codes, scales, ydbg);
-        });
+        }, false);
+        return;
+    }
+
+    // Kronecker transform: wave 0 (one lane per block and channel group)
+    // derives the coefficients; a ballot picks one form for the workgroup, so
+    // the branch below is uniform and the row loop carries no divergence. Wave
+    // 0 issues its factor loads before its row loads, so waiting for the
+    // factors leaves the rows in flight.
+    __shared__ float coef[64][17];
+    __shared__ int all_shear;
+    float f[20];
+    if (wave == 0 && active) load_factors20(params + (int64_t)j * 20, f);
+    load_group(0);
+    if (wave == 0) {
+        SetupLane S;
+        if (active) setup_ratios(f, S);
+        const bool all = __builtin_amdgcn_ballot_w64(active && !S.shear) == 0;
+        if (!active) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) coef[lane][i] = 0.f;
+        } else if (all) {
+            write_shear_coefs(f, S, sub, coef[lane]);
+        } else {
+            write_general_coefs(f, sub, coef[lane]);
+        }
+        if (lane == 0) all_shear = all;
+    }
+    __syncthreads();
+    float c[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = coef[lane][i];
+    if (__builtin_amdgcn_readfirstlane(all_shear)) {
+        rows([&](float y[8]) { apply_coefs<true>(y, c); }, true);
     } else {
-        // Per-block setup is shared through LDS when the workgroup's first row
-        // of quads holds all its blocks (strip mapping): those quads (wave 0
-        // for CB = 16) derive the shear coefficients, everyone reads them back.
-        // With PRE the first rows' loads are in flight during the setup.
-        ShearLane S;
-        if (MAP == kStrip) {
-            __shared__ ShearLane lds[64];
-            const int quad = threadIdx.x >> 2;
-            const bool setter = (quad >> g.cb_log2) == 0;
-            float f[20];
-            if (setter) load_factors20(params + (int64_t)j * 20, f);
-            if (PRE && row0 < g.m) load_rows<U, NT>(g, A, row0, c0, 0, q);
-            if (setter) shear_lane_setup(f, sub, lds[threadIdx.x]);
-            __syncthreads();
-            S = lds[((quad & ((1 << g.cb_log2) - 1)) << 2) | sub];
-        } else {
-            float f[20];
-            load_factors20(params + (int64_t)j * 20, f);
-            if (PRE && row0 < g.m) load_rows<U, NT>(g, A, row0, c0, 0, q);
-            shear_lane_setup(f, sub, S);
-        }
-        if (S.ok) {  // one block per quad: uniform within the quad
-            for_rows<U, NT>(g, A, row0, c0, q, PRE, [&](const uint4 &x, int64_t row) {
-                float y[8];
-                widen8(x, y);
-                shear_apply8(y, S);
-                finish_f32<YOUT>(y, g, row, j, sub, c0, codes, scales, ydbg);
-            });
-        } else {
-            float f[20];
-            load_factors20(params + (int64_t)j * 20, f);
-            KronLane L;
-            kron_lane_setup(f, sub, L);
-            for_rows<U, NT>(g, A, row0, c0, q, PRE, [&](const uint4 &x, int64_t row) {
-                float y[8];
-                widen8(x, y);
-                kron_apply8(y, L);
-                finish_f32<YOUT>(y, g, row, j, sub, c0, codes, scales, ydbg);
-            });
-        }
+        rows([&](float y[8]) { apply_coefs<false>(y, c); }, true);
     }
 }
 
@@ -345,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void f32_kernel(
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ out) {
     int j, sub;
     int64_t row0;
-    lane_coords<kFlat>(g, j, sub, row0);
+    flat_coords(g, j, sub, row0);
     const int64_t R = g.rstep;
     const int64_t c0 = (int64_t)j * 32 + sub * 8;
 
@@ -408,13 +542,7 @@ int64_t gcd64(int64_t a, int64_t b) {
     return a;
 }
 
-int pick_cb_log2(int64_t nblk, int max_log2) {
-    for (int l = max_log2; l > 0; --l)
-        if (nblk % (1 << l) == 0) return l;
-    return 0;
-}
-
-// kFlat: about `target_wg` workgroups (fewer if the matrix is small), a multiple
+// Grid-stride geometry: about `target_wg` workgroups (fewer if the matrix is small), a multiple
 // of nblk / gcd(64, nblk) so that 64 * gridDim.x is a multiple of nblk.
 // `iters` (sweeps per workgroup) is rounded up to a multiple of `unroll`.
 bool make_geom_flat(int64_t m, int64_t d, int64_t ld, int unroll, int64_t target_wg, kq::Geom &g,
@@ -423,8 +551,6 @@ bool make_geom_flat(int64_t m, int64_t d, int64_t ld, int unroll, int64_t target
     g.d = d;
     g.lda = ld;
     g.nblk = (int)(d / 32);
-    g.cb_log2 = 0;
-    g.ncg = 1;
     const int64_t k0 = g.nblk / gcd64(64, g.nblk);
     const int64_t need = (m * g.nblk + 63) / 64;
     int64_t w = need < target_wg ? need : target_wg;
@@ -436,30 +562,6 @@ bool make_geom_flat(int64_t m, int64_t d, int64_t ld, int unroll, int64_t target
     if (iters > 0x7FFFFFFF) return false;
     g.iters = (int)iters;
     nwg = (unsigned)w;
-    return true;
-}
-
-// kStrip: column groups of CB blocks (the largest power of two <= 2^max_cb_log2
-// dividing nblk), row tiles of R = 64 / CB rows, `iters_per_wg` row tiles per
-// workgroup (rounded up to a multiple of `unroll`).
-bool make_geom_strip(int64_t m, int64_t d, int64_t ld, int unroll, int64_t iters_per_wg, kq::Geom &g,
-                     unsigned &nwg, int max_cb_log2 = 4) {
-    g.m = m;
-    g.d = d;
-    g.lda = ld;
-    g.nblk = (int)(d / 32);
-    g.cb_log2 = pick_cb_log2(g.nblk, max_cb_log2);
-    g.ncg = g.nblk >> g.cb_log2;
-    g.rstep = 64 >> g.cb_log2;
-    const int64_t row_tiles = (m + g.rstep - 1) / g.rstep;
-    int64_t iters = iters_per_wg < 1 ? 1 : iters_per_wg;
-    iters = (iters + unroll - 1) / unroll * unroll;
-    if (iters > row_tiles) iters = (row_tiles + unroll - 1) / unroll * unroll;
-    const int64_t nslab = (row_tiles + iters - 1) / iters;
-    const int64_t total = nslab * g.ncg;
-    if (total > 0x7FFFFFFF || iters > 0x7FFFFFFF) return false;
-    g.iters = (int)iters;
-    nwg = (unsigned)total;
     return true;
 }
 
@@ -488,36 +590,41 @@ bool make_mgeom(int64_t m, int64_t d, int64_t lda, int nb, int unroll, kq::MGeom
     return true;
 }
 
-// Launch shape of the bf16 quad kernels: column strips of 16 blocks, row tiles
-// of 4 rows, non-temporal loads. Workgroups are kept short, which the HBM
-// system rewards: SmoothQuant walks 2 row tiles (both loads in flight), the
-// transform 8 row tiles, 4 at a time (its per-block setup is amortized over
-// more rows, and the first 4 rows' loads are issued before the setup). Chosen
-// by sweeping tile counts, unroll depth, prefetching and the strip, flat and
-// column-per-wave mappings on the 18432 x 3072 and 18432 x 12288 shapes.
+// Row-wave geometry: 16-block segments (the last one partial when nblk % 16 !=
+// 0), workgroups of NW waves on NW consecutive rows, `iters` row groups each.
+bool make_rgeom(int64_t m, int64_t d, int64_t lda, int nw, int iters, kq::RGeom &g, unsigned &nwg) {
+    // buffer records and offsets are 32-bit: a row's bytes (fp32 y in check
+    // mode: 4 d) must fit
+    if (d > ((int64_t)1 << 29)) return false;
+    g.m = m;
+    g.d = d;
+    g.lda = lda;
+    g.nblk = (int)(d / 32);
+    g.nseg = (g.nblk + 15) / 16;
+    g.iters = iters;
+    const int64_t slabs = (m + (int64_t)nw * iters - 1) / ((int64_t)nw * iters);
+    const int64_t total = slabs * g.nseg;
+    if (total > 0x7FFFFFFF) return false;
+    nwg = (unsigned)total;
+    return true;
+}
+
+// Launch shapes, chosen by sweeping waves per workgroup (4, 8, 16), rows per
+// load group (2, 3, 4, 8) and row groups per workgroup (2 ... 16) on the
+// 18432 x 3072 and 18432 x 12288 shapes: the transform takes 4 waves that
+// each load 4 rows at once and finish (a workgroup covers 16 blocks x 16
+// rows; longer-lived workgroups were slower although they amortize the setup);
+// SmoothQuant, with no setup, takes 8 waves of 4 rows.
 template <int MODE, int YOUT>
-kq_status launch_quad(const uint16_t *A, int64_t m, int64_t d, int64_t lda, const float *params,
-                      uint8_t *codes, uint8_t *scales, void *ydbg, kq_stream_t stream) {
-    kq::Geom g;
+kq_status launch_rowwave(const uint16_t *A, int64_t m, int64_t d, int64_t lda, const float *params,
+                         uint8_t *codes, uint8_t *scales, void *yout, kq_stream_t stream) {
+    constexpr int NW = MODE == kq::kKron ? 4 : 8;
+    constexpr int U = 4;
+    kq::RGeom g;
     unsigned nwg;
-    if (MODE == kq::kKron) {
-        // 8 row tiles per workgroup, 4 rows' loads at a time; when that leaves
-        // fewer than 1024 workgroups (4 per CU), 2 row tiles of 2 rows instead:
-        // small inputs need the parallelism more than the amortized setup.
-        if (!make_geom_strip(m, d, lda, 4, 8, g, nwg)) return KQ_ERR_SHAPE;
-        if (nwg >= 1024) {
-            hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, YOUT, 4, true, kq::kStrip, true>), dim3(nwg),
-                               dim3(kq::kThreads), 0, (hipStream_t)stream, A, g, params, codes, scales, ydbg);
-            return launched();
-        }
-        if (!make_geom_strip(m, d, lda, 2, 2, g, nwg)) return KQ_ERR_SHAPE;
-        hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, YOUT, 2, true, kq::kStrip, true>), dim3(nwg),
-                           dim3(kq::kThreads), 0, (hipStream_t)stream, A, g, params, codes, scales, ydbg);
-        return launched();
-    }
-    if (!make_geom_strip(m, d, lda, 2, 2, g, nwg)) return KQ_ERR_SHAPE;
-    hipLaunchKernelGGL((kq::bf16_quad_kernel<MODE, YOUT, 2, true, kq::kStrip, false>), dim3(nwg),
-                       dim3(kq::kThreads), 0, (hipStream_t)stream, A, g, params, codes, scales, ydbg);
+    if (!make_rgeom(m, d, lda, NW, U, g, nwg)) return KQ_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((kq::rowwave_kernel<MODE, YOUT, NW, U>), dim3(nwg), dim3(NW * 64), 0, (hipStream_t)stream, A,
+                       g, params, codes, scales, yout);
     return launched();
 }
 
@@ -583,8 +690,8 @@ kq_status launch_fused(const uint16_t *A, int64_t m, int64_t d, int64_t lda, con
     if (f == kFormMfmaLds && (d / 32) % 16 == 0)
         return launch_mfma_lds<DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
     if (f != kFormMfma)
-        return launch_quad<kq::kKron, DEBUG ? kq::kYF32 : kq::kYNone>(A, m, d, lda, factors, codes, scales, ydbg,
-                                                                       stream);
+        return launch_rowwave<kq::kKron, DEBUG ? kq::kYF32 : kq::kYNone>(A, m, d, lda, factors, codes, scales, ydbg,
+                                                                          stream);
     if ((d / 32) % 2 == 0)
         return launch_mfma<2, DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
     return launch_mfma<1, DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
@@ -616,7 +723,7 @@ kq_status kq_transform_quantize_mxfp4_y16(const uint16_t *A, int64_t m, int64_t 
     if ((s = check_bf16_io(A, lda, codes, scales)) != KQ_OK) return s;
     if (!factors || !y16) return KQ_ERR_NULL;
     if (!aligned(factors, 16) || !aligned(y16, 16)) return KQ_ERR_ALIGN;
-    return launch_quad<kq::kKron, kq::kYBF16>(A, m, d, lda, factors, codes, scales, y16, stream);
+    return launch_rowwave<kq::kKron, kq::kYBF16>(A, m, d, lda, factors, codes, scales, y16, stream);
 }
 
 kq_status kq_smoothquant_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
@@ -628,7 +735,7 @@ kq_status kq_smoothquant_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d,
     if ((s = check_bf16_io(A, lda, codes, scales)) != KQ_OK) return s;
     if (!inv_scale) return KQ_ERR_NULL;
     if (!aligned(inv_scale, 16)) return KQ_ERR_ALIGN;
-    return launch_quad<kq::kSmooth, kq::kYNone>(A, m, d, lda, inv_scale, codes, scales, nullptr, stream);
+    return launch_rowwave<kq::kSmooth, kq::kYNone>(A, m, d, lda, inv_scale, codes, scales, nullptr, stream);
 }
 
 kq_status kq_quantize_mxfp4_f32(const float *X, int64_t m, int64_t d, int64_t ldx, uint8_t *codes,

@@ -146,6 +146,25 @@ def test_fused_exact_factors_reduce_to_quantizer(torch_dev, kq, orc, kind, form)
         parity.assert_codes_equal_mod_signed_zero(q_codes.cpu().numpy(), codes.cpu().numpy())
 
 
+def test_fused_segments_with_a_nonshear_block(torch_dev, kq, orc, form):
+    """LU-perturbed factors everywhere except a few blocks whose G2 is a swap (zero
+    diagonal, so no shear form): every block sharing a 16-block segment with one of
+    them runs the general 2x2 stages. Ragged rows and a partial last segment."""
+    torch = torch_dev
+    case("fused non-shear blocks form=" + form)
+    m, d = 4133, 1152
+    A_full = synth.random_bf16_matrix(m, d, seed=91, scale=3.0)
+    fac = synth.lu_perturbed_factors(d // 32, seed=92)
+    for blk in (5, 21, 35):  # segments 0, 1 and the 4-block tail segment 2
+        fac[blk, 1] = np.array([[0.0, 1.0], [1.0, 0.0]], np.float32)
+    y = torch.empty((m, d), dtype=torch.float32, device="cuda")
+    codes, scales = kq.transform_quantize_mxfp4(dev_bf16(torch, A_full), torch.from_numpy(fac).cuda(), y_debug=y)
+    codes_fast, scales_fast = kq.transform_quantize_mxfp4(dev_bf16(torch, A_full), torch.from_numpy(fac).cuda())
+    assert torch.equal(codes, codes_fast) and torch.equal(scales, scales_fast)
+    rep = parity.fused_report(orc, A_full, fac, codes.cpu().numpy(), scales.cpu().numpy(), y.cpu().numpy())
+    print("[parity] non-shear blocks %s %s" % (form, rep), flush=True)
+
+
 def test_fused_hadamard_worked_example(torch_dev, kq, orc, form):
     torch = torch_dev
     case("fused hadamard worked example form=" + form)
