@@ -34,6 +34,11 @@ HBM_PEAK_GBPS = 8000.0
 ROTATE_BYTES = 512 << 20
 WORKLOAD = ("flux_18432x3072", "flux_18432x12288")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_flux_18432x12288.json")
+# device kernels behind each timed entry point (as rocprofv3 names them)
+KERNEL_NAMES = {"fused": "kq::rowwave_kernel<2, 0, 4, 4> (fused transform + MXFP4)",
+                "smoothquant": "kq::rowwave_kernel<1, 0, 8, 4> (SmoothQuant + MXFP4)",
+                "quantize": "kq::flat_quantize_kernel (quantize-only)"}
+FUSED_KERNEL = "rowwave_kernel<2, 0, 4, 4>"
 
 
 def log(msg):
@@ -415,8 +420,8 @@ def summarize_pmc(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_json):
         grid = max(r[1] for r in sel)
         vals = [r[2] for r in sel if r[1] == grid]
         return sum(vals) / len(vals), len(vals), sel[0][0], grid
-    f_fused, n_f, kname, grid = largest_kernel(_pmc_rows(fetch_dir, "FETCH_SIZE"), "bf16_quad_kernel<2")
-    w_fused, n_w, _, _ = largest_kernel(_pmc_rows(write_dir, "WRITE_SIZE"), "bf16_quad_kernel<2")
+    f_fused, n_f, kname, grid = largest_kernel(_pmc_rows(fetch_dir, "FETCH_SIZE"), FUSED_KERNEL)
+    w_fused, n_w, _, _ = largest_kernel(_pmc_rows(write_dir, "WRITE_SIZE"), FUSED_KERNEL)
     f_copy, n_cf, cname, _ = largest_kernel(_pmc_rows(cfetch_dir, "FETCH_SIZE"), COPY_KERNEL)
     w_copy, n_cw, _, _ = largest_kernel(_pmc_rows(cwrite_dir, "WRITE_SIZE"), COPY_KERNEL)
     kf = COPY_BYTES / (f_copy * 1024.0)
@@ -508,7 +513,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "kq::bf16_quad_kernel (%s) on %dx%d" % (kinds[0], sets[big].m, sets[big].d)},
+                     "kernel": "%s on %dx%d" % (KERNEL_NAMES[kinds[0]], sets[big].m, sets[big].d)},
         "kernels": {k: v["per_tensor"] for k, v in res.items()},
     }
     if "fused" in res and "smoothquant" in res:
