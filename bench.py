@@ -243,6 +243,19 @@ def extras(torch, kq, synth, flux_sets, reps=100, warmup=20):
                                          "TFLOPs": round(flops / (med * 1e-6) / 1e12, 1),
                                          "pct_fp4_peak": round(100 * flops / (med * 1e-6) / 10.1e15, 2)}
     log("weight side / gemm: %s %s" % (out["weight_fold_3072x3072"], out["w4a4_gemm_18432x3072x3072"]))
+    # the same product on the 128 x 512-tile kernel, and the layer with the transform and
+    # quantizer in the product's prologue against the two launches it replaces
+    d_w = _events_us(torch, lambda: kq.mxfp4_gemm_wide(ca, sa, cw, sw, out=O), 20, 3)
+    d_f = _events_us(torch, lambda: kq.transform_quantize_mxfp4_gemm(A, fac, cw, sw, out=O), 20, 3)
+    d_q = _events_us(torch, lambda: kq.transform_quantize_mxfp4(A, fac, codes=ca, scales=sa), 20, 3)
+    med_w, med_f, med_q = (float(np.median(x)) for x in (d_w, d_f, d_q))
+    out["w4a4_layer_fused_18432x3072x3072"] = {
+        "wide_gemm_us": round(med_w, 1), "wide_gemm_TFLOPs": round(flops / (med_w * 1e-6) / 1e12, 1),
+        "wide_gemm_pct_fp4_peak": round(100 * flops / (med_w * 1e-6) / 10.1e15, 2),
+        "fused_layer_us": round(med_f, 1), "fused_layer_TFLOPs": round(flops / (med_f * 1e-6) / 1e12, 1),
+        "quantizer_us": round(med_q, 1),
+        "pipeline_us": round(med_q + min(med, med_w), 1)}
+    log("fused layer: %s" % out["w4a4_layer_fused_18432x3072x3072"])
     out["w4a4_layer_lowrank_18432x3072x3072_r128"] = lowrank_layer_timing(torch, kq, A, fac, cw, sw, W)
     log("low-rank layer: %s" % out["w4a4_layer_lowrank_18432x3072x3072_r128"])
     out["calibration_4096x3072x3072"] = calibration_timing(torch, kq, synth, A, W)

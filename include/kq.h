@@ -139,6 +139,45 @@ kq_status kq_mxfp4_gemm(const uint8_t *codes_a, const uint8_t *scales_a, const u
                         kq_stream_t stream);
 
 /*
+ * The same W4A4 GEMM as kq_mxfp4_gemm (identical arguments, layouts and error
+ * rules) on 128 x 512 output tiles of eight waves, k advancing 128 per stage.
+ * Both kernels accumulate one 128-k block per matrix instruction in increasing
+ * k, so their results are bit-identical.
+ * m rows of codes_a (k/2 bytes each) and 512 rows of codes_w must each span
+ * fewer than 2^31 bytes per tile (KQ_ERR_UNSUPPORTED otherwise).
+ */
+kq_status kq_mxfp4_gemm_wide(const uint8_t *codes_a, const uint8_t *scales_a, const uint8_t *codes_w,
+                             const uint8_t *scales_w, int64_t m, int64_t n, int64_t k, float *O, int64_t ldo,
+                             kq_stream_t stream);
+
+/*
+ * The W4A4 layer with the activation transform and quantizer inside the
+ * product (Sec. 1 Eq. 1-2; Sec. 3.2 Eq. 5 and Sec. 3.5.1 Eq. 12 for T; Sec. 3.1
+ * for Q):
+ *   O = deq(Q(A T)) deq(W)^T,
+ * where Q(A T) is what kq_transform_quantize_mxfp4 writes for the same A and
+ * factors, computed in the product's prologue and kept on chip, and W is
+ * already in MXFP4 (e.g. kq_quantize_mxfp4_f32 of kq_inverse_fold_weights).
+ * Blocks are transformed in groups of four (128 channels, one k stage); a group
+ * in which every block admits the shear form uses it, else the general 2x2
+ * stages, so for factors where some block lacks the shear form the activation
+ * codes can differ from the standalone quantizer's at rounding ties (both
+ * meet the same tolerance against the exact transform). When every block
+ * admits it, O is bit-identical to kq_transform_quantize_mxfp4 followed by
+ * kq_mxfp4_gemm.
+ *   A         device, bf16 bits [m][lda], lda >= k, lda % 8 == 0, 16-byte aligned
+ *   factors   device, fp32 [k/32][5][2][2] (as kq_transform_quantize_mxfp4), 16-byte aligned
+ *   codes_w   device, [n][k/2] bytes, 16-byte aligned
+ *   scales_w  device, [n][k/32] (4-byte aligned when k/32 % 4 == 0)
+ *   O         device, fp32 [m][ldo], ldo >= n; written, not accumulated into
+ * k % 32 == 0 (KQ_ERR_SHAPE); 128 rows of A (2 lda bytes each) and 512 rows of
+ * codes_w must each span fewer than 2^31 bytes (KQ_ERR_UNSUPPORTED).
+ */
+kq_status kq_transform_quantize_mxfp4_gemm(const uint16_t *A, int64_t m, int64_t k, int64_t lda,
+                                           const float *factors, const uint8_t *codes_w, const uint8_t *scales_w,
+                                           int64_t n, float *O, int64_t ldo, kq_stream_t stream);
+
+/*
  * Block-Hadamard transform + quantize: the fixed-rotation baselines the paper
  * compares against -- Sec. 1 and Table 2 (Hadamard at the MXFP4 block size,
  * n = 32) and Sec. 4.4 / Table 3 (the fast Walsh-Hadamard transform over the

@@ -28,6 +28,8 @@ EXPORTS = (
     "kq_quantize_mxfp4_f32",
     "kq_inverse_fold_weights",
     "kq_mxfp4_gemm",
+    "kq_mxfp4_gemm_wide",
+    "kq_transform_quantize_mxfp4_gemm",
     "kq_hadamard_quantize_mxfp4",
     "kq_transform_quantize_mxfp4_y16",
     "kq_lowrank_project",
@@ -69,6 +71,8 @@ def lib():
             "kq_inverse_fold_weights": [p, i64, i64, p, p, p],
             "kq_factors_from_lu": [p, i64, p],
             "kq_mxfp4_gemm": [p, p, p, p, i64, i64, i64, p, i64, p],
+            "kq_mxfp4_gemm_wide": [p, p, p, p, i64, i64, i64, p, i64, p],
+            "kq_transform_quantize_mxfp4_gemm": [p, i64, i64, i64, p, p, p, i64, p, i64, p],
             "kq_hadamard_quantize_mxfp4": [p, i64, i64, i64, i64, p, p, p, p],
             "kq_transform_quantize_mxfp4_y16": [p, i64, i64, i64, p, p, p, p, p],
             "kq_lowrank_project": [p, i64, i64, i64, p, p, i64, p, p],
@@ -311,8 +315,7 @@ def inverse_fold_weights(W, factors, out=None, stream=None):
     return out
 
 
-def mxfp4_gemm(codes_a, scales_a, codes_w, scales_w, out=None, stream=None):
-    """O = deq(A) deq(W)^T in fp32 from MXFP4 operands (codes [rows][k/2], scales [rows][k/32])."""
+def _gemm_operands(codes_a, scales_a, codes_w, scales_w, out):
     torch = _torch()
     for t, nm in ((codes_a, "codes_a"), (scales_a, "scales_a"), (codes_w, "codes_w"), (scales_w, "scales_w")):
         _dev(t, nm, (torch.uint8,))
@@ -329,9 +332,52 @@ def mxfp4_gemm(codes_a, scales_a, codes_w, scales_w, out=None, stream=None):
     _dev(out, "out", (torch.float32,))
     if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
         raise ValueError("out must be fp32 [m][n] with unit column stride")
+    return m, n, k, out
+
+
+def mxfp4_gemm(codes_a, scales_a, codes_w, scales_w, out=None, stream=None):
+    """O = deq(A) deq(W)^T in fp32 from MXFP4 operands (codes [rows][k/2], scales [rows][k/32])."""
+    m, n, k, out = _gemm_operands(codes_a, scales_a, codes_w, scales_w, out)
     _check("kq_mxfp4_gemm",
            lib().kq_mxfp4_gemm(_p(codes_a), _p(scales_a), _p(codes_w), _p(scales_w), m, n, k, _p(out),
                                out.stride(0), _stream_ptr(stream)))
+    return out
+
+
+def mxfp4_gemm_wide(codes_a, scales_a, codes_w, scales_w, out=None, stream=None):
+    """As mxfp4_gemm, on the 128 x 512-tile kernel (bit-identical results)."""
+    torch = _torch()
+    m, n, k, out = _gemm_operands(codes_a, scales_a, codes_w, scales_w, out)
+    _check("kq_mxfp4_gemm_wide",
+           lib().kq_mxfp4_gemm_wide(_p(codes_a), _p(scales_a), _p(codes_w), _p(scales_w), m, n, k, _p(out),
+                                    out.stride(0), _stream_ptr(stream)))
+    return out
+
+
+def transform_quantize_mxfp4_gemm(A, factors, codes_w, scales_w, out=None, stream=None):
+    """O = deq(Q(A T)) deq(W)^T in fp32: the Kronecker transform and MXFP4 quantizer of A
+    (bf16 [m][k], factors fp32 [k/32][5][2][2]) run inside the W4A4 product with the MXFP4
+    weights (codes [n][k/2], scales [n][k/32])."""
+    torch = _torch()
+    m, k, lda = _bf16_input(A)
+    _dev(factors, "factors", (torch.float32,))
+    if factors.numel() != (k // 32) * 20 or not factors.is_contiguous():
+        raise ValueError("factors must be contiguous fp32 [k/32][5][2][2]")
+    for t, nm in ((codes_w, "codes_w"), (scales_w, "scales_w")):
+        _dev(t, nm, (torch.uint8,))
+        if not t.is_contiguous():
+            raise ValueError(nm + " must be contiguous")
+    n = codes_w.shape[0]
+    if tuple(codes_w.shape) != (n, k // 2) or tuple(scales_w.shape) != (n, k // 32):
+        raise ValueError("weight operand shapes do not match A")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=A.device)
+    _dev(out, "out", (torch.float32,))
+    if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
+        raise ValueError("out must be fp32 [m][n] with unit column stride")
+    _check("kq_transform_quantize_mxfp4_gemm",
+           lib().kq_transform_quantize_mxfp4_gemm(_p(A), m, k, lda, _p(factors), _p(codes_w), _p(scales_w), n,
+                                                  _p(out), out.stride(0), _stream_ptr(stream)))
     return out
 
 

@@ -65,6 +65,30 @@ GOOD = P(0x10000)  # never dereferenced: every case below fails before a launch
     ("kq_mxfp4_gemm", (GOOD, None, GOOD, GOOD, 4, 4, 64, GOOD, 4, None), kq.KQ_ERR_NULL),
     ("kq_mxfp4_gemm", (P(0x10008), GOOD, GOOD, GOOD, 4, 4, 64, GOOD, 4, None), kq.KQ_ERR_ALIGN),
     ("kq_mxfp4_gemm", (None, None, None, None, 0, 4, 64, None, 4, None), kq.KQ_OK),
+    ("kq_mxfp4_gemm_wide", (GOOD, GOOD, GOOD, GOOD, 4, 4, 48, GOOD, 4, None), kq.KQ_ERR_SHAPE),
+    ("kq_mxfp4_gemm_wide", (GOOD, GOOD, GOOD, GOOD, 4, 4, 64, GOOD, 3, None), kq.KQ_ERR_SHAPE),
+    ("kq_mxfp4_gemm_wide", (GOOD, None, GOOD, GOOD, 4, 4, 64, GOOD, 4, None), kq.KQ_ERR_NULL),
+    ("kq_mxfp4_gemm_wide", (GOOD, GOOD, None, GOOD, 4, 4, 64, GOOD, 4, None), kq.KQ_ERR_NULL),
+    ("kq_mxfp4_gemm_wide", (P(0x10008), GOOD, GOOD, GOOD, 4, 4, 64, GOOD, 4, None), kq.KQ_ERR_ALIGN),
+    ("kq_mxfp4_gemm_wide", (GOOD, GOOD, GOOD, P(0x10002), 4, 4, 128, GOOD, 4, None), kq.KQ_ERR_ALIGN),
+    ("kq_mxfp4_gemm_wide", (None, None, None, None, 0, 4, 64, None, 4, None), kq.KQ_OK),
+    ("kq_transform_quantize_mxfp4_gemm", (GOOD, 4, 48, 48, GOOD, GOOD, GOOD, 4, GOOD, 4, None),
+     kq.KQ_ERR_SHAPE),
+    ("kq_transform_quantize_mxfp4_gemm", (GOOD, 4, 64, 64, GOOD, GOOD, GOOD, 4, GOOD, 3, None),
+     kq.KQ_ERR_SHAPE),
+    ("kq_transform_quantize_mxfp4_gemm", (GOOD, 4, 64, 32, GOOD, GOOD, GOOD, 4, GOOD, 4, None),
+     kq.KQ_ERR_SHAPE),
+    ("kq_transform_quantize_mxfp4_gemm", (GOOD, 4, 64, 64, None, GOOD, GOOD, 4, GOOD, 4, None),
+     kq.KQ_ERR_NULL),
+    ("kq_transform_quantize_mxfp4_gemm", (GOOD, 4, 64, 64, GOOD, GOOD, GOOD, 4, None, 4, None),
+     kq.KQ_ERR_NULL),
+    ("kq_transform_quantize_mxfp4_gemm", (P(0x10008), 4, 64, 64, GOOD, GOOD, GOOD, 4, GOOD, 4, None),
+     kq.KQ_ERR_ALIGN),
+    ("kq_transform_quantize_mxfp4_gemm", (GOOD, 4, 64, 68, GOOD, GOOD, GOOD, 4, GOOD, 4, None),
+     kq.KQ_ERR_ALIGN),
+    ("kq_transform_quantize_mxfp4_gemm", (GOOD, 4, 64, 64, P(0x10004), GOOD, GOOD, 4, GOOD, 4, None),
+     kq.KQ_ERR_ALIGN),
+    ("kq_transform_quantize_mxfp4_gemm", (None, 0, 64, 64, None, None, None, 4, None, 4, None), kq.KQ_OK),
     ("kq_hadamard_quantize_mxfp4", (GOOD, 4, 96, 96, 48, GOOD, GOOD, None, None), kq.KQ_ERR_SHAPE),
     ("kq_hadamard_quantize_mxfp4", (GOOD, 4, 64, 64, 16, GOOD, GOOD, None, None), kq.KQ_ERR_SHAPE),
     ("kq_hadamard_quantize_mxfp4", (GOOD, 4, 96, 96, 64, GOOD, GOOD, None, None), kq.KQ_ERR_SHAPE),
