@@ -242,6 +242,17 @@ def extras(torch, kq, synth, flux_sets, reps=100, warmup=20):
     out["w4a4_gemm_18432x3072x3072"] = {"median_us": round(med, 1),
                                          "TFLOPs": round(flops / (med * 1e-6) / 1e12, 1),
                                          "pct_fp4_peak": round(100 * flops / (med * 1e-6) / 10.1e15, 2)}
+    # the packed-scale kernel (256 x 256 tiles, 32 x 32 x 64 instruction): W's scales are
+    # packed once (offline, like the fold), A's on every call
+    psa = kq.pack_mxfp4_scales(sa)
+    psw = kq.pack_mxfp4_scales(sw)
+    d_pk = _events_us(torch, lambda: kq.pack_mxfp4_scales(sa, out=psa), 20, 3)
+    d_gp = _events_us(torch, lambda: kq.mxfp4_gemm_packed(ca, psa, cw, psw, out=O), 20, 3)
+    med_pk, med_gp = float(np.median(d_pk)), float(np.median(d_gp))
+    out["w4a4_gemm_18432x3072x3072"].update({
+        "packed_median_us": round(med_gp, 1), "packed_TFLOPs": round(flops / (med_gp * 1e-6) / 1e12, 1),
+        "packed_pct_fp4_peak": round(100 * flops / (med_gp * 1e-6) / 10.1e15, 2),
+        "pack_a_scales_us": round(med_pk, 2)})
     log("weight side / gemm: %s %s" % (out["weight_fold_3072x3072"], out["w4a4_gemm_18432x3072x3072"]))
     # the same product on the 128 x 512-tile kernel, and the layer with the transform and
     # quantizer in the product's prologue against the two launches it replaces
@@ -254,7 +265,8 @@ def extras(torch, kq, synth, flux_sets, reps=100, warmup=20):
         "wide_gemm_pct_fp4_peak": round(100 * flops / (med_w * 1e-6) / 10.1e15, 2),
         "fused_layer_us": round(med_f, 1), "fused_layer_TFLOPs": round(flops / (med_f * 1e-6) / 1e12, 1),
         "quantizer_us": round(med_q, 1),
-        "pipeline_us": round(med_q + min(med, med_w), 1)}
+        "pipeline_us": round(med_q + min(med, med_w), 1),
+        "pipeline_packed_us": round(med_q + med_pk + med_gp, 1)}
     log("fused layer: %s" % out["w4a4_layer_fused_18432x3072x3072"])
     out["w4a4_layer_lowrank_18432x3072x3072_r128"] = lowrank_layer_timing(torch, kq, A, fac, cw, sw, W)
     log("low-rank layer: %s" % out["w4a4_layer_lowrank_18432x3072x3072_r128"])

@@ -151,6 +151,42 @@ kq_status kq_mxfp4_gemm_wide(const uint8_t *codes_a, const uint8_t *scales_a, co
                              kq_stream_t stream);
 
 /*
+ * Re-layout of MXFP4 scales for kq_mxfp4_gemm_packed (a format change only,
+ * no arithmetic): the E8M0 bytes of Sec. 3.1's blocks, [rows][k/32] as the
+ * quantizers write them, become [k/256][rows][8], i.e. the eight scale bytes
+ * of one 256-wide k stage of consecutive rows are consecutive.
+ *   packed[(s * rows + i) * 8 + j] = scales[i * (k/32) + 8 s + j]
+ *   scales   device, [rows][k/32] bytes (no alignment needed)
+ *   packed   device, rows * (k/32) bytes, 8-byte aligned; must not overlap scales
+ * k % 256 == 0 (KQ_ERR_SHAPE); rows == 0 or k == 0 is a no-op.
+ */
+kq_status kq_pack_mxfp4_scales(const uint8_t *scales, int64_t rows, int64_t k, uint8_t *packed,
+                               kq_stream_t stream);
+
+/*
+ * The W4A4 GEMM of Eq. 2 (as kq_mxfp4_gemm: O[i][j] = sum_k deq(A)[i][k]
+ * deq(W)[j][k], fp32 accumulation on the scaled FP4 matrix instructions) with
+ * both operands' scales in the packed layout of kq_pack_mxfp4_scales. It runs
+ * on 256 x 256 output tiles with the 32 x 32 x 64 instruction (64 k per
+ * instruction, increasing k), so its results agree with kq_mxfp4_gemm to fp32
+ * rounding of the partial sums, and bit-for-bit whenever the fp32 sums are
+ * exact.
+ *   codes_a          device, [m][k/2] bytes, 16-byte aligned
+ *   packed_scales_a  device, packed [k/256][m][8], 16-byte aligned
+ *   codes_w          device, [n][k/2] bytes, 16-byte aligned
+ *   packed_scales_w  device, packed [k/256][n][8], 16-byte aligned
+ *   O                device, fp32 [m][ldo], ldo >= n, 4-byte aligned; written, not
+ *                    accumulated into (k == 0 writes zeros and reads no operand, which
+ *                    may then be NULL)
+ * k % 256 == 0 (KQ_ERR_SHAPE). 256 rows of codes, m k/32 and n k/32 scale
+ * bytes and 256 rows of O must each span fewer than 2^31 bytes
+ * (KQ_ERR_UNSUPPORTED).
+ */
+kq_status kq_mxfp4_gemm_packed(const uint8_t *codes_a, const uint8_t *packed_scales_a, const uint8_t *codes_w,
+                               const uint8_t *packed_scales_w, int64_t m, int64_t n, int64_t k, float *O,
+                               int64_t ldo, kq_stream_t stream);
+
+/*
  * The W4A4 layer with the activation transform and quantizer inside the
  * product (Sec. 1 Eq. 1-2; Sec. 3.2 Eq. 5 and Sec. 3.5.1 Eq. 12 for T; Sec. 3.1
  * for Q):

@@ -29,6 +29,8 @@ EXPORTS = (
     "kq_inverse_fold_weights",
     "kq_mxfp4_gemm",
     "kq_mxfp4_gemm_wide",
+    "kq_pack_mxfp4_scales",
+    "kq_mxfp4_gemm_packed",
     "kq_transform_quantize_mxfp4_gemm",
     "kq_hadamard_quantize_mxfp4",
     "kq_transform_quantize_mxfp4_y16",
@@ -72,6 +74,8 @@ def lib():
             "kq_factors_from_lu": [p, i64, p],
             "kq_mxfp4_gemm": [p, p, p, p, i64, i64, i64, p, i64, p],
             "kq_mxfp4_gemm_wide": [p, p, p, p, i64, i64, i64, p, i64, p],
+            "kq_pack_mxfp4_scales": [p, i64, i64, p, p],
+            "kq_mxfp4_gemm_packed": [p, p, p, p, i64, i64, i64, p, i64, p],
             "kq_transform_quantize_mxfp4_gemm": [p, i64, i64, i64, p, p, p, i64, p, i64, p],
             "kq_hadamard_quantize_mxfp4": [p, i64, i64, i64, i64, p, p, p, p],
             "kq_transform_quantize_mxfp4_y16": [p, i64, i64, i64, p, p, p, p, p],
@@ -341,6 +345,49 @@ def mxfp4_gemm(codes_a, scales_a, codes_w, scales_w, out=None, stream=None):
     _check("kq_mxfp4_gemm",
            lib().kq_mxfp4_gemm(_p(codes_a), _p(scales_a), _p(codes_w), _p(scales_w), m, n, k, _p(out),
                                out.stride(0), _stream_ptr(stream)))
+    return out
+
+
+def pack_mxfp4_scales(scales, out=None, stream=None):
+    """MXFP4 scales [rows][k/32] -> the GEMM-ready layout [k/256][rows][8] (k % 256 == 0)."""
+    torch = _torch()
+    _dev(scales, "scales", (torch.uint8,))
+    if scales.dim() != 2 or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous [rows][k/32] uint8 tensor")
+    rows, kb = scales.shape
+    k = kb * 32
+    if out is None:
+        out = torch.empty((kb // 8 if kb % 8 == 0 else 0, rows, 8), dtype=torch.uint8, device=scales.device)
+    _dev(out, "out", (torch.uint8,))
+    if out.numel() != rows * kb or not out.is_contiguous():
+        raise ValueError("out must be a contiguous uint8 tensor of rows * k/32 bytes")
+    _check("kq_pack_mxfp4_scales",
+           lib().kq_pack_mxfp4_scales(_p(scales), rows, k, _p(out), _stream_ptr(stream)))
+    return out
+
+
+def mxfp4_gemm_packed(codes_a, packed_scales_a, codes_w, packed_scales_w, out=None, stream=None):
+    """O = deq(A) deq(W)^T in fp32, scales packed by pack_mxfp4_scales (k % 256 == 0)."""
+    torch = _torch()
+    for t, nm in ((codes_a, "codes_a"), (packed_scales_a, "packed_scales_a"), (codes_w, "codes_w"),
+                  (packed_scales_w, "packed_scales_w")):
+        _dev(t, nm, (torch.uint8,))
+        if not t.is_contiguous():
+            raise ValueError(nm + " must be contiguous")
+    m, kb = codes_a.shape
+    n = codes_w.shape[0]
+    k = kb * 2
+    if tuple(codes_w.shape) != (n, kb) or packed_scales_a.numel() != m * (k // 32) or \
+            packed_scales_w.numel() != n * (k // 32):
+        raise ValueError("operand shapes do not match")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=codes_a.device)
+    _dev(out, "out", (torch.float32,))
+    if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
+        raise ValueError("out must be fp32 [m][n] with unit column stride")
+    _check("kq_mxfp4_gemm_packed",
+           lib().kq_mxfp4_gemm_packed(_p(codes_a), _p(packed_scales_a), _p(codes_w), _p(packed_scales_w), m, n, k,
+                                      _p(out), out.stride(0), _stream_ptr(stream)))
     return out
 
 

@@ -1,0 +1,350 @@
+// The W4A4 GEMM of Eq. 2 (KroQuant, arXiv 2607.21446v1),
+//   O = deq(Q(A T)) deq(Q(W T^{-T}))^T,
+// on 256 x 256 output tiles with gfx950's 32 x 32 x 64 scaled FP4 matrix
+// instruction, plus the scale re-layout it reads.
+//
+// Why this shape. On gfx950 the 16 x 16 x 128 scaled instruction issues at the
+// FP8 rate whatever the operand format, while the 32 x 32 x 64 form runs FP4
+// at twice that (measured: 4.35 vs 8.69 PFLOP/s of independent instructions).
+// A 256 x 256 tile per workgroup (four waves, 128 x 128 each, 256 accumulator
+// registers per lane) is the largest the register file holds, and it sets the
+// operand bytes per flop: the product is bound by how fast L2 and HBM feed the
+// CUs (about 30 TB/s for L2 hits, 6.5 TB/s once a working set leaves L2), so
+// every choice below is about moving fewer and fuller cache lines:
+//  - a stage covers 256 k, i.e. 128 code bytes (one full cache line) per row;
+//  - operands go straight from memory into LDS (buffer loads with the LDS bit),
+//    two stages double-buffered (2 x 68 KB), the next stage's 17 loads per wave
+//    issued among the current stage's first 16 matrix instructions;
+//  - scales are read in a GEMM-ready layout (kq_pack_mxfp4_scales): the 8 scale
+//    bytes of one 256-k stage of consecutive rows are consecutive, so a stage's
+//    scales for 256 rows are one 2 KB run instead of 256 scattered lines;
+//  - tiles are numbered so that each XCD (workgroups are dealt to the eight XCDs
+//    round robin) gets a contiguous run, walked in bands of 4 row tiles, which
+//    keeps the operand rows a run shares in that XCD's L2.
+//
+// LDS layout of a stage: A codes [256 rows][128 bytes], W codes likewise, A
+// scales [256 rows][8 bytes], W scales likewise. Code rows are stored with
+// their eight 16-byte chunks permuted (chunk c of row r at slot c ^ swz8(r));
+// a matrix read (32 rows of one chunk) then hits 32 distinct bank groups.
+//
+// Matrix layout (swapped operands, so a lane owns output rows): the
+// instruction's A operand is a W fragment and its B operand an A fragment;
+// lane l supplies row l % 32 of each and k group 2 j + l / 32 of step j (one MX
+// block: 16 code bytes, one scale byte), and receives O row l % 32 of its
+// fragment, columns 8 q + 4 (l / 32) + 0..3 of the W fragment in accumulator
+// registers 4 q .. 4 q + 3, so it stores 16 contiguous bytes per q.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kq.h"
+#include "kq_device.hpp"
+#include "kq_host.hpp"
+
+namespace kq {
+namespace g256 {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 256;
+constexpr int kCode = kTile * 128;              // code bytes per operand per stage
+constexpr int kScl = kTile * 8;                 // scale bytes per operand per stage
+constexpr int kStage = 2 * kCode + 2 * kScl;    // 68 KB
+constexpr int kGroupM = 4;                      // row tiles per band of the tile order
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+struct Geom {
+    int64_t m, n, ldo;
+    int kbytes;  // k / 2
+    int stages;  // k / 256
+    int tiles_m, tiles_n, nwg;
+    int vec_out;  // O 16-byte aligned and ldo % 4 == 0: 16-byte stores
+};
+
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Raw buffer descriptor in SGPRs: base, 32-bit record count (bytes); loads at
+// or past the count return zero.
+__device__ __forceinline__ i32x4_t sdesc(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4_t d;
+    d.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    d.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+    d.z = __builtin_amdgcn_readfirstlane((int)bytes);
+    d.w = 0x00020000;
+    return d;
+}
+
+// 16 bytes per lane from the buffer straight into LDS: lane l's bytes land at
+// lds + 16 l. M0 carries the LDS address and is restored afterwards; the
+// compiler does not track these loads, so completion is waited for explicitly
+// (vmcnt) before a barrier.
+__device__ __forceinline__ void dma16(const i32x4_t &d, uint32_t lds, uint32_t voff, uint32_t soff) {
+    uint32_t keep;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(keep)
+        : "s"(lds), "v"(voff), "s"(d), "s"(soff)
+        : "memory");
+}
+
+__device__ __forceinline__ void wait_loads_and_lds_then_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+struct Frag {
+    i32x8_t a[4], b[4];
+    uint32_t sa[4], sb[4];
+};
+
+__global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__restrict__ ca,
+                                                           const uint8_t *__restrict__ psa,
+                                                           const uint8_t *__restrict__ cw,
+                                                           const uint8_t *__restrict__ psw, Geom g,
+                                                           float *__restrict__ O) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+    const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+
+    // tile order: a contiguous run per XCD, bands of kGroupM row tiles, column-major inside a band
+    int tile = blockIdx.x;
+    {
+        const int q = g.nwg / 8, rm = g.nwg % 8, x = tile % 8, loc = tile / 8;
+        tile = x < rm ? x * (q + 1) + loc : rm * (q + 1) + (x - rm) * q + loc;
+    }
+    const int band = tile / (kGroupM * g.tiles_n), within = tile % (kGroupM * g.tiles_n);
+    const int gm = min(kGroupM, g.tiles_m - band * kGroupM);
+    const int tm = band * kGroupM + within % gm, tn = within / gm;
+    const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+    const int rows_a = (int)min<int64_t>(kTile, g.m - m0), rows_w = (int)min<int64_t>(kTile, g.n - n0);
+
+    // codes: rows past m or n are past the record count and read zero
+    const i32x4_t dca = sdesc(ca + m0 * g.kbytes, (uint32_t)(rows_a * g.kbytes));
+    const i32x4_t dcw = sdesc(cw + n0 * g.kbytes, (uint32_t)(rows_w * g.kbytes));
+    // packed scales: stage s of row i at 8 (s rows + i); a padding row past m or n
+    // reads some other row's bytes, harmless because its codes are zero and its
+    // outputs are never stored
+    const i32x4_t dsa = sdesc(psa, (uint32_t)(g.stages * 8 * g.m));
+    const i32x4_t dsw = sdesc(psw, (uint32_t)(g.stages * 8 * g.n));
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+    // code load j (0..7) of wave w: rows 64 w + 8 j + (lane >> 3), slot lane & 7
+    uint32_t cvoff[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int row = 64 * w + 8 * j + (lane >> 3);
+        cvoff[j] = (uint32_t)(row * g.kbytes) + 16u * (uint32_t)((lane & 7) ^ swz8(row & 15));
+    }
+    // loads of stage s: i in 0..7 A codes, 8..15 W codes
+    auto issue_code = [&](int s, int i) {
+        const uint32_t st = lds0 + (uint32_t)((s & 1) * kStage);
+        const uint32_t kb = 128u * (uint32_t)s;
+        if (i < 8) dma16(dca, st + (64 * w + 8 * i) * 128, cvoff[i], kb);
+        else dma16(dcw, st + kCode + (64 * w + 8 * (i - 8)) * 128, cvoff[i - 8], kb);
+    };
+    // scales of stage s: 1 KB per wave (w < 2: A rows 128 w .., else W rows 128 (w - 2) ..)
+    const int srow = 128 * (w & 1) + 2 * lane;
+    auto issue_scl = [&](int s) {
+        const uint32_t st = lds0 + (uint32_t)((s & 1) * kStage) + 2 * kCode + 1024 * (w & 1);
+        if (w < 2) dma16(dsa, st, (uint32_t)(8 * (m0 + srow)), (uint32_t)(8 * g.m) * (uint32_t)s);
+        else dma16(dsw, st + kScl, (uint32_t)(8 * (n0 + srow)), (uint32_t)(8 * g.n) * (uint32_t)s);
+    };
+
+    const int r = lane & 31, hi = lane >> 5;
+    const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
+    const int sh = 8 * hi;
+    int rdo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rdo[j] = r * 128 + 16 * ((2 * j + hi) ^ swz8(r & 15));
+
+    // step j of stage s: 16-byte fragments (k group 2 j + hi) and the scale dword holding it
+    auto read_frags = [&](int s, int j, Frag &F) {
+        const uint8_t *st = smem + (s & 1) * kStage;
+        const uint8_t *sc = st + 2 * kCode + 4 * (j >> 1) + 8 * r;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) F.sa[a] = *reinterpret_cast<const uint32_t *>(sc + 8 * (wm + 32 * a));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) F.sb[b] = *reinterpret_cast<const uint32_t *>(sc + kScl + 8 * (wn + 32 * b));
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(st + (wm + 32 * a) * 128 + rdo[j]);
+            F.a[a] = i32x8_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(st + kCode + (wn + 32 * b) * 128 + rdo[j]);
+            F.b[b] = i32x8_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+        }
+    };
+
+    floatx16_t acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+    // the scale byte of group 2 j + hi is byte 2 (j & 1) + hi of the dword
+    auto mma = [&](const Frag &F, int j, int a, int b) {
+        const int shj = sh + 16 * (j & 1);
+        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[b], F.a[a], acc[a][b], 4, 4, 0,
+                                                                    (int)(F.sb[b] >> shj), 0, (int)(F.sa[a] >> shj));
+    };
+    auto step = [&](const Frag &F, int j) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) mma(F, j, a, b);
+    };
+
+    if (g.stages > 0) {  // k == 0: O = 0
+    issue_scl(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) issue_code(0, i);
+    wait_loads_and_lds_then_barrier();
+    Frag F0, F1;
+    read_frags(0, 0, F0);
+
+    // Stage s (s + 1 < stages): the buffer of stage s + 1 held stage s - 1, whose
+    // last reads came before the previous barrier, so its loads go out during
+    // step 0; the barrier after step 2 makes them visible and ends every wave's
+    // reads of stage s before stage s + 2 reuses the buffer.
+    for (int s = 0; s + 1 < g.stages; ++s) {
+        read_frags(s, 1, F1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                mma(F0, 0, a, b);
+                issue_code(s + 1, 4 * a + b);
+                if (a == 1 && b == 3) issue_scl(s + 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        read_frags(s, 2, F0);
+        __builtin_amdgcn_sched_barrier(0);
+        step(F1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(s, 3, F1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(F0, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_loads_and_lds_then_barrier();
+        read_frags(s + 1, 0, F0);
+        __builtin_amdgcn_sched_barrier(0);
+        step(F1, 3);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    {
+        const int s = g.stages - 1;
+        read_frags(s, 1, F1);
+        step(F0, 0);
+        read_frags(s, 2, F0);
+        step(F1, 1);
+        read_frags(s, 3, F1);
+        step(F0, 2);
+        step(F1, 3);
+    }
+    }
+
+    // lane (r, hi) holds O row wm + 32 a + r, columns wn + 32 b + 8 q + 4 hi + 0..3;
+    // rows past m are past the record count and dropped, columns checked
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        O + m0 * g.ldo + n0, (short)0, (int)(((int64_t)(rows_a - 1) * g.ldo + (g.n - n0)) * 4), 0x00020000);
+    const bool full_n = g.vec_out && n0 + kTile <= g.n;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int row = wm + 32 * a + r;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = wn + 32 * b + 8 * q + 4 * hi;
+                const uint32_t off = (uint32_t)((row * g.ldo + col) * 4);
+                const u32x4_t v = {__float_as_uint(acc[a][b][4 * q]), __float_as_uint(acc[a][b][4 * q + 1]),
+                                   __float_as_uint(acc[a][b][4 * q + 2]), __float_as_uint(acc[a][b][4 * q + 3])};
+                if (full_n) {
+                    __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n0 + col + e < g.n) __builtin_amdgcn_raw_buffer_store_b32(v[e], ro, off + 4 * e, 0, 0);
+                }
+            }
+    }
+}
+
+// scales [rows][kblocks] -> [kblocks / 8][rows][8]: one 8-byte run per thread
+__global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t *__restrict__ in, int64_t rows,
+                                                          int64_t kblocks, uint8_t *__restrict__ out) {
+    const int64_t total = rows * (kblocks / 8);
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t s = i / rows, row = i % rows;
+        uint2 v;
+        __builtin_memcpy(&v, in + row * kblocks + 8 * s, 8);
+        *reinterpret_cast<uint2 *>(out + 8 * i) = v;
+    }
+}
+
+}  // namespace g256
+}  // namespace kq
+
+namespace {
+using kqhost::aligned;
+using kqhost::launched;
+}  // namespace
+
+extern "C" {
+
+kq_status kq_pack_mxfp4_scales(const uint8_t *scales, int64_t rows, int64_t k, uint8_t *packed,
+                               kq_stream_t stream) {
+    if (rows < 0 || k < 0 || k % 256 != 0) return KQ_ERR_SHAPE;
+    if (rows == 0 || k == 0) return KQ_OK;
+    if (!scales || !packed) return KQ_ERR_NULL;
+    if (!aligned(packed, 8)) return KQ_ERR_ALIGN;
+    if (rows > INT64_MAX / (k / 32)) return KQ_ERR_SHAPE;
+    const int64_t total = rows * (k / 256);
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(kq::g256::pack_scales_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
+                       dim3(256), 0, (hipStream_t)stream, scales, rows, k / 32, packed);
+    return launched();
+}
+
+kq_status kq_mxfp4_gemm_packed(const uint8_t *codes_a, const uint8_t *packed_scales_a, const uint8_t *codes_w,
+                               const uint8_t *packed_scales_w, int64_t m, int64_t n, int64_t k, float *O,
+                               int64_t ldo, kq_stream_t stream) {
+    if (m < 0 || n < 0 || k < 0 || k % 256 != 0 || ldo < n) return KQ_ERR_SHAPE;
+    if (m == 0 || n == 0) return KQ_OK;
+    if (!O || (k > 0 && (!codes_a || !packed_scales_a || !codes_w || !packed_scales_w))) return KQ_ERR_NULL;
+    if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || !aligned(packed_scales_a, 16) ||
+        !aligned(packed_scales_w, 16) || !aligned(O, 4))
+        return KQ_ERR_ALIGN;
+    // buffer record counts and offsets are 32-bit
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
+    if ((int64_t)256 * (k / 2) >= lim || m * (k / 32) >= lim || n * (k / 32) >= lim ||
+        ((int64_t)255 * ldo + n) * 4 >= lim || tiles_m * tiles_n >= lim)
+        return KQ_ERR_UNSUPPORTED;
+    kq::g256::Geom g;
+    g.m = m;
+    g.n = n;
+    g.ldo = ldo;
+    g.kbytes = (int)(k / 2);
+    g.stages = (int)(k / 256);
+    g.tiles_m = (int)tiles_m;
+    g.tiles_n = (int)tiles_n;
+    g.nwg = (int)(tiles_m * tiles_n);
+    g.vec_out = aligned(O, 16) && ldo % 4 == 0;
+    hipLaunchKernelGGL(kq::g256::gemm256_kernel, dim3((unsigned)g.nwg), dim3(kq::g256::kThreads), 0,
+                       (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, O);
+    return launched();
+}
+
+}  // extern "C"

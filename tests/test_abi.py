@@ -72,6 +72,23 @@ GOOD = P(0x10000)  # never dereferenced: every case below fails before a launch
     ("kq_mxfp4_gemm_wide", (P(0x10008), GOOD, GOOD, GOOD, 4, 4, 64, GOOD, 4, None), kq.KQ_ERR_ALIGN),
     ("kq_mxfp4_gemm_wide", (GOOD, GOOD, GOOD, P(0x10002), 4, 4, 128, GOOD, 4, None), kq.KQ_ERR_ALIGN),
     ("kq_mxfp4_gemm_wide", (None, None, None, None, 0, 4, 64, None, 4, None), kq.KQ_OK),
+    ("kq_pack_mxfp4_scales", (GOOD, 4, 128, GOOD, None), kq.KQ_ERR_SHAPE),
+    ("kq_pack_mxfp4_scales", (GOOD, -1, 256, GOOD, None), kq.KQ_ERR_SHAPE),
+    ("kq_pack_mxfp4_scales", (None, 4, 256, GOOD, None), kq.KQ_ERR_NULL),
+    ("kq_pack_mxfp4_scales", (GOOD, 4, 256, None, None), kq.KQ_ERR_NULL),
+    ("kq_pack_mxfp4_scales", (GOOD, 4, 256, P(0x10004), None), kq.KQ_ERR_ALIGN),
+    ("kq_pack_mxfp4_scales", (None, 0, 256, None, None), kq.KQ_OK),
+    ("kq_pack_mxfp4_scales", (None, 4, 0, None, None), kq.KQ_OK),
+    ("kq_mxfp4_gemm_packed", (GOOD, GOOD, GOOD, GOOD, 4, 4, 128, GOOD, 4, None), kq.KQ_ERR_SHAPE),
+    ("kq_mxfp4_gemm_packed", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, GOOD, 3, None), kq.KQ_ERR_SHAPE),
+    ("kq_mxfp4_gemm_packed", (GOOD, GOOD, GOOD, GOOD, -1, 4, 256, GOOD, 4, None), kq.KQ_ERR_SHAPE),
+    ("kq_mxfp4_gemm_packed", (GOOD, None, GOOD, GOOD, 4, 4, 256, GOOD, 4, None), kq.KQ_ERR_NULL),
+    ("kq_mxfp4_gemm_packed", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, None, 4, None), kq.KQ_ERR_NULL),
+    ("kq_mxfp4_gemm_packed", (P(0x10008), GOOD, GOOD, GOOD, 4, 4, 256, GOOD, 4, None), kq.KQ_ERR_ALIGN),
+    ("kq_mxfp4_gemm_packed", (GOOD, P(0x10008), GOOD, GOOD, 4, 4, 256, GOOD, 4, None), kq.KQ_ERR_ALIGN),
+    ("kq_mxfp4_gemm_packed", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, P(0x10002), 4, None), kq.KQ_ERR_ALIGN),
+    ("kq_mxfp4_gemm_packed", (GOOD, GOOD, GOOD, GOOD, 4, 4, 1 << 24, GOOD, 4, None), kq.KQ_ERR_UNSUPPORTED),
+    ("kq_mxfp4_gemm_packed", (None, None, None, None, 0, 4, 256, None, 4, None), kq.KQ_OK),
     ("kq_transform_quantize_mxfp4_gemm", (GOOD, 4, 48, 48, GOOD, GOOD, GOOD, 4, GOOD, 4, None),
      kq.KQ_ERR_SHAPE),
     ("kq_transform_quantize_mxfp4_gemm", (GOOD, 4, 64, 64, GOOD, GOOD, GOOD, 4, GOOD, 3, None),

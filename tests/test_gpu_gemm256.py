@@ -1,0 +1,173 @@
+"""GPU parity of the packed-scale W4A4 GEMM (kq_mxfp4_gemm_packed, 256 x 256 tiles on
+the 32 x 32 x 64 scaled FP4 instruction) and of its scale re-layout
+(kq_pack_mxfp4_scales): the re-layout against its definition (byte for byte), the
+product against the oracle's dequantized fp64 product (per element, to fp32 rounding
+of the partial sums), against kq_mxfp4_gemm (bit-identical where every fp32 partial
+sum is exact), ragged shapes, padded and unaligned outputs, k = 0, and the FLUX
+18432 x 3072 x 3072 layer.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+def case(msg):
+    print("[case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch
+
+
+@pytest.fixture(scope="module")
+def kq():
+    import mxfp4_activation_quantizer_amd as kq
+    kq.lib()
+    return kq
+
+
+def dev(torch, x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def packed_reference(scales):
+    """[rows][k/32] -> [k/256][rows][8], written out from the layout's definition."""
+    rows, kb = scales.shape
+    out = np.empty((kb // 8, rows, 8), dtype=np.uint8)
+    for s in range(kb // 8):
+        out[s] = scales[:, 8 * s:8 * s + 8]
+    return out
+
+
+def operands(rng, m, n, k, lo=118, hi=136):
+    ca = rng.integers(0, 256, (m, k // 2), dtype=np.uint8)
+    cw = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    sa = rng.integers(lo, hi, (m, k // 32), dtype=np.uint8)
+    sw = rng.integers(lo, hi, (n, k // 32), dtype=np.uint8)
+    return ca, sa, cw, sw
+
+
+def run_packed(torch, kq, ca, sa, cw, sw, out=None):
+    dca, dsa, dcw, dsw = (dev(torch, x) for x in (ca, sa, cw, sw))
+    psa = kq.pack_mxfp4_scales(dsa)
+    psw = kq.pack_mxfp4_scales(dsw)
+    O = kq.mxfp4_gemm_packed(dca, psa, dcw, psw, out=out)
+    torch.cuda.synchronize()
+    return O, (dca, dsa, dcw, dsw)
+
+
+def bound(orc, ca, sa, cw, sw, k):
+    absdot = np.abs(orc.dequantize(ca, sa, k)) @ np.abs(orc.dequantize(cw, sw, k)).T
+    return 64 * 2.0 ** -24 * absdot + 1e-30
+
+
+@pytest.mark.parametrize("rows,k,seed", [(1, 256, 1), (37, 512, 2), (300, 3072, 3), (4099, 768, 4)])
+def test_pack_scales_is_the_layout(torch_dev, kq, rows, k, seed):
+    torch = torch_dev
+    case("pack scales rows=%d k=%d" % (rows, k))
+    rng = np.random.default_rng(seed)
+    s = rng.integers(0, 256, (rows, k // 32), dtype=np.uint8)
+    got = kq.pack_mxfp4_scales(dev(torch, s))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().reshape(-1), packed_reference(s).reshape(-1))
+
+
+@pytest.mark.parametrize("m,n,k,seed", [(1, 1, 256, 1), (37, 70, 256, 2), (257, 513, 512, 3),
+                                        (300, 1100, 768, 4), (256, 256, 2304, 5), (1000, 700, 512, 6)])
+def test_packed_gemm_matches_oracle(torch_dev, kq, orc, m, n, k, seed):
+    """Seeded random MXFP4 operands (any code byte, scales around 2^0); ragged m and n."""
+    torch = torch_dev
+    case("packed gemm m=%d n=%d k=%d" % (m, n, k))
+    ca, sa, cw, sw = operands(np.random.default_rng(seed), m, n, k)
+    O, ops = run_packed(torch, kq, ca, sa, cw, sw)
+    got = O.cpu().numpy().astype(np.float64)
+    ref = orc.gemm_dequant(ca, sa, cw, sw, k)
+    assert np.all(np.abs(got - ref) <= bound(orc, ca, sa, cw, sw, k))
+    O_old = kq.mxfp4_gemm(*ops).cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - O_old) <= 2 * bound(orc, ca, sa, cw, sw, k))
+
+
+@pytest.mark.parametrize("m,n,k,seed", [(300, 600, 3072, 7), (513, 257, 1024, 8)])
+def test_packed_gemm_exact_sums_bit_identical(torch_dev, kq, orc, m, n, k, seed):
+    """Scales in 2^-1 .. 2^1: every product is a multiple of 2^-4 below 144 in magnitude,
+    so for k <= 3072 every fp32 partial sum is exact and all summation orders agree:
+    the packed kernel, kq_mxfp4_gemm and the fp64 oracle give the same fp32 values."""
+    torch = torch_dev
+    case("packed gemm exact sums m=%d n=%d k=%d" % (m, n, k))
+    ca, sa, cw, sw = operands(np.random.default_rng(seed), m, n, k, 126, 129)
+    O, ops = run_packed(torch, kq, ca, sa, cw, sw)
+    O_old = kq.mxfp4_gemm(*ops)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O_old)
+    ref = orc.gemm_dequant(ca, sa, cw, sw, k)
+    assert np.array_equal(O.cpu().numpy(), ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("ldo,off", [(260, 0), (263, 1)])
+def test_packed_gemm_padded_output_and_guard(torch_dev, kq, orc, ldo, off):
+    """ldo > n (16-byte stores when O is 16-byte aligned and ldo % 4 == 0, single
+    stores otherwise): the padding columns and the bytes around O stay untouched."""
+    torch = torch_dev
+    case("packed gemm ldo=%d offset=%d" % (ldo, off))
+    m, n, k = 300, 256, 512
+    ca, sa, cw, sw = operands(np.random.default_rng(9), m, n, k)
+    guard = 64
+    buf = torch.full((off + m * ldo + guard,), -7.5, dtype=torch.float32, device="cuda")
+    out = buf[off:off + m * ldo].view(m, ldo)[:, :n]
+    O, _ = run_packed(torch, kq, ca, sa, cw, sw, out=out)
+    whole = buf.cpu().numpy()
+    assert np.all(whole[:off] == -7.5) and np.all(whole[off + m * ldo:] == -7.5)
+    mat = whole[off:off + m * ldo].reshape(m, ldo)
+    assert np.all(mat[:, n:] == -7.5)
+    ref = orc.gemm_dequant(ca, sa, cw, sw, k)
+    assert np.all(np.abs(mat[:, :n].astype(np.float64) - ref) <= bound(orc, ca, sa, cw, sw, k))
+
+
+def test_packed_gemm_k0_and_empty(torch_dev, kq):
+    torch = torch_dev
+    case("packed gemm k=0 and empty")
+    z = torch.zeros((0,), dtype=torch.uint8, device="cuda")
+    ca = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
+    cw = torch.zeros((7, 0), dtype=torch.uint8, device="cuda")
+    out = torch.full((5, 7), 3.0, dtype=torch.float32, device="cuda")
+    kq.mxfp4_gemm_packed(ca, z, cw, z, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+    e = torch.zeros((0, 128), dtype=torch.uint8, device="cuda")
+    O = kq.mxfp4_gemm_packed(e, torch.zeros((0,), dtype=torch.uint8, device="cuda"), e,
+                             torch.zeros((0,), dtype=torch.uint8, device="cuda"))
+    assert O.shape == (0, 0)
+
+
+def test_packed_gemm_flux_layer(torch_dev, kq, orc):
+    """FLUX 18432 x 3072 activations against 3072 x 3072 weights, the launch the bench
+    times: every element against kq_mxfp4_gemm (fp32 rounding of different partial
+    sums), sampled rows against the oracle's fp64 product."""
+    torch = torch_dev
+    m, n, k = 18432, 3072, 3072
+    case("packed gemm flux %dx%dx%d" % (m, n, k))
+    ca, sa, cw, sw = operands(np.random.default_rng(12), m, n, k)
+    O, ops = run_packed(torch, kq, ca, sa, cw, sw)
+    O_old = kq.mxfp4_gemm(*ops)
+    torch.cuda.synchronize()
+    got = O.cpu().numpy().astype(np.float64)
+    old = O_old.cpu().numpy().astype(np.float64)
+    # every element: both kernels are within 64 ulp-steps of the exact sum, and
+    # sum_k |a_ik| max_j |w_jk| bounds every sum of |products| in row i
+    wmax = np.abs(orc.dequantize(cw, sw, k)).max(axis=0)
+    rowbound = np.abs(orc.dequantize(ca, sa, k)) @ wmax
+    diff = np.abs(got - old)
+    assert np.all(diff <= 2 * 64 * 2.0 ** -24 * rowbound[:, None] + 1e-30)
+    rows = np.random.default_rng(13).choice(m, 48, replace=False)
+    ref = orc.gemm_dequant(ca, sa, cw, sw, k, rows=rows)
+    assert np.all(np.abs(got[rows] - ref) <= bound(orc, ca[rows], sa[rows], cw, sw, k))
+    print("[gemm256] flux: max |packed - gemm| %.3g (max allowed %.3g), sampled rows vs oracle max rel %.3g" % (
+        diff.max(), (2 * 64 * 2.0 ** -24 * rowbound).max(),
+        np.max(np.abs(got[rows] - ref) / (np.abs(ref) + 1e-30))), flush=True)
