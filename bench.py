@@ -294,7 +294,13 @@ def lowrank_layer_timing(torch, kq, A, fac, cw, sw, W, r=128, reps=20):
            "gemm_lowrank_us": med(lambda: kq.mxfp4_gemm_lowrank(ca, sa, cw, sw, Z, cl, sl, out=O)),
            "quantize_us": med(lambda: kq.transform_quantize_mxfp4(A, fac, codes=ca, scales=sa)),
            "gemm_us": med(lambda: kq.mxfp4_gemm(ca, sa, cw, sw, out=O))}
+    # R decoded to bf16 once per call, then the projection without in-kernel decoding
+    r16 = kq.dequantize_mxfp4_bf16(cr, sr)
+    res["decode_r_us"] = med(lambda: kq.dequantize_mxfp4_bf16(cr, sr, out=r16))
+    res["project_bf16_us"] = med(lambda: kq.lowrank_project_bf16(y16, r16, out=Z))
     res["layer_with_branch_us"] = round(res["quantize_y16_us"] + res["project_us"] + res["gemm_lowrank_us"], 1)
+    res["layer_with_branch_r16_us"] = round(res["quantize_y16_us"] + res["decode_r_us"] + res["project_bf16_us"] +
+                                            res["gemm_lowrank_us"], 1)
     res["layer_plain_us"] = round(res["quantize_us"] + res["gemm_us"], 1)
     return res
 

@@ -258,6 +258,29 @@ kq_status kq_lowrank_project(const uint16_t *X16, int64_t m, int64_t d, int64_t 
                              const uint8_t *scales_r, int64_t r, float *Z, kq_stream_t stream);
 
 /*
+ * As kq_lowrank_project with R already in bf16 (for example R decoded once per
+ * call by kq_dequantize_mxfp4_bf16: the decode is exact, so Z is bit-identical
+ * to kq_lowrank_project's), so the product spends no vector ALU time on R.
+ *   R16  device, bf16 bits [r][d] contiguous, 16-byte aligned
+ * Other arguments and rules as kq_lowrank_project; 64 rows of X16 and 128 rows
+ * of R16 must each span fewer than 2^31 bytes (KQ_ERR_UNSUPPORTED).
+ */
+kq_status kq_lowrank_project_bf16(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint16_t *R16,
+                                  int64_t r, float *Z, kq_stream_t stream);
+
+/*
+ * MXFP4 -> bf16 (Sec. 3.1's dequantization deq(code, scale) = E2M1(code)
+ * 2^(scale - 127)): every value has at most two significant bits, so it is
+ * exact in bf16 whenever it is a normal or subnormal bf16 number.
+ *   codes   device, [rows][k/2] bytes, 4-byte aligned
+ *   scales  device, [rows][k/32]
+ *   out     device, bf16 bits [rows][k], 16-byte aligned
+ * k % 32 == 0 (KQ_ERR_SHAPE).
+ */
+kq_status kq_dequantize_mxfp4_bf16(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t k,
+                                   uint16_t *out, kq_stream_t stream);
+
+/*
  * The W4A4 layer of Eq. 11: O = deq(A) deq(W)^T + Z deq(L)^T, the low-rank term
  * added in the same kernel (Z split into two bf16 terms, exact to 2^-16
  * relative; deq(L) exact in bf16), so O is written once.

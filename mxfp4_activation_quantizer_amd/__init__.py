@@ -30,6 +30,8 @@ EXPORTS = (
     "kq_mxfp4_gemm",
     "kq_mxfp4_gemm_wide",
     "kq_pack_mxfp4_scales",
+    "kq_lowrank_project_bf16",
+    "kq_dequantize_mxfp4_bf16",
     "kq_mxfp4_gemm_packed",
     "kq_transform_quantize_mxfp4_gemm",
     "kq_hadamard_quantize_mxfp4",
@@ -75,6 +77,8 @@ def lib():
             "kq_mxfp4_gemm": [p, p, p, p, i64, i64, i64, p, i64, p],
             "kq_mxfp4_gemm_wide": [p, p, p, p, i64, i64, i64, p, i64, p],
             "kq_pack_mxfp4_scales": [p, i64, i64, p, p],
+            "kq_lowrank_project_bf16": [p, i64, i64, i64, p, i64, p, p],
+            "kq_dequantize_mxfp4_bf16": [p, p, i64, i64, p, p],
             "kq_mxfp4_gemm_packed": [p, p, p, p, i64, i64, i64, p, i64, p],
             "kq_transform_quantize_mxfp4_gemm": [p, i64, i64, i64, p, p, p, i64, p, i64, p],
             "kq_hadamard_quantize_mxfp4": [p, i64, i64, i64, i64, p, p, p, p],
@@ -242,6 +246,46 @@ def lowrank_project(X16, codes_r, scales_r, out=None, stream=None):
         raise ValueError("out must be a contiguous fp32 [m][r] tensor")
     _check("kq_lowrank_project",
            lib().kq_lowrank_project(_p(X16), m, d, ldx, _p(codes_r), _p(scales_r), r, _p(out), _stream_ptr(stream)))
+    return out
+
+
+def dequantize_mxfp4_bf16(codes, scales, out=None, stream=None):
+    """deq(codes, scales) as bf16 [rows][k] (exact): codes [rows][k/2], scales [rows][k/32]."""
+    torch = _torch()
+    for t, nm in ((codes, "codes"), (scales, "scales")):
+        _dev(t, nm, (torch.uint8,))
+        if t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(nm + " must be a contiguous 2-D uint8 tensor")
+    rows, kb = codes.shape
+    k = kb * 2
+    if tuple(scales.shape) != (rows, k // 32):
+        raise ValueError("scales must be [rows][k/32]")
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.bfloat16, device=codes.device)
+    _dev(out, "out", (torch.bfloat16, torch.int16, torch.uint16))
+    if tuple(out.shape) != (rows, k) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [rows][k] tensor")
+    _check("kq_dequantize_mxfp4_bf16",
+           lib().kq_dequantize_mxfp4_bf16(_p(codes), _p(scales), rows, k, _p(out), _stream_ptr(stream)))
+    return out
+
+
+def lowrank_project_bf16(X16, R16, out=None, stream=None):
+    """Z = X16 R16^T in fp32: X16 bf16 [m][d], R16 bf16 [r][d] (e.g. dequantize_mxfp4_bf16 of R)."""
+    torch = _torch()
+    _dev(X16, "X16", (torch.bfloat16, torch.int16, torch.uint16))
+    _dev(R16, "R16", (torch.bfloat16, torch.int16, torch.uint16))
+    m, d, ldx = _rows(X16, "X16")
+    if R16.dim() != 2 or R16.shape[1] != d or not R16.is_contiguous():
+        raise ValueError("R16 must be a contiguous bf16 [r][d] tensor")
+    r = R16.shape[0]
+    if out is None:
+        out = torch.empty((m, r), dtype=torch.float32, device=X16.device)
+    _dev(out, "out", (torch.float32,))
+    if tuple(out.shape) != (m, r) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [m][r] tensor")
+    _check("kq_lowrank_project_bf16",
+           lib().kq_lowrank_project_bf16(_p(X16), m, d, ldx, _p(R16), r, _p(out), _stream_ptr(stream)))
     return out
 
 

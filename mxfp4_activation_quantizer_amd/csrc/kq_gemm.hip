@@ -48,6 +48,14 @@ __device__ __forceinline__ void split_bf16x8(const float x[8], bf16x8_t &hi, bf1
     __builtin_memcpy(&lo, l, 16);
 }
 
+// MXFP4 -> bf16, exact (see decode_fp4x8_bf16): one thread per 8 codes.
+__global__ __launch_bounds__(kThreads) void dequantize_bf16_kernel(const uint32_t *__restrict__ codes,
+                                                                   const uint8_t *__restrict__ scales, int64_t n8,
+                                                                   bf16x8_t *__restrict__ out) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x)
+        out[i] = decode_fp4x8_bf16(codes[i], scales[i / 4]);
+}
+
 // Z = X Q(R)^T: X bf16 [m][ldx] (the branch's 16-bit activations), R MXFP4
 // [r][d] (codes [r][d/2], scales [r][d/32]), Z fp32 [m][r]. A workgroup
 // computes 64 rows x 128 columns of Z, each wave 16 rows x 128 columns (8 MFMA
@@ -64,10 +72,15 @@ struct ProjGeom {
 };
 
 constexpr int kProjRow = 128 * 2 + 16;  // bytes per staged R column: 128 bf16 + 16 of padding
+constexpr int kProjAhead = 3;            // steps of X in flight per wave
 
+// R16: R arrives already in bf16 ([r][d], e.g. from kq_dequantize_mxfp4_bf16) and
+// is copied into LDS as it is; otherwise the workgroup decodes MXFP4 R itself.
+template <bool R16>
 __global__ __launch_bounds__(kThreads) void lowrank_project_kernel(const uint16_t *__restrict__ X, ProjGeom g,
                                                                    const uint8_t *__restrict__ cr,
                                                                    const uint8_t *__restrict__ sr,
+                                                                   const uint16_t *__restrict__ r16,
                                                                    float *__restrict__ Z) {
     __shared__ __attribute__((aligned(16))) uint8_t rl[2][128 * kProjRow];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -80,20 +93,52 @@ __global__ __launch_bounds__(kThreads) void lowrank_project_kernel(const uint16_
     struct RRegs {
         uint4 c[2];
         uint32_t s[2];
+        uint4 h[8];  // R16: 64 bf16 of column dc
     };
+    // Loads go through per-tile buffer descriptors whose record counts end at the
+    // last valid row (rows past m or r read zero), with no branches around them,
+    // so the compiler's wait counts stay exact; a load past d gets an offset
+    // beyond the record count and reads zero too.
+    const int64_t rows_r = g.r - col0 < 128 ? g.r - col0 : 128;
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(R16 ? nullptr : cr + col0 * (g.d / 2)), (short)0,
+                                          (int)(R16 ? 0 : rows_r * (g.d / 2)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(R16 ? nullptr : sr + col0 * (g.d / 32)), (short)0,
+                                          (int)(R16 ? 0 : rows_r * (g.d / 32)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(R16 ? r16 + col0 * g.d : nullptr), (short)0, (int)(R16 ? rows_r * g.d * 2 : 0),
+        0x00020000);
     auto fetch_r = [&](int64_t k0, RRegs &R) {
+        if (R16) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int64_t k = k0 + 64 * dh + 8 * i;
+                const uint32_t o = k < g.d ? (uint32_t)((dc * g.d + k) * 2) : 0x80000000u;
+                const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rh, o, 0, 0);
+                R.h[i] = make_uint4(v[0], v[1], v[2], v[3]);
+            }
+            return;
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int64_t k = k0 + 64 * dh + 32 * h;  // a 32-k group
-            R.c[h] = make_uint4(0, 0, 0, 0);
-            R.s[h] = 127;
-            if (rn < g.r && k < g.d) {
-                R.c[h] = *reinterpret_cast<const uint4 *>(cr + rn * (g.d / 2) + k / 2);
-                R.s[h] = sr[rn * (g.d / 32) + k / 32];
-            }
+            // past d the offset is moved beyond every record count, so the load
+            // returns zero codes (and a zero scale byte, which only scales zeros)
+            const bool in = k < g.d;
+            const uint32_t co = in ? (uint32_t)(dc * (g.d / 2) + k / 2) : 0x80000000u;
+            const uint32_t so = in ? (uint32_t)(dc * (g.d / 32) + k / 32) : 0x80000000u;
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc, co, 0, 0);
+            R.c[h] = make_uint4(v[0], v[1], v[2], v[3]);
+            R.s[h] = __builtin_amdgcn_raw_buffer_load_b8(rs, so, 0, 0);
         }
     };
     auto stash_r = [&](uint8_t *buf, const RRegs &R) {
+        if (R16) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4 *>(buf + dc * kProjRow + 128 * dh + 16 * i) = R.h[i];
+            return;
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             uint8_t *dst = buf + dc * kProjRow + 128 * dh + 64 * h;
@@ -103,46 +148,58 @@ __global__ __launch_bounds__(kThreads) void lowrank_project_kernel(const uint16_
             *reinterpret_cast<bf16x8_t *>(dst + 48) = decode_fp4x8_bf16(R.c[h].w, R.s[h]);
         }
     };
+    const int64_t rows_x = g.m - tm * 64 < 64 ? g.m - tm * 64 : 64;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(X + tm * 64 * g.ldx), (short)0, (int)(rows_x * g.ldx * 2), 0x00020000);
+    const uint32_t xoff = (uint32_t)(((wave * 16 + (lane & 15)) * g.ldx + 8 * grp) * 2);
     auto fetch_x = [&](int64_t k0, uint4 q[4]) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int64_t k = k0 + 32 * u + 8 * grp;
-            q[u] = make_uint4(0, 0, 0, 0);
-            if (row < g.m && k < g.d) q[u] = load_stream(reinterpret_cast<const uint4 *>(X + row * g.ldx + k), true);
+            const uint32_t xo = k < g.d ? xoff + (uint32_t)((k0 + 32 * u) * 2) : 0x80000000u;
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 2);
+            q[u] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     };
     floatx4_t acc[8];
 #pragma unroll
     for (int b = 0; b < 8; ++b) acc[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    // X is the only HBM stream and there is about one wave per SIMD, so each
+    // wave keeps kProjAhead steps of its X rows in flight (a register ring);
+    // the R slice (L2-resident) is fetched one step ahead into the other LDS buffer.
     RRegs R;
-    uint4 xq[4], xn[4];
+    uint4 xq[kProjAhead][4];
+    const int64_t steps = (g.d + 127) / 128;
     fetch_r(0, R);
-    fetch_x(0, xq);
+#pragma unroll
+    for (int p = 0; p < kProjAhead; ++p) fetch_x((int64_t)p * 128, xq[p]);
     stash_r(rl[0], R);
     __syncthreads();
-    const int64_t steps = (g.d + 127) / 128;
-    for (int64_t st = 0; st < steps; ++st) {
-        const int cur = (int)(st & 1);
-        if (st + 1 < steps) {
+    // the step count is rounded up to a multiple of kProjAhead: a step past d loads
+    // zeros (X and R), so its products add exact zeros, and the loop body has no
+    // branch for the compiler's wait counts to lose track across
+    const int64_t steps_up = (steps + kProjAhead - 1) / kProjAhead * kProjAhead;
+    for (int64_t st0 = 0; st0 < steps_up; st0 += kProjAhead) {
+#pragma unroll
+        for (int p = 0; p < kProjAhead; ++p) {
+            const int64_t st = st0 + p;
+            const int cur = (int)(st & 1);
             fetch_r((st + 1) * 128, R);
-            fetch_x((st + 1) * 128, xn);
-        }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const bf16x8_t xa = as_bf16x8(xq[u]);
+            for (int u = 0; u < 4; ++u) {
+                const bf16x8_t xa = as_bf16x8(xq[p][u]);
 #pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const bf16x8_t rb = *reinterpret_cast<const bf16x8_t *>(rl[cur] + (b * 16 + (lane & 15)) * kProjRow +
-                                                                        64 * u + 16 * grp);
-                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, rb, acc[b], 0, 0, 0);
+                for (int b = 0; b < 8; ++b) {
+                    const bf16x8_t rb = *reinterpret_cast<const bf16x8_t *>(
+                        rl[cur] + (b * 16 + (lane & 15)) * kProjRow + 64 * u + 16 * grp);
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, rb, acc[b], 0, 0, 0);
+                }
             }
-        }
-        if (st + 1 < steps) {
+            // refill this slot with the step kProjAhead ahead (zeros past d)
+            fetch_x((st + kProjAhead) * 128, xq[p]);
             stash_r(rl[cur ^ 1], R);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) xq[u] = xn[u];
+            __syncthreads();
         }
-        __syncthreads();
     }
     const int64_t orow0 = tm * 64 + wave * 16 + grp * 4;
 #pragma unroll
@@ -444,9 +501,42 @@ kq_status kq_lowrank_project(const uint16_t *X16, int64_t m, int64_t d, int64_t 
     if (!aligned(X16, 16) || ldx % 8 != 0 || !aligned(codes_r, 16) || !aligned(Z, 16)) return KQ_ERR_ALIGN;
     const int64_t tiles_m = (m + 63) / 64, tiles_r = (r + 127) / 128;
     if (tiles_m * tiles_r > 0x7FFFFFFF || m > INT64_MAX / 4 / (ldx > r ? ldx : r)) return KQ_ERR_SHAPE;
+    // per-tile buffer records are 32-bit: 64 rows of X, 128 rows of R's codes
+    if ((int64_t)64 * ldx * 2 >= ((int64_t)1 << 31) || (int64_t)128 * (d / 2) + 128 >= ((int64_t)1 << 31))
+        return KQ_ERR_UNSUPPORTED;
     kq::ProjGeom g{m, d, ldx, r, tiles_r};
-    hipLaunchKernelGGL(kq::lowrank_project_kernel, dim3((unsigned)(tiles_m * tiles_r)), dim3(kq::kThreads), 0,
-                       (hipStream_t)stream, X16, g, codes_r, scales_r, Z);
+    hipLaunchKernelGGL(kq::lowrank_project_kernel<false>, dim3((unsigned)(tiles_m * tiles_r)), dim3(kq::kThreads),
+                       0, (hipStream_t)stream, X16, g, codes_r, scales_r, nullptr, Z);
+    return launched();
+}
+
+kq_status kq_lowrank_project_bf16(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint16_t *R16,
+                                  int64_t r, float *Z, kq_stream_t stream) {
+    if (m < 0 || d < 0 || d % 32 != 0 || ldx < d || r <= 0 || r % 32 != 0) return KQ_ERR_SHAPE;
+    if (m == 0 || d == 0) return KQ_OK;
+    if (!X16 || !R16 || !Z) return KQ_ERR_NULL;
+    if (!aligned(X16, 16) || ldx % 8 != 0 || !aligned(R16, 16) || !aligned(Z, 16)) return KQ_ERR_ALIGN;
+    const int64_t tiles_m = (m + 63) / 64, tiles_r = (r + 127) / 128;
+    if (tiles_m * tiles_r > 0x7FFFFFFF || m > INT64_MAX / 4 / (ldx > r ? ldx : r)) return KQ_ERR_SHAPE;
+    if ((int64_t)64 * ldx * 2 >= ((int64_t)1 << 31) || (int64_t)128 * d * 2 >= ((int64_t)1 << 31))
+        return KQ_ERR_UNSUPPORTED;
+    kq::ProjGeom g{m, d, ldx, r, tiles_r};
+    hipLaunchKernelGGL(kq::lowrank_project_kernel<true>, dim3((unsigned)(tiles_m * tiles_r)), dim3(kq::kThreads),
+                       0, (hipStream_t)stream, X16, g, nullptr, nullptr, R16, Z);
+    return launched();
+}
+
+kq_status kq_dequantize_mxfp4_bf16(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t k,
+                                   uint16_t *out, kq_stream_t stream) {
+    if (rows < 0 || k < 0 || k % 32 != 0) return KQ_ERR_SHAPE;
+    if (rows == 0 || k == 0) return KQ_OK;
+    if (!codes || !scales || !out) return KQ_ERR_NULL;
+    if (!aligned(codes, 4) || !aligned(out, 16)) return KQ_ERR_ALIGN;
+    if (rows > INT64_MAX / k) return KQ_ERR_SHAPE;
+    const int64_t n8 = rows * (k / 8), blocks = (n8 + kq::kThreads - 1) / kq::kThreads;
+    hipLaunchKernelGGL(kq::dequantize_bf16_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)),
+                       dim3(kq::kThreads), 0, (hipStream_t)stream, reinterpret_cast<const uint32_t *>(codes), scales,
+                       n8, reinterpret_cast<kq::bf16x8_t *>(out));
     return launched();
 }
 

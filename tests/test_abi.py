@@ -72,6 +72,17 @@ GOOD = P(0x10000)  # never dereferenced: every case below fails before a launch
     ("kq_mxfp4_gemm_wide", (P(0x10008), GOOD, GOOD, GOOD, 4, 4, 64, GOOD, 4, None), kq.KQ_ERR_ALIGN),
     ("kq_mxfp4_gemm_wide", (GOOD, GOOD, GOOD, P(0x10002), 4, 4, 128, GOOD, 4, None), kq.KQ_ERR_ALIGN),
     ("kq_mxfp4_gemm_wide", (None, None, None, None, 0, 4, 64, None, 4, None), kq.KQ_OK),
+    ("kq_lowrank_project_bf16", (GOOD, 4, 48, 48, GOOD, 32, GOOD, None), kq.KQ_ERR_SHAPE),
+    ("kq_lowrank_project_bf16", (GOOD, 4, 64, 64, GOOD, 48, GOOD, None), kq.KQ_ERR_SHAPE),
+    ("kq_lowrank_project_bf16", (GOOD, 4, 64, 32, GOOD, 32, GOOD, None), kq.KQ_ERR_SHAPE),
+    ("kq_lowrank_project_bf16", (GOOD, 4, 64, 64, None, 32, GOOD, None), kq.KQ_ERR_NULL),
+    ("kq_lowrank_project_bf16", (GOOD, 4, 64, 64, P(0x10008), 32, GOOD, None), kq.KQ_ERR_ALIGN),
+    ("kq_lowrank_project_bf16", (GOOD, 4, 64, 68, GOOD, 32, GOOD, None), kq.KQ_ERR_ALIGN),
+    ("kq_lowrank_project_bf16", (None, 0, 64, 64, None, 32, None, None), kq.KQ_OK),
+    ("kq_dequantize_mxfp4_bf16", (GOOD, GOOD, 4, 48, GOOD, None), kq.KQ_ERR_SHAPE),
+    ("kq_dequantize_mxfp4_bf16", (None, GOOD, 4, 64, GOOD, None), kq.KQ_ERR_NULL),
+    ("kq_dequantize_mxfp4_bf16", (GOOD, GOOD, 4, 64, P(0x10008), None), kq.KQ_ERR_ALIGN),
+    ("kq_dequantize_mxfp4_bf16", (None, None, 0, 64, None, None), kq.KQ_OK),
     ("kq_pack_mxfp4_scales", (GOOD, 4, 128, GOOD, None), kq.KQ_ERR_SHAPE),
     ("kq_pack_mxfp4_scales", (GOOD, -1, 256, GOOD, None), kq.KQ_ERR_SHAPE),
     ("kq_pack_mxfp4_scales", (None, 4, 256, GOOD, None), kq.KQ_ERR_NULL),

@@ -73,6 +73,38 @@ def test_lowrank_project(torch_dev, kq, orc, m, d, r):
     assert (np.abs(Z.cpu().numpy() - ref) <= bound).all()
 
 
+@pytest.mark.parametrize("rows,k,seed", [(1, 32, 1), (160, 3072, 2), (37, 96, 3)])
+def test_dequantize_bf16_is_exact(torch_dev, kq, orc, rows, k, seed):
+    """Every MXFP4 value has at most two significant bits: its bf16 is the oracle's
+    fp64 value exactly, down to bf16 subnormals (scale bytes 1 .. 250)."""
+    torch = torch_dev
+    case("dequantize bf16 %dx%d" % (rows, k))
+    rng = np.random.default_rng(seed)
+    c = rng.integers(0, 256, (rows, k // 2), dtype=np.uint8)
+    sc = rng.integers(1, 251, (rows, k // 32), dtype=np.uint8)
+    out = kq.dequantize_mxfp4_bf16(torch.from_numpy(c).cuda(), torch.from_numpy(sc).cuda())
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, orc.dequantize(c, sc, k))
+
+
+@pytest.mark.parametrize("m,d,r", [(100, 96, 32), (300, 3072, 128), (64, 512, 160), (18432, 3072, 128)])
+def test_lowrank_project_bf16_matches(torch_dev, kq, orc, m, d, r):
+    """R decoded once to bf16, then the projection without in-kernel decoding: the same
+    R values, k order and matrix instructions, so Z is bit-identical."""
+    torch = torch_dev
+    case("project bf16 %dx%d r=%d" % (m, d, r))
+    X = synth.random_bf16_matrix(m, d, seed=d + r + 7)
+    R = np.random.default_rng(r + 7).standard_normal((r, d)) / np.sqrt(d)
+    cr, sr = quantize_host(orc, R)
+    dcr, dsr = torch.from_numpy(cr).cuda(), torch.from_numpy(sr).cuda()
+    dX = dev_bf16(torch, X)
+    Z = kq.lowrank_project(dX, dcr, dsr)
+    Z16 = kq.lowrank_project_bf16(dX, kq.dequantize_mxfp4_bf16(dcr, dsr))
+    torch.cuda.synchronize()
+    assert torch.equal(Z, Z16)
+
+
 @pytest.mark.parametrize("m,n,k,r", [(130, 70, 96, 32), (256, 256, 512, 128), (200, 130, 256, 160)])
 def test_gemm_lowrank_epilogue(torch_dev, kq, orc, m, n, k, r):
     torch = torch_dev
