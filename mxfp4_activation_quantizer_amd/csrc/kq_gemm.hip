@@ -213,6 +213,123 @@ __global__ __launch_bounds__(kThreads) void lowrank_project_kernel(const uint16_
     }
 }
 
+// Z = X R16^T with R already in bf16 [r][d]: the same tiling and matrix
+// instructions as lowrank_project_kernel (bit-identical Z), with the work split
+// by wave. Waves 0-3 stream X only, kProjAhead steps ahead in registers, so
+// their memory waits are for their own X loads alone; wave 4 moves each step's
+// 128 x 128 slice of R (L2-resident) straight into LDS and waits for it before
+// the step's barrier. LDS holds two slices of 32 KB, columns of 256 bytes with
+// their 16-byte chunks permuted (chunk q of column c at slot q ^ (c % 16)), so
+// the 16 columns a matrix read touches fall in distinct banks and one
+// direct-to-LDS load (4 columns, 1 KB) stays contiguous.
+__device__ __forceinline__ void proj_dma16(__amdgpu_buffer_rsrc_t d, uint32_t lds, uint32_t voff) {
+    uint32_t keep;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(keep)
+        : "s"(lds), "v"(voff), "s"(d)
+        : "memory");
+}
+
+__global__ __launch_bounds__(320) void lowrank_project_r16_kernel(const uint16_t *__restrict__ X, ProjGeom g,
+                                                                  const uint16_t *__restrict__ r16,
+                                                                  float *__restrict__ Z) {
+    __shared__ __attribute__((aligned(16))) uint8_t rl[2][128 * 256];
+    const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int64_t tm = blockIdx.x / g.tiles_r, tr = blockIdx.x % g.tiles_r;
+    const int64_t col0 = tr * 128;
+    const int64_t steps = (g.d + 127) / 128;
+    // a step past d loads zeros (X and R): its products add exact zeros
+    const int64_t steps_up = (steps + kProjAhead - 1) / kProjAhead * kProjAhead;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)&rl[0][0];
+
+    if (wave == 4) {
+        // producer: 32 loads of 1 KB per step; load j covers columns 4 j .. 4 j + 3
+        const int64_t rows_r = g.r - col0 < 128 ? g.r - col0 : 128;
+        const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(r16 + col0 * g.d), (short)0, (int)(rows_r * g.d * 2), 0x00020000);
+        const int p = lane & 15;
+        auto issue = [&](int64_t st) {
+            const uint32_t buf = lds0 + (uint32_t)((st & 1) * 128 * 256);
+#pragma unroll 8
+            for (int j = 0; j < 32; ++j) {
+                const int c = 4 * j + (lane >> 4);
+                const int q = p ^ (c & 15);
+                const int64_t k = st * 128 + 8 * q;
+                const uint32_t o = k < g.d ? (uint32_t)((c * g.d + k) * 2) : 0x80000000u;
+                proj_dma16(rh, buf + 1024 * j, o);
+            }
+        };
+        issue(0);
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        for (int64_t st = 0; st < steps_up; ++st) {
+            // the slot of step st + 1 held step st - 1, read before the last barrier
+            if (st + 1 < steps_up) issue(st + 1);
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+        return;
+    }
+
+    // consumers: 16 rows each, all 128 columns of the tile (8 MFMA tiles)
+    const int grp = lane >> 4;
+    const int64_t rows_x = g.m - tm * 64 < 64 ? g.m - tm * 64 : 64;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(X + tm * 64 * g.ldx), (short)0, (int)(rows_x * g.ldx * 2), 0x00020000);
+    const uint32_t xoff = (uint32_t)(((wave * 16 + (lane & 15)) * g.ldx + 8 * grp) * 2);
+    auto fetch_x = [&](int64_t k0, uint4 q[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t k = k0 + 32 * u + 8 * grp;
+            const uint32_t xo = k < g.d ? xoff + (uint32_t)((k0 + 32 * u) * 2) : 0x80000000u;
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 2);
+            q[u] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+    };
+    floatx4_t acc[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    uint4 xq[kProjAhead][4];
+#pragma unroll
+    for (int p = 0; p < kProjAhead; ++p) fetch_x((int64_t)p * 128, xq[p]);
+    asm volatile("s_barrier" ::: "memory");
+    const int cl = lane & 15;
+    for (int64_t st0 = 0; st0 < steps_up; st0 += kProjAhead) {
+#pragma unroll
+        for (int p = 0; p < kProjAhead; ++p) {
+            const int64_t st = st0 + p;
+            const uint8_t *buf = rl[st & 1];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bf16x8_t xa = as_bf16x8(xq[p][u]);
+                const int q = 4 * u + grp;
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    const bf16x8_t rb =
+                        *reinterpret_cast<const bf16x8_t *>(buf + (b * 16 + cl) * 256 + 16 * (q ^ cl));
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, rb, acc[b], 0, 0, 0);
+                }
+            }
+            fetch_x((st + kProjAhead) * 128, xq[p]);
+            // done reading this slot (the producer refills it after the barrier)
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+    }
+    const int64_t orow0 = tm * 64 + wave * 16 + grp * 4;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const int64_t col = col0 + b * 16 + cl;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int64_t orow = orow0 + tt;
+            if (orow < g.m && col < g.r) Z[orow * g.r + col] = acc[b][tt];
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // W4A4 GEMM on MXFP4 operands: O[i][j] = sum_k deq(A)[i][k] deq(W)[j][k]
 // (Eq. 2's Q(A T) Q(W T^{-T})^T), fp32 accumulation on
@@ -521,8 +638,8 @@ kq_status kq_lowrank_project_bf16(const uint16_t *X16, int64_t m, int64_t d, int
     if ((int64_t)64 * ldx * 2 >= ((int64_t)1 << 31) || (int64_t)128 * d * 2 >= ((int64_t)1 << 31))
         return KQ_ERR_UNSUPPORTED;
     kq::ProjGeom g{m, d, ldx, r, tiles_r};
-    hipLaunchKernelGGL(kq::lowrank_project_kernel<true>, dim3((unsigned)(tiles_m * tiles_r)), dim3(kq::kThreads),
-                       0, (hipStream_t)stream, X16, g, nullptr, nullptr, R16, Z);
+    hipLaunchKernelGGL(kq::lowrank_project_r16_kernel, dim3((unsigned)(tiles_m * tiles_r)), dim3(320), 0,
+                       (hipStream_t)stream, X16, g, R16, Z);
     return launched();
 }
 
