@@ -294,6 +294,10 @@ def lowrank_layer_timing(torch, kq, A, fac, cw, sw, W, r=128, reps=20):
            "gemm_lowrank_us": med(lambda: kq.mxfp4_gemm_lowrank(ca, sa, cw, sw, Z, cl, sl, out=O)),
            "quantize_us": med(lambda: kq.transform_quantize_mxfp4(A, fac, codes=ca, scales=sa)),
            "gemm_us": med(lambda: kq.mxfp4_gemm(ca, sa, cw, sw, out=O))}
+    # the low-rank epilogue on the packed-scale GEMM (W's scales packed offline, A's per call)
+    psa, psw = kq.pack_mxfp4_scales(sa), kq.pack_mxfp4_scales(sw)
+    res["gemm_lowrank_packed_us"] = med(lambda: kq.mxfp4_gemm_packed_lowrank(ca, psa, cw, psw, Z, cl, sl, out=O))
+    res["pack_a_scales_us"] = med(lambda: kq.pack_mxfp4_scales(sa, out=psa))
     # R decoded to bf16 once per call, then the projection without in-kernel decoding
     r16 = kq.dequantize_mxfp4_bf16(cr, sr)
     res["decode_r_us"] = med(lambda: kq.dequantize_mxfp4_bf16(cr, sr, out=r16))
@@ -301,6 +305,8 @@ def lowrank_layer_timing(torch, kq, A, fac, cw, sw, W, r=128, reps=20):
     res["layer_with_branch_us"] = round(res["quantize_y16_us"] + res["project_us"] + res["gemm_lowrank_us"], 1)
     res["layer_with_branch_r16_us"] = round(res["quantize_y16_us"] + res["decode_r_us"] + res["project_bf16_us"] +
                                             res["gemm_lowrank_us"], 1)
+    res["layer_with_branch_packed_us"] = round(res["quantize_y16_us"] + res["decode_r_us"] + res["project_bf16_us"] +
+                                               res["pack_a_scales_us"] + res["gemm_lowrank_packed_us"], 1)
     res["layer_plain_us"] = round(res["quantize_us"] + res["gemm_us"], 1)
     return res
 

@@ -187,6 +187,21 @@ kq_status kq_mxfp4_gemm_packed(const uint8_t *codes_a, const uint8_t *packed_sca
                                int64_t ldo, kq_stream_t stream);
 
 /*
+ * The layer of Sec. 3.4 Eq. 11 on the packed-scale GEMM: O = deq(A) deq(W)^T +
+ * Z deq(L)^T, the low-rank term added after the product in the same kernel (Z
+ * split into two bf16 terms, exact to 2^-16 relative; deq(L) exact in bf16),
+ * so O is written once.
+ *   codes_a ... k, O, ldo   as kq_mxfp4_gemm_packed (W here is the residual W~ - L R)
+ *   Z                       device, fp32 [m][r], 16-byte aligned (kq_lowrank_project)
+ *   codes_l, scales_l       device, L in MXFP4: [n][r/2] (4-byte aligned), [n][r/32]
+ * r > 0, r % 32 == 0 (KQ_ERR_SHAPE); limits as kq_mxfp4_gemm_packed.
+ */
+kq_status kq_mxfp4_gemm_packed_lowrank(const uint8_t *codes_a, const uint8_t *packed_scales_a,
+                                       const uint8_t *codes_w, const uint8_t *packed_scales_w, int64_t m, int64_t n,
+                                       int64_t k, const float *Z, const uint8_t *codes_l, const uint8_t *scales_l,
+                                       int64_t r, float *O, int64_t ldo, kq_stream_t stream);
+
+/*
  * The W4A4 layer with the activation transform and quantizer inside the
  * product (Sec. 1 Eq. 1-2; Sec. 3.2 Eq. 5 and Sec. 3.5.1 Eq. 12 for T; Sec. 3.1
  * for Q):

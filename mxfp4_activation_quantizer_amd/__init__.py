@@ -33,6 +33,7 @@ EXPORTS = (
     "kq_lowrank_project_bf16",
     "kq_dequantize_mxfp4_bf16",
     "kq_mxfp4_gemm_packed",
+    "kq_mxfp4_gemm_packed_lowrank",
     "kq_transform_quantize_mxfp4_gemm",
     "kq_hadamard_quantize_mxfp4",
     "kq_transform_quantize_mxfp4_y16",
@@ -80,6 +81,7 @@ def lib():
             "kq_lowrank_project_bf16": [p, i64, i64, i64, p, i64, p, p],
             "kq_dequantize_mxfp4_bf16": [p, p, i64, i64, p, p],
             "kq_mxfp4_gemm_packed": [p, p, p, p, i64, i64, i64, p, i64, p],
+            "kq_mxfp4_gemm_packed_lowrank": [p, p, p, p, i64, i64, i64, p, p, p, i64, p, i64, p],
             "kq_transform_quantize_mxfp4_gemm": [p, i64, i64, i64, p, p, p, i64, p, i64, p],
             "kq_hadamard_quantize_mxfp4": [p, i64, i64, i64, i64, p, p, p, p],
             "kq_transform_quantize_mxfp4_y16": [p, i64, i64, i64, p, p, p, p, p],
@@ -432,6 +434,37 @@ def mxfp4_gemm_packed(codes_a, packed_scales_a, codes_w, packed_scales_w, out=No
     _check("kq_mxfp4_gemm_packed",
            lib().kq_mxfp4_gemm_packed(_p(codes_a), _p(packed_scales_a), _p(codes_w), _p(packed_scales_w), m, n, k,
                                       _p(out), out.stride(0), _stream_ptr(stream)))
+    return out
+
+
+def mxfp4_gemm_packed_lowrank(codes_a, packed_scales_a, codes_w, packed_scales_w, Z, codes_l, scales_l, out=None,
+                              stream=None):
+    """O = deq(A) deq(W)^T + Z deq(L)^T on the packed-scale GEMM (k % 256 == 0): Z fp32 [m][r],
+    L in MXFP4 (codes [n][r/2], scales [n][r/32])."""
+    torch = _torch()
+    for t, nm in ((codes_a, "codes_a"), (packed_scales_a, "packed_scales_a"), (codes_w, "codes_w"),
+                  (packed_scales_w, "packed_scales_w"), (codes_l, "codes_l"), (scales_l, "scales_l")):
+        _dev(t, nm, (torch.uint8,))
+        if not t.is_contiguous():
+            raise ValueError(nm + " must be contiguous")
+    _dev(Z, "Z", (torch.float32,))
+    m, kb = codes_a.shape
+    n = codes_w.shape[0]
+    k = kb * 2
+    r = Z.shape[1] if Z.dim() == 2 else -1
+    if tuple(codes_w.shape) != (n, kb) or packed_scales_a.numel() != m * (k // 32) or \
+            packed_scales_w.numel() != n * (k // 32) or tuple(Z.shape) != (m, r) or not Z.is_contiguous() or \
+            tuple(codes_l.shape) != (n, r // 2) or tuple(scales_l.shape) != (n, r // 32):
+        raise ValueError("operand shapes do not match")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=codes_a.device)
+    _dev(out, "out", (torch.float32,))
+    if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
+        raise ValueError("out must be fp32 [m][n] with unit column stride")
+    _check("kq_mxfp4_gemm_packed_lowrank",
+           lib().kq_mxfp4_gemm_packed_lowrank(_p(codes_a), _p(packed_scales_a), _p(codes_w), _p(packed_scales_w), m,
+                                              n, k, _p(Z), _p(codes_l), _p(scales_l), r, _p(out), out.stride(0),
+                                              _stream_ptr(stream)))
     return out
 
 

@@ -294,6 +294,37 @@ __device__ __forceinline__ void ksplit_setup(const float *f20, int lane, KSplit 
     }
 }
 
+// 8 E2M1 codes (element 2i in the low nibble of byte i) with one E8M0 scale,
+// decoded exactly to bf16: a level has at most two significant bits and the
+// scale is a power of two, so the fp32 product is exact and its top 16 bits
+// are the bf16 value.
+__device__ __forceinline__ bf16x8_t decode_fp4x8_bf16(uint32_t c8, uint32_t sbyte) {
+    const float scale = ldexpf(1.0f, (int)sbyte - 127);
+    uint16_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t code = (c8 >> (4 * i)) & 15u, n = code & 7u;
+        const float lvl = n < 2 ? 0.5f * (float)n : ldexpf(1.0f + 0.5f * (float)(n & 1), (int)(n >> 1) - 1);
+        const float v = (code & 8u) ? -(lvl * scale) : lvl * scale;
+        h[i] = (uint16_t)(__float_as_uint(v) >> 16);
+    }
+    bf16x8_t out;
+    __builtin_memcpy(&out, h, 16);
+    return out;
+}
+
+// fp32 x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi) (x - hi is exact in fp32).
+__device__ __forceinline__ void split_bf16x8(const float x[8], bf16x8_t &hi, bf16x8_t &lo) {
+    uint16_t h[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        h[i] = bf16_rne_bits(x[i]);
+        l[i] = bf16_rne_bits(x[i] - __uint_as_float((uint32_t)h[i] << 16));
+    }
+    __builtin_memcpy(&hi, h, 16);
+    __builtin_memcpy(&lo, l, 16);
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 &q) {
     bf16x8_t v;
     __builtin_memcpy(&v, &q, 16);

@@ -61,6 +61,7 @@ struct Geom {
     int stages;  // k / 256
     int tiles_m, tiles_n, nwg;
     int vec_out;  // O 16-byte aligned and ldo % 4 == 0: 16-byte stores
+    int r;        // rank of the low-rank term (LR kernels)
 };
 
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -103,10 +104,20 @@ struct Frag {
     uint32_t sa[4], sb[4];
 };
 
+typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
+
+// LR: after the product, the low-rank term Z deq(L)^T of Sec. 3.4 Eq. 11 is
+// added into the same accumulators (Z fp32 [m][r] split as hi + lo bf16, exact
+// to 2^-16 relative; deq(L) exact in bf16), 64 of r at a time through LDS, on
+// v_mfma_f32_32x32x16_bf16 with the same swapped operands and 32 x 32 layout.
+template <bool LR>
 __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__restrict__ ca,
                                                            const uint8_t *__restrict__ psa,
                                                            const uint8_t *__restrict__ cw,
                                                            const uint8_t *__restrict__ psw, Geom g,
+                                                           const float *__restrict__ Z,
+                                                           const uint8_t *__restrict__ cl,
+                                                           const uint8_t *__restrict__ sl,
                                                            float *__restrict__ O) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
     const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -253,6 +264,64 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
     }
     }
 
+    if (LR) {
+        // LDS after the product: Z hi [256][64] bf16, Z lo likewise, deq(L) [256][64]
+        // bf16, rows of 128 bytes with the 16-byte chunks permuted as the codes are
+        uint8_t *zh = smem, *zl = smem + 32768, *ll = smem + 65536;
+        const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(Z + m0 * g.r), (short)0, (int)(rows_a * g.r * 4), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rcl = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(cl + n0 * (g.r / 2)), (short)0, (int)(rows_w * (g.r / 2)), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rsl = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(sl + n0 * (g.r / 32)), (short)0, (int)(rows_w * (g.r / 32)), 0x00020000);
+        const int sw_t = swz8(t & 15);
+        for (int r0 = 0; r0 < g.r; r0 += 64) {
+            // every wave is done with the previous contents of LDS
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            // thread t stages row t of Z (64 fp32) and row t of L (64 codes, 2 scales);
+            // columns past r read as zero
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int kc = r0 + 8 * c;
+                const uint32_t zo = kc < g.r ? (uint32_t)((t * g.r + kc) * 4) : 0x80000000u;
+                const u32x4_t z0 = __builtin_amdgcn_raw_buffer_load_b128(rz, zo, 0, 0);
+                const u32x4_t z1 = __builtin_amdgcn_raw_buffer_load_b128(rz, zo + 16u, 0, 0);
+                const float x[8] = {__uint_as_float(z0[0]), __uint_as_float(z0[1]), __uint_as_float(z0[2]),
+                                    __uint_as_float(z0[3]), __uint_as_float(z1[0]), __uint_as_float(z1[1]),
+                                    __uint_as_float(z1[2]), __uint_as_float(z1[3])};
+                bf16x8_t h, l;
+                split_bf16x8(x, h, l);
+                const int slot = 16 * (c ^ sw_t);
+                *reinterpret_cast<bf16x8_t *>(zh + t * 128 + slot) = h;
+                *reinterpret_cast<bf16x8_t *>(zl + t * 128 + slot) = l;
+                const uint32_t co = kc < g.r ? (uint32_t)(t * (g.r / 2) + kc / 2) : 0x80000000u;
+                const uint32_t so = kc < g.r ? (uint32_t)(t * (g.r / 32) + kc / 32) : 0x80000000u;
+                const uint32_t c8 = __builtin_amdgcn_raw_buffer_load_b32(rcl, co, 0, 0);
+                const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b8(rsl, so, 0, 0);
+                *reinterpret_cast<bf16x8_t *>(ll + t * 128 + slot) = decode_fp4x8_bf16(c8, sb);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int off = 16 * ((2 * kk + hi) ^ swz8(r & 15));
+                bf16x8v_t lf[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    lf[b] = *reinterpret_cast<const bf16x8v_t *>(ll + (wn + 32 * b + r) * 128 + off);
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const bf16x8v_t hf = *reinterpret_cast<const bf16x8v_t *>(zh + (wm + 32 * a + r) * 128 + off);
+                    const bf16x8v_t lo = *reinterpret_cast<const bf16x8v_t *>(zl + (wm + 32 * a + r) * 128 + off);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[b], hf, acc[a][b], 0, 0, 0);
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[b], lo, acc[a][b], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+
     // lane (r, hi) holds O row wm + 32 a + r, columns wn + 32 b + 8 q + 4 hi + 0..3;
     // rows past m are past the record count and dropped, columns checked
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
@@ -342,8 +411,43 @@ kq_status kq_mxfp4_gemm_packed(const uint8_t *codes_a, const uint8_t *packed_sca
     g.tiles_n = (int)tiles_n;
     g.nwg = (int)(tiles_m * tiles_n);
     g.vec_out = aligned(O, 16) && ldo % 4 == 0;
-    hipLaunchKernelGGL(kq::g256::gemm256_kernel, dim3((unsigned)g.nwg), dim3(kq::g256::kThreads), 0,
-                       (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, O);
+    g.r = 0;
+    hipLaunchKernelGGL(kq::g256::gemm256_kernel<false>, dim3((unsigned)g.nwg), dim3(kq::g256::kThreads), 0,
+                       (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, nullptr, nullptr,
+                       nullptr, O);
+    return launched();
+}
+
+kq_status kq_mxfp4_gemm_packed_lowrank(const uint8_t *codes_a, const uint8_t *packed_scales_a,
+                                       const uint8_t *codes_w, const uint8_t *packed_scales_w, int64_t m, int64_t n,
+                                       int64_t k, const float *Z, const uint8_t *codes_l, const uint8_t *scales_l,
+                                       int64_t r, float *O, int64_t ldo, kq_stream_t stream) {
+    if (m < 0 || n < 0 || k < 0 || k % 256 != 0 || ldo < n || r <= 0 || r % 32 != 0) return KQ_ERR_SHAPE;
+    if (m == 0 || n == 0) return KQ_OK;
+    if (!O || !Z || !codes_l || !scales_l || (k > 0 && (!codes_a || !packed_scales_a || !codes_w || !packed_scales_w)))
+        return KQ_ERR_NULL;
+    if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || !aligned(packed_scales_a, 16) ||
+        !aligned(packed_scales_w, 16) || !aligned(O, 4) || !aligned(Z, 16) || !aligned(codes_l, 4))
+        return KQ_ERR_ALIGN;
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
+    if ((int64_t)256 * (k / 2) >= lim || m * (k / 32) >= lim || n * (k / 32) >= lim ||
+        ((int64_t)255 * ldo + n) * 4 >= lim || tiles_m * tiles_n >= lim || (int64_t)256 * r * 4 + 32 >= lim)
+        return KQ_ERR_UNSUPPORTED;
+    kq::g256::Geom g;
+    g.m = m;
+    g.n = n;
+    g.ldo = ldo;
+    g.kbytes = (int)(k / 2);
+    g.stages = (int)(k / 256);
+    g.tiles_m = (int)tiles_m;
+    g.tiles_n = (int)tiles_n;
+    g.nwg = (int)(tiles_m * tiles_n);
+    g.vec_out = aligned(O, 16) && ldo % 4 == 0;
+    g.r = (int)r;
+    hipLaunchKernelGGL(kq::g256::gemm256_kernel<true>, dim3((unsigned)g.nwg), dim3(kq::g256::kThreads), 0,
+                       (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, Z, codes_l,
+                       scales_l, O);
     return launched();
 }
 

@@ -130,6 +130,29 @@ def test_packed_gemm_padded_output_and_guard(torch_dev, kq, orc, ldo, off):
     assert np.all(np.abs(mat[:, :n].astype(np.float64) - ref) <= bound(orc, ca, sa, cw, sw, k))
 
 
+@pytest.mark.parametrize("m,n,k,r", [(130, 70, 256, 32), (256, 256, 512, 128), (300, 520, 768, 160)])
+def test_packed_gemm_lowrank_matches_oracle(torch_dev, kq, orc, m, n, k, r):
+    """Eq. 11 with the low-rank term in the packed GEMM's epilogue, against the oracle's
+    dequantized product plus Z deq(L)^T in fp64 (ragged m, n; r not a multiple of 64)."""
+    torch = torch_dev
+    case("packed gemm lowrank %dx%dx%d r=%d" % (m, n, k, r))
+    rng = np.random.default_rng(m + n + k + r)
+    ca, sa, cw, sw = operands(rng, m, n, k)
+    cl = rng.integers(0, 256, (n, r // 2), dtype=np.uint8)
+    sl = rng.integers(120, 128, (n, r // 32), dtype=np.uint8)
+    Z = (rng.standard_normal((m, r)) * 3.0).astype(np.float32)
+    dca, dsa, dcw, dsw = (dev(torch, x) for x in (ca, sa, cw, sw))
+    O = kq.mxfp4_gemm_packed_lowrank(dca, kq.pack_mxfp4_scales(dsa), dcw, kq.pack_mxfp4_scales(dsw), dev(torch, Z),
+                                     dev(torch, cl), dev(torch, sl))
+    torch.cuda.synchronize()
+    Lq = orc.dequantize(cl, sl, r)
+    absz = np.abs(Z.astype(np.float64)) @ np.abs(Lq).T
+    ref = orc.gemm_dequant(ca, sa, cw, sw, k) + Z.astype(np.float64) @ Lq.T
+    # the split of Z is exact to 2^-16 relative; fp32 sums add a few 2^-24 per term
+    b = bound(orc, ca, sa, cw, sw, k) + (2.0 ** -15 + r * 2.0 ** -23) * absz + 2.0 ** -20 * np.abs(ref)
+    assert np.all(np.abs(O.cpu().numpy().astype(np.float64) - ref) <= b)
+
+
 def test_packed_gemm_k0_and_empty(torch_dev, kq):
     torch = torch_dev
     case("packed gemm k=0 and empty")
