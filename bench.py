@@ -408,10 +408,20 @@ def cpu_baseline(ws, seconds):
             done_elems += w.m * w.d
         reps += 1
     gbps = done_elems * BYTES_PER_ELEM / t_used / 1e9
+    # the other two oracle paths on the same step, once each (context beside the fused rate)
+    others = {}
+    for name, fn in (("quantize_only", lambda w: orc.quantize_bf16(w.A)),
+                     ("smoothquant", lambda w: orc.smoothquant_quantize(w.A, w.inv_scale))):
+        t0 = time.perf_counter()
+        n = 0
+        for w in ws:
+            fn(w)
+            n += w.m * w.d
+        others[name + "_Gelem_per_s"] = round(n / (time.perf_counter() - t0) / 1e9, 4)
     return {"value": round(gbps, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "oracle transform+quantize (dense fp64 K, Eq. 12) over the whole FLUX step "
                       "(18432x3072 and 18432x12288), %d pass(es), %.1f s" % (reps, t_used),
-            "Gelem_per_s": round(done_elems / t_used / 1e9, 4)}
+            "Gelem_per_s": round(done_elems / t_used / 1e9, 4), **others}
 
 
 COPY_BYTES = 1 << 30
