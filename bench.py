@@ -499,7 +499,7 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (the quantizer needs no collectives); "
+        print("bench.py: measures one GPU only (the quantizer needs no collectives); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch

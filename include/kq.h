@@ -63,7 +63,7 @@ typedef enum {
     KQ_ERR_SHAPE = 2,       /* negative size, d % 32 != 0, lda < d, or size overflow */
     KQ_ERR_ALIGN = 3,       /* a pointer or leading dimension breaks the stated alignment */
     KQ_ERR_HIP = 4,         /* the HIP runtime rejected the launch */
-    KQ_ERR_UNSUPPORTED = 5  /* argument combination not supported by this build */
+    KQ_ERR_UNSUPPORTED = 5  /* argument combination outside what the kernels handle */
 } kq_status;
 
 /*
