@@ -277,7 +277,7 @@ kq_status kq_lowrank_project(const uint16_t *X16, int64_t m, int64_t d, int64_t 
  * call by kq_dequantize_mxfp4_bf16: the decode is exact, so Z is bit-identical
  * to kq_lowrank_project's), so the product spends no vector ALU time on R.
  *   R16  device, bf16 bits [r][d] contiguous, 16-byte aligned
- * Other arguments and rules as kq_lowrank_project; 64 rows of X16 and 128 rows
+ * Other arguments and rules as kq_lowrank_project; 80 rows of X16 and 128 rows
  * of R16 must each span fewer than 2^31 bytes (KQ_ERR_UNSUPPORTED).
  */
 kq_status kq_lowrank_project_bf16(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint16_t *R16,

@@ -182,15 +182,27 @@ __global__ __launch_bounds__(kThreads) void lowrank_project_kernel(const uint16_
     }
 }
 
-// Z = X R16^T with R already in bf16 [r][d]: the same tiling and matrix
-// instructions as lowrank_project_kernel (bit-identical Z), with the work split
-// by wave. Waves 0-3 stream X only, kProjAhead steps ahead in registers, so
-// their memory waits are for their own X loads alone; wave 4 moves each step's
-// 128 x 128 slice of R (L2-resident) straight into LDS and waits for it before
-// the step's barrier. LDS holds two slices of 32 KB, columns of 256 bytes with
-// their 16-byte chunks permuted (chunk q of column c at slot q ^ (c % 16)), so
-// the 16 columns a matrix read touches fall in distinct banks and one
-// direct-to-LDS load (4 columns, 1 KB) stays contiguous.
+// Z = X R16^T with R already in bf16 [r][d]: per output element the same
+// matrix instructions in the same k order as lowrank_project_kernel
+// (bit-identical Z), with the work split by wave. A workgroup covers 80 rows of
+// X (18432 rows make 231 workgroups, one round on 256 CUs; 64-row tiles left a
+// second round of 32): waves 0-4 own 16 rows each and stream them, kProjAhead
+// steps ahead in registers, so their memory waits are for their own X loads
+// alone; waves 5 and 6 move each step's 128 x 128 slice of R (L2-resident)
+// straight into LDS, 16 loads of 1 KB each, two steps ahead of the one being
+// read. LDS holds three slices of 32 KB, columns of 256 bytes with their 16-byte
+// chunks permuted (chunk q of column c at slot q ^ (c % 16)), so the 16 columns
+// a matrix read touches fall in distinct banks and one direct-to-LDS load (4
+// columns, 1 KB) stays contiguous. Measured on 18432 x 3072, r = 128: 39 us,
+// against 91 us with one producer wave, one step ahead and 64-row tiles; the
+// step time followed how fast R reached LDS, not the X stream or the matrix
+// work.
+constexpr int kProjWaves = 5;                    // consumer waves, 16 rows each
+constexpr int kProjRows = 16 * kProjWaves;       // rows of X per workgroup
+constexpr int kProjProducers = 2;                // waves moving R into LDS
+constexpr int kProjSlots = 3;                    // R slices in LDS
+constexpr int kProjLoads = 32 / kProjProducers;  // 1 KB loads per producer per step
+static_assert(kProjSlots == kProjAhead, "the consumers' slot index is their ring position");
 __device__ __forceinline__ void proj_dma16(__amdgpu_buffer_rsrc_t d, uint32_t lds, uint32_t voff) {
     uint32_t keep;
     asm volatile(
@@ -204,10 +216,9 @@ __device__ __forceinline__ void proj_dma16(__amdgpu_buffer_rsrc_t d, uint32_t ld
         : "memory");
 }
 
-__global__ __launch_bounds__(320) void lowrank_project_r16_kernel(const uint16_t *__restrict__ X, ProjGeom g,
-                                                                  const uint16_t *__restrict__ r16,
-                                                                  float *__restrict__ Z) {
-    __shared__ __attribute__((aligned(16))) uint8_t rl[2][128 * 256];
+__global__ __launch_bounds__(64 * (kProjWaves + kProjProducers)) void lowrank_project_r16_kernel(
+    const uint16_t *__restrict__ X, ProjGeom g, const uint16_t *__restrict__ r16, float *__restrict__ Z) {
+    __shared__ __attribute__((aligned(16))) uint8_t rl[kProjSlots][128 * 256];
     const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t tm = blockIdx.x / g.tiles_r, tr = blockIdx.x % g.tiles_r;
     const int64_t col0 = tr * 128;
@@ -215,17 +226,20 @@ __global__ __launch_bounds__(320) void lowrank_project_r16_kernel(const uint16_t
     // a step past d loads zeros (X and R): its products add exact zeros
     const int64_t steps_up = (steps + kProjAhead - 1) / kProjAhead * kProjAhead;
     const uint32_t lds0 = (uint32_t)(uintptr_t)&rl[0][0];
+    constexpr int kAhead = kProjSlots - 1;  // R steps in flight beyond the one being read
 
-    if (wave == 4) {
-        // producer: 32 loads of 1 KB per step; load j covers columns 4 j .. 4 j + 3
+    if (wave >= kProjWaves) {
+        // producer pi: loads j = kProjLoads pi .. of each step; load j covers columns 4 j .. 4 j + 3
+        const int pi = wave - kProjWaves;
         const int64_t rows_r = g.r - col0 < 128 ? g.r - col0 : 128;
         const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(r16 + col0 * g.d), (short)0, (int)(rows_r * g.d * 2), 0x00020000);
         const int p = lane & 15;
         auto issue = [&](int64_t st) {
-            const uint32_t buf = lds0 + (uint32_t)((st & 1) * 128 * 256);
-#pragma unroll 8
-            for (int j = 0; j < 32; ++j) {
+            const uint32_t buf = lds0 + (uint32_t)((st % kProjSlots) * 128 * 256);
+#pragma unroll
+            for (int jj = 0; jj < kProjLoads; ++jj) {
+                const int j = kProjLoads * pi + jj;
                 const int c = 4 * j + (lane >> 4);
                 const int q = p ^ (c & 15);
                 const int64_t k = st * 128 + 8 * q;
@@ -233,21 +247,29 @@ __global__ __launch_bounds__(320) void lowrank_project_r16_kernel(const uint16_t
                 proj_dma16(rh, buf + 1024 * j, o);
             }
         };
-        issue(0);
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        // wait for the oldest step in flight while the `younger` steps issued after
+        // it (kProjLoads loads each) stay in flight, then the step's barrier
+        auto wait_then_barrier = [&](int64_t younger) {
+            if (younger >= 1) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kProjLoads) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        };
+        static_assert(kAhead == 2, "wait_then_barrier covers at most one younger step");
+        for (int s = 0; s < kAhead; ++s)
+            if (s < steps_up) issue(s);
+        wait_then_barrier(steps_up > 1 ? 1 : 0);
         for (int64_t st = 0; st < steps_up; ++st) {
-            // the slot of step st + 1 held step st - 1, read before the last barrier
-            if (st + 1 < steps_up) issue(st + 1);
-            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+            // the slot of step st + kAhead held step st - 1, read before the last barrier
+            if (st + kAhead < steps_up) issue(st + kAhead);
+            wait_then_barrier((st + kAhead < steps_up ? st + kAhead : steps_up - 1) - (st + 1));
         }
         return;
     }
 
     // consumers: 16 rows each, all 128 columns of the tile (8 MFMA tiles)
     const int grp = lane >> 4;
-    const int64_t rows_x = g.m - tm * 64 < 64 ? g.m - tm * 64 : 64;
+    const int64_t rows_x = g.m - tm * kProjRows < kProjRows ? g.m - tm * kProjRows : kProjRows;
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(X + tm * 64 * g.ldx), (short)0, (int)(rows_x * g.ldx * 2), 0x00020000);
+        const_cast<uint16_t *>(X + tm * kProjRows * g.ldx), (short)0, (int)(rows_x * g.ldx * 2), 0x00020000);
     const uint32_t xoff = (uint32_t)(((wave * 16 + (lane & 15)) * g.ldx + 8 * grp) * 2);
     auto fetch_x = [&](int64_t k0, uint4 q[4]) {
 #pragma unroll
@@ -270,7 +292,7 @@ __global__ __launch_bounds__(320) void lowrank_project_r16_kernel(const uint16_t
 #pragma unroll
         for (int p = 0; p < kProjAhead; ++p) {
             const int64_t st = st0 + p;
-            const uint8_t *buf = rl[st & 1];
+            const uint8_t *buf = rl[p];  // slot st % kProjSlots
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const bf16x8_t xa = as_bf16x8(xq[p][u]);
@@ -287,7 +309,7 @@ __global__ __launch_bounds__(320) void lowrank_project_r16_kernel(const uint16_t
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         }
     }
-    const int64_t orow0 = tm * 64 + wave * 16 + grp * 4;
+    const int64_t orow0 = tm * kProjRows + wave * 16 + grp * 4;
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
         const int64_t col = col0 + b * 16 + cl;
@@ -602,13 +624,13 @@ kq_status kq_lowrank_project_bf16(const uint16_t *X16, int64_t m, int64_t d, int
     if (m == 0 || d == 0) return KQ_OK;
     if (!X16 || !R16 || !Z) return KQ_ERR_NULL;
     if (!aligned(X16, 16) || ldx % 8 != 0 || !aligned(R16, 16) || !aligned(Z, 16)) return KQ_ERR_ALIGN;
-    const int64_t tiles_m = (m + 63) / 64, tiles_r = (r + 127) / 128;
+    const int64_t tiles_m = (m + kq::kProjRows - 1) / kq::kProjRows, tiles_r = (r + 127) / 128;
     if (tiles_m * tiles_r > 0x7FFFFFFF || m > INT64_MAX / 4 / (ldx > r ? ldx : r)) return KQ_ERR_SHAPE;
-    if ((int64_t)64 * ldx * 2 >= ((int64_t)1 << 31) || (int64_t)128 * d * 2 >= ((int64_t)1 << 31))
+    if ((int64_t)kq::kProjRows * ldx * 2 >= ((int64_t)1 << 31) || (int64_t)128 * d * 2 >= ((int64_t)1 << 31))
         return KQ_ERR_UNSUPPORTED;
     kq::ProjGeom g{m, d, ldx, r, tiles_r};
-    hipLaunchKernelGGL(kq::lowrank_project_r16_kernel, dim3((unsigned)(tiles_m * tiles_r)), dim3(320), 0,
-                       (hipStream_t)stream, X16, g, R16, Z);
+    hipLaunchKernelGGL(kq::lowrank_project_r16_kernel, dim3((unsigned)(tiles_m * tiles_r)),
+                       dim3(64 * (kq::kProjWaves + kq::kProjProducers)), 0, (hipStream_t)stream, X16, g, R16, Z);
     return launched();
 }
 

@@ -88,7 +88,8 @@ def test_dequantize_bf16_is_exact(torch_dev, kq, orc, rows, k, seed):
     assert np.array_equal(got, orc.dequantize(c, sc, k))
 
 
-@pytest.mark.parametrize("m,d,r", [(100, 96, 32), (300, 3072, 128), (64, 512, 160), (18432, 3072, 128)])
+@pytest.mark.parametrize("m,d,r", [(100, 96, 32), (300, 3072, 128), (64, 512, 160), (1, 32, 32), (79, 800, 96),
+                                   (81, 1152, 256), (241, 4608, 128), (18432, 3072, 128)])
 def test_lowrank_project_bf16_matches(torch_dev, kq, orc, m, d, r):
     """R decoded once to bf16, then the projection without in-kernel decoding: the same
     R values, k order and matrix instructions, so Z is bit-identical."""
