@@ -274,32 +274,46 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
             const_cast<uint8_t *>(cl + n0 * (g.r / 2)), (short)0, (int)(rows_w * (g.r / 2)), 0x00020000);
         const __amdgpu_buffer_rsrc_t rsl = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t *>(sl + n0 * (g.r / 32)), (short)0, (int)(rows_w * (g.r / 32)), 0x00020000);
-        const int sw_t = swz8(t & 15);
+        // a chunk (64 of r) is staged by 8 passes of 32 rows: lane t & 7 of row
+        // 32 p + t / 8 takes 8 consecutive columns, so 8 lanes read a row's 256
+        // bytes of Z (32 of L's code bytes) together; the next chunk's loads go
+        // out before this chunk's matrix work (a chunk past r reads zeros)
+        u32x4_t zr[8][2];
+        uint32_t lc[8], ls[8];
+        const int cc = t & 7;
+        auto load_chunk = [&](int r0) {
+            const int kc = r0 + 8 * cc;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const int row = 32 * p + (t >> 3);
+                const uint32_t zo = kc < g.r ? (uint32_t)((row * g.r + kc) * 4) : 0x80000000u;
+                zr[p][0] = __builtin_amdgcn_raw_buffer_load_b128(rz, zo, 0, 0);
+                zr[p][1] = __builtin_amdgcn_raw_buffer_load_b128(rz, zo + 16u, 0, 0);
+                const uint32_t co = kc < g.r ? (uint32_t)(row * (g.r / 2) + kc / 2) : 0x80000000u;
+                const uint32_t so = kc < g.r ? (uint32_t)(row * (g.r / 32) + kc / 32) : 0x80000000u;
+                lc[p] = __builtin_amdgcn_raw_buffer_load_b32(rcl, co, 0, 0);
+                ls[p] = __builtin_amdgcn_raw_buffer_load_b8(rsl, so, 0, 0);
+            }
+        };
+        load_chunk(0);
         for (int r0 = 0; r0 < g.r; r0 += 64) {
             // every wave is done with the previous contents of LDS
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            // thread t stages row t of Z (64 fp32) and row t of L (64 codes, 2 scales);
-            // columns past r read as zero
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int kc = r0 + 8 * c;
-                const uint32_t zo = kc < g.r ? (uint32_t)((t * g.r + kc) * 4) : 0x80000000u;
-                const u32x4_t z0 = __builtin_amdgcn_raw_buffer_load_b128(rz, zo, 0, 0);
-                const u32x4_t z1 = __builtin_amdgcn_raw_buffer_load_b128(rz, zo + 16u, 0, 0);
-                const float x[8] = {__uint_as_float(z0[0]), __uint_as_float(z0[1]), __uint_as_float(z0[2]),
-                                    __uint_as_float(z0[3]), __uint_as_float(z1[0]), __uint_as_float(z1[1]),
-                                    __uint_as_float(z1[2]), __uint_as_float(z1[3])};
+            for (int p = 0; p < 8; ++p) {
+                const int row = 32 * p + (t >> 3);
+                const float x[8] = {__uint_as_float(zr[p][0][0]), __uint_as_float(zr[p][0][1]),
+                                    __uint_as_float(zr[p][0][2]), __uint_as_float(zr[p][0][3]),
+                                    __uint_as_float(zr[p][1][0]), __uint_as_float(zr[p][1][1]),
+                                    __uint_as_float(zr[p][1][2]), __uint_as_float(zr[p][1][3])};
                 bf16x8_t h, l;
                 split_bf16x8(x, h, l);
-                const int slot = 16 * (c ^ sw_t);
-                *reinterpret_cast<bf16x8_t *>(zh + t * 128 + slot) = h;
-                *reinterpret_cast<bf16x8_t *>(zl + t * 128 + slot) = l;
-                const uint32_t co = kc < g.r ? (uint32_t)(t * (g.r / 2) + kc / 2) : 0x80000000u;
-                const uint32_t so = kc < g.r ? (uint32_t)(t * (g.r / 32) + kc / 32) : 0x80000000u;
-                const uint32_t c8 = __builtin_amdgcn_raw_buffer_load_b32(rcl, co, 0, 0);
-                const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b8(rsl, so, 0, 0);
-                *reinterpret_cast<bf16x8_t *>(ll + t * 128 + slot) = decode_fp4x8_bf16(c8, sb);
+                const int slot = row * 128 + 16 * (cc ^ swz8(row & 15));
+                *reinterpret_cast<bf16x8_t *>(zh + slot) = h;
+                *reinterpret_cast<bf16x8_t *>(zl + slot) = l;
+                *reinterpret_cast<bf16x8_t *>(ll + slot) = decode_fp4x8_bf16(lc[p], ls[p]);
             }
+            load_chunk(r0 + 64);
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
