@@ -154,8 +154,12 @@ kq_status kq_mxfp4_gemm_wide(const uint8_t *codes_a, const uint8_t *scales_a, co
  * Re-layout of MXFP4 scales for kq_mxfp4_gemm_packed (a format change only,
  * no arithmetic): the E8M0 bytes of Sec. 3.1's blocks, [rows][k/32] as the
  * quantizers write them, become [k/256][rows][8], i.e. the eight scale bytes
- * of one 256-wide k stage of consecutive rows are consecutive.
- *   packed[(s * rows + i) * 8 + j] = scales[i * (k/32) + 8 s + j]
+ * of one 256-wide k stage of consecutive rows are consecutive, even blocks of
+ * the stage first: bytes 0-3 hold blocks 0, 2, 4, 6 and bytes 4-7 blocks 1, 3,
+ * 5, 7 (the product reads the dword of its block parity and selects byte j for
+ * the stage's j-th pair of blocks with the instruction's byte select).
+ *   packed[(s * rows + i) * 8 + 4 p + j] = scales[i * (k/32) + 8 s + 2 j + p]
+ *   (p in 0..1, j in 0..3)
  *   scales   device, [rows][k/32] bytes (no alignment needed)
  *   packed   device, rows * (k/32) bytes, 8-byte aligned; must not overlap scales
  * k % 256 == 0 (KQ_ERR_SHAPE); rows == 0 or k == 0 is a no-op.

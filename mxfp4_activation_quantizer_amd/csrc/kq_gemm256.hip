@@ -17,7 +17,10 @@
 //    issued among the current stage's first 16 matrix instructions;
 //  - scales are read in a GEMM-ready layout (kq_pack_mxfp4_scales): the 8 scale
 //    bytes of one 256-k stage of consecutive rows are consecutive, so a stage's
-//    scales for 256 rows are one 2 KB run instead of 256 scattered lines;
+//    scales for 256 rows are one 2 KB run instead of 256 scattered lines, and
+//    they are ordered even blocks first, so the scale a lane needs at step j
+//    is byte j of the dword of its block parity: the instruction's byte select
+//    picks it, with no per-lane shift;
 //  - tiles are numbered so that each XCD (workgroups are dealt to the eight XCDs
 //    round robin) gets a contiguous run, walked in bands of 4 row tiles, which
 //    keeps the operand rows a run shares in that XCD's L2.
@@ -35,6 +38,8 @@
 // registers 4 q .. 4 q + 3, so it stores 16 contiguous bytes per q.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "kq.h"
 #include "kq_device.hpp"
@@ -168,15 +173,15 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
 
     const int r = lane & 31, hi = lane >> 5;
     const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
-    const int sh = 8 * hi;
     int rdo[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) rdo[j] = r * 128 + 16 * ((2 * j + hi) ^ swz8(r & 15));
 
-    // step j of stage s: 16-byte fragments (k group 2 j + hi) and the scale dword holding it
+    // step j of stage s: 16-byte fragments (k group 2 j + hi) and the scale dword of
+    // the lane's block parity hi (byte j is block 2 j + hi)
     auto read_frags = [&](int s, int j, Frag &F) {
         const uint8_t *st = smem + (s & 1) * kStage;
-        const uint8_t *sc = st + 2 * kCode + 4 * (j >> 1) + 8 * r;
+        const uint8_t *sc = st + 2 * kCode + 4 * hi + 8 * r;
 #pragma unroll
         for (int a = 0; a < 4; ++a) F.sa[a] = *reinterpret_cast<const uint32_t *>(sc + 8 * (wm + 32 * a));
 #pragma unroll
@@ -201,18 +206,23 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-    // the scale byte of group 2 j + hi is byte 2 (j & 1) + hi of the dword
-    auto mma = [&](const Frag &F, int j, int a, int b) {
-        const int shj = sh + 16 * (j & 1);
-        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[b], F.a[a], acc[a][b], 4, 4, 0,
-                                                                    (int)(F.sb[b] >> shj), 0, (int)(F.sa[a] >> shj));
+    // the scale of group 2 j + hi is byte j of the lane's scale dword: the byte
+    // select (op_sel) of the instruction's scale operands, uniform across lanes
+    auto mma = [&](const Frag &F, auto jc, int a, int b) {
+        constexpr int j = decltype(jc)::value;
+        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[b], F.a[a], acc[a][b], 4, 4, j, (int)F.sb[b],
+                                                                    j, (int)F.sa[a]);
     };
-    auto step = [&](const Frag &F, int j) {
+    auto step = [&](const Frag &F, auto jc) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) mma(F, j, a, b);
+            for (int b = 0; b < 4; ++b) mma(F, jc, a, b);
     };
+    using J0 = std::integral_constant<int, 0>;
+    using J1 = std::integral_constant<int, 1>;
+    using J2 = std::integral_constant<int, 2>;
+    using J3 = std::integral_constant<int, 3>;
 
     if (g.stages > 0) {  // k == 0: O = 0
     issue_scl(0);
@@ -233,34 +243,34 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                mma(F0, 0, a, b);
+                mma(F0, J0(), a, b);
                 issue_code(s + 1, 4 * a + b);
                 if (a == 1 && b == 3) issue_scl(s + 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
         read_frags(s, 2, F0);
         __builtin_amdgcn_sched_barrier(0);
-        step(F1, 1);
+        step(F1, J1());
         __builtin_amdgcn_sched_barrier(0);
         read_frags(s, 3, F1);
         __builtin_amdgcn_sched_barrier(0);
-        step(F0, 2);
+        step(F0, J2());
         __builtin_amdgcn_sched_barrier(0);
         wait_loads_and_lds_then_barrier();
         read_frags(s + 1, 0, F0);
         __builtin_amdgcn_sched_barrier(0);
-        step(F1, 3);
+        step(F1, J3());
         __builtin_amdgcn_sched_barrier(0);
     }
     {
         const int s = g.stages - 1;
         read_frags(s, 1, F1);
-        step(F0, 0);
+        step(F0, J0());
         read_frags(s, 2, F0);
-        step(F1, 1);
+        step(F1, J1());
         read_frags(s, 3, F1);
-        step(F0, 2);
-        step(F1, 3);
+        step(F0, J2());
+        step(F1, J3());
     }
     }
 
@@ -363,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
     }
 }
 
-// scales [rows][kblocks] -> [kblocks / 8][rows][8]: one 8-byte run per thread
+// scales [rows][kblocks] -> [kblocks / 8][rows][8], even blocks first: one 8-byte run per thread
 __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t *__restrict__ in, int64_t rows,
                                                           int64_t kblocks, uint8_t *__restrict__ out) {
     const int64_t total = rows * (kblocks / 8);
@@ -372,7 +382,11 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t *__restr
         const int64_t s = i / rows, row = i % rows;
         uint2 v;
         __builtin_memcpy(&v, in + row * kblocks + 8 * s, 8);
-        *reinterpret_cast<uint2 *>(out + 8 * i) = v;
+        // bytes b0..b7 -> b0 b2 b4 b6 | b1 b3 b5 b7
+        uint2 o;
+        o.x = (v.x & 0xFFu) | ((v.x >> 8) & 0xFF00u) | ((v.y << 16) & 0xFF0000u) | ((v.y << 8) & 0xFF000000u);
+        o.y = ((v.x >> 8) & 0xFFu) | ((v.x >> 16) & 0xFF00u) | ((v.y << 8) & 0xFF0000u) | (v.y & 0xFF000000u);
+        *reinterpret_cast<uint2 *>(out + 8 * i) = o;
     }
 }
 

@@ -38,11 +38,14 @@ def dev(torch, x):
 
 
 def packed_reference(scales):
-    """[rows][k/32] -> [k/256][rows][8], written out from the layout's definition."""
+    """[rows][k/32] -> [k/256][rows][8], written out from the layout's definition: within a
+    256-k stage the even blocks 0, 2, 4, 6 first, then the odd blocks 1, 3, 5, 7."""
     rows, kb = scales.shape
     out = np.empty((kb // 8, rows, 8), dtype=np.uint8)
     for s in range(kb // 8):
-        out[s] = scales[:, 8 * s:8 * s + 8]
+        for p in range(2):
+            for j in range(4):
+                out[s, :, 4 * p + j] = scales[:, 8 * s + 2 * j + p]
     return out
 
 
