@@ -106,6 +106,10 @@ __device__ __forceinline__ void wait_loads_and_lds_then_barrier() {
 
 struct Frag {
     i32x8_t a[4], b[4];
+};
+
+// a stage's scale dwords of the lane's rows (the same dword serves all four steps)
+struct Scl {
     uint32_t sa[4], sb[4];
 };
 
@@ -177,15 +181,17 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
 #pragma unroll
     for (int j = 0; j < 4; ++j) rdo[j] = r * 128 + 16 * ((2 * j + hi) ^ swz8(r & 15));
 
-    // step j of stage s: 16-byte fragments (k group 2 j + hi) and the scale dword of
-    // the lane's block parity hi (byte j is block 2 j + hi)
+    // stage s: the scale dword of the lane's block parity hi (byte j is block 2 j + hi)
+    auto read_scl = [&](int s, Scl &S) {
+        const uint8_t *sc = smem + (s & 1) * kStage + 2 * kCode + 4 * hi + 8 * r;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) S.sa[a] = *reinterpret_cast<const uint32_t *>(sc + 8 * (wm + 32 * a));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) S.sb[b] = *reinterpret_cast<const uint32_t *>(sc + kScl + 8 * (wn + 32 * b));
+    };
+    // step j of stage s: 16-byte fragments (k group 2 j + hi)
     auto read_frags = [&](int s, int j, Frag &F) {
         const uint8_t *st = smem + (s & 1) * kStage;
-        const uint8_t *sc = st + 2 * kCode + 4 * hi + 8 * r;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) F.sa[a] = *reinterpret_cast<const uint32_t *>(sc + 8 * (wm + 32 * a));
-#pragma unroll
-        for (int b = 0; b < 4; ++b) F.sb[b] = *reinterpret_cast<const uint32_t *>(sc + kScl + 8 * (wn + 32 * b));
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const uint4 q = *reinterpret_cast<const uint4 *>(st + (wm + 32 * a) * 128 + rdo[j]);
@@ -208,16 +214,16 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
 
     // the scale of group 2 j + hi is byte j of the lane's scale dword: the byte
     // select (op_sel) of the instruction's scale operands, uniform across lanes
-    auto mma = [&](const Frag &F, auto jc, int a, int b) {
+    auto mma = [&](const Frag &F, const Scl &S, auto jc, int a, int b) {
         constexpr int j = decltype(jc)::value;
-        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[b], F.a[a], acc[a][b], 4, 4, j, (int)F.sb[b],
-                                                                    j, (int)F.sa[a]);
+        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[b], F.a[a], acc[a][b], 4, 4, j, (int)S.sb[b],
+                                                                    j, (int)S.sa[a]);
     };
-    auto step = [&](const Frag &F, auto jc) {
+    auto step = [&](const Frag &F, const Scl &S, auto jc) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) mma(F, jc, a, b);
+            for (int b = 0; b < 4; ++b) mma(F, S, jc, a, b);
     };
     using J0 = std::integral_constant<int, 0>;
     using J1 = std::integral_constant<int, 1>;
@@ -230,6 +236,8 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
     for (int i = 0; i < 16; ++i) issue_code(0, i);
     wait_loads_and_lds_then_barrier();
     Frag F0, F1;
+    Scl S, Sn;
+    read_scl(0, S);
     read_frags(0, 0, F0);
 
     // Stage s (s + 1 < stages): the buffer of stage s + 1 held stage s - 1, whose
@@ -243,34 +251,36 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                mma(F0, J0(), a, b);
+                mma(F0, S, J0(), a, b);
                 issue_code(s + 1, 4 * a + b);
                 if (a == 1 && b == 3) issue_scl(s + 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
         read_frags(s, 2, F0);
         __builtin_amdgcn_sched_barrier(0);
-        step(F1, J1());
+        step(F1, S, J1());
         __builtin_amdgcn_sched_barrier(0);
         read_frags(s, 3, F1);
         __builtin_amdgcn_sched_barrier(0);
-        step(F0, J2());
+        step(F0, S, J2());
         __builtin_amdgcn_sched_barrier(0);
         wait_loads_and_lds_then_barrier();
+        read_scl(s + 1, Sn);
         read_frags(s + 1, 0, F0);
         __builtin_amdgcn_sched_barrier(0);
-        step(F1, J3());
+        step(F1, S, J3());
         __builtin_amdgcn_sched_barrier(0);
+        S = Sn;
     }
     {
         const int s = g.stages - 1;
         read_frags(s, 1, F1);
-        step(F0, J0());
+        step(F0, S, J0());
         read_frags(s, 2, F0);
-        step(F1, J1());
+        step(F1, S, J1());
         read_frags(s, 3, F1);
-        step(F0, J2());
-        step(F1, J3());
+        step(F0, S, J2());
+        step(F1, S, J3());
     }
     }
 
