@@ -106,6 +106,25 @@ def test_lowrank_project_bf16_matches(torch_dev, kq, orc, m, d, r):
     assert torch.equal(Z, Z16)
 
 
+def test_lowrank_project_bf16_strided_x(torch_dev, kq, orc):
+    """X16 a row-strided view (ldx = d + 64) over several 80-row tiles and a ragged last
+    one: the same Z, bit for bit, as the in-workgroup decode path on the same view."""
+    torch = torch_dev
+    m, d, r, pad = 333, 1152, 96, 64
+    case("project bf16 strided X %dx%d ldx=%d r=%d" % (m, d, d + pad, r))
+    Xw = synth.random_bf16_matrix(m, d + pad, seed=21)
+    R = np.random.default_rng(22).standard_normal((r, d)) / np.sqrt(d)
+    cr, sr = quantize_host(orc, R)
+    dcr, dsr = torch.from_numpy(cr).cuda(), torch.from_numpy(sr).cuda()
+    dX = dev_bf16(torch, Xw)[:, :d]
+    assert dX.stride(0) == d + pad
+    Z = kq.lowrank_project(dX, dcr, dsr)
+    Z16 = kq.lowrank_project_bf16(dX, kq.dequantize_mxfp4_bf16(dcr, dsr))
+    Zc = kq.lowrank_project_bf16(dX.contiguous(), kq.dequantize_mxfp4_bf16(dcr, dsr))
+    torch.cuda.synchronize()
+    assert torch.equal(Z, Z16) and torch.equal(Z16, Zc)
+
+
 @pytest.mark.parametrize("m,n,k,r", [(130, 70, 96, 32), (256, 256, 512, 128), (200, 130, 256, 160)])
 def test_gemm_lowrank_epilogue(torch_dev, kq, orc, m, n, k, r):
     torch = torch_dev
