@@ -317,8 +317,10 @@ kq_status kq_mxfp4_gemm_lowrank(const uint8_t *codes_a, const uint8_t *scales_a,
  * fp32 GEMM: D = alpha op(A) op(B) + beta C, row-major operands; op(A) is m x k
  * (A is m x k, or k x m when transa), op(B) is k x n (B is k x n, or n x k when
  * transb). C may be NULL when beta == 0; C and D use the row strides ldc, ldd.
- * fp32 fused multiply-adds in ascending k. Used by the calibration below and
- * usable on its own.
+ * fp32 products accumulated in fp32 on the fp32 matrix instruction, two k at a
+ * time in ascending k (not bit-identical to a scalar fused multiply-add chain;
+ * within the usual fp32 dot-product error bound). Used by the calibration below
+ * and usable on its own.
  */
 kq_status kq_gemm_f32(int transa, int transb, int64_t m, int64_t n, int64_t k, float alpha, const float *A,
                       int64_t lda, const float *B, int64_t ldb, float beta, const float *C, int64_t ldc, float *D,

@@ -134,74 +134,138 @@ __global__ __launch_bounds__(256) void widen_kernel(const uint16_t *__restrict__
 }
 
 // --- fp32 GEMM: D = alpha op(A) op(B) + beta C ----------------------------------
-// 64 x 64 output tile per workgroup, k in steps of 16 through LDS (k-major
-// tiles, so the inner loop reads 4 consecutive m and 4 consecutive n), 4 x 4
-// outputs per thread. op(A) is m x k (A row-major m x k, or k x m when TA);
-// op(B) is k x n (B row-major k x n, or n x k when TB). Optional: per-workgroup
-// sum of squares of D (double).
-template <bool TA, bool TB>
+// On the fp32 matrix instruction v_mfma_f32_32x32x2_f32 (gfx950 runs it at the fp32
+// peak without packed vector math). 128 x 128 output tile per workgroup of four
+// waves, each wave 64 x 64 = 2 x 2 instruction tiles; k in steps of 16 through LDS,
+// double-buffered, both operands staged k-major (As[k][m], Bs[k][n]) so a matrix
+// operand (lane l: row or column l % 32 at k row 2 kk + l / 32) is 32 consecutive
+// floats; rows are padded to 160 floats, which puts the two k rows a read touches
+// in opposite bank halves. The next step's elements go to registers before the
+// current step's matrix work and to LDS after it. op(A) is m x k (A row-major m x k,
+// or k x m when TA); op(B) is k x n (B row-major k x n, or n x k when TB). Elements
+// past m, n or k read as zero. Optional: per-workgroup sum of squares of D (double).
+constexpr int kGT = 128;      // output tile
+constexpr int kGK = 16;       // k per step
+constexpr int kGP = kGT + 32; // LDS row pitch (floats)
+
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+template <bool TA, bool TB, bool VEC>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(int64_t m, int64_t n, int64_t k, float alpha,
                                                        const float *__restrict__ A, int64_t lda,
                                                        const float *__restrict__ B, int64_t ldb, float beta,
                                                        const float *__restrict__ C, int64_t ldc,
                                                        float *__restrict__ D, int64_t ldd,
                                                        double *__restrict__ sumsq) {
-    __shared__ float As[16][68];
-    __shared__ float Bs[16][68];
-    const int t = threadIdx.x;
-    const int64_t tiles_n = (n + 63) / 64;
-    const int64_t m0 = (blockIdx.x / tiles_n) * 64, n0 = (blockIdx.x % tiles_n) * 64;
-    const int tm = (t >> 4) * 4, tn = (t & 15) * 4;
-    float acc[4][4] = {};
-    for (int64_t k0 = 0; k0 < k; k0 += 16) {
-        // 64 x 16 of op(A) and 16 x 64 of op(B), 4 elements per thread each
+    __shared__ __attribute__((aligned(16))) float As[2][kGK][kGP];
+    __shared__ __attribute__((aligned(16))) float Bs[2][kGK][kGP];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int64_t tiles_n = (n + kGT - 1) / kGT;
+    const int64_t m0 = (blockIdx.x / tiles_n) * kGT, n0 = (blockIdx.x % tiles_n) * kGT;
+    // staging of one step, 8 elements of each operand per thread:
+    //   row-major m x k side: row t % 128, k 8 (t / 128) .. + 7 (a wave writes 64
+    //   consecutive rows of one k row of the tile: no bank conflicts);
+    //   k-major side: k row t / 16, columns 8 (t % 16) .. + 7
+    float ra[8], rb[8];
+    // 8 consecutive elements of one row of a row-major matrix, as two 16-byte loads when
+    // VEC (16-byte aligned matrix, row stride a multiple of 4) and all 8 are in range
+    auto run8 = [&](const float *M, int64_t ld, int64_t row, int64_t rows, int64_t c0, int64_t cols, float v[8]) {
+        if (VEC && row < rows && c0 + 7 < cols) {
+            const float4 x = *reinterpret_cast<const float4 *>(M + row * ld + c0);
+            const float4 y = *reinterpret_cast<const float4 *>(M + row * ld + c0 + 4);
+            v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+            v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int idx = t * 4 + e;  // 0..1023
-            int mm, kk;
-            if (TA) { kk = idx >> 6; mm = idx & 63; } else { mm = idx >> 4; kk = idx & 15; }
-            const int64_t gm = m0 + mm, gk = k0 + kk;
-            float v = 0.0f;
-            if (gm < m && gk < k) v = TA ? A[gk * lda + gm] : A[gm * lda + gk];
-            As[kk][mm] = v;
-            int nn, kb;
-            if (TB) { nn = idx >> 4; kb = idx & 15; } else { kb = idx >> 6; nn = idx & 63; }
-            const int64_t gn = n0 + nn, gkb = k0 + kb;
-            float w = 0.0f;
-            if (gn < n && gkb < k) w = TB ? B[gn * ldb + gkb] : B[gkb * ldb + gn];
-            Bs[kb][nn] = w;
+            for (int e = 0; e < 8; ++e) v[e] = (row < rows && c0 + e < cols) ? M[row * ld + c0 + e] : 0.0f;
         }
-        __syncthreads();
+    };
+    auto fetch = [&](int64_t k0) {
+        if (VEC) {
+            if (!TA) run8(A, lda, m0 + (t & 127), m, k0 + 8 * (t >> 7), k, ra);
+            else run8(A, lda, k0 + (t >> 4), k, m0 + 8 * (t & 15), m, ra);
+            if (!TB) run8(B, ldb, k0 + (t >> 4), k, n0 + 8 * (t & 15), n, rb);
+            else run8(B, ldb, n0 + (t & 127), n, k0 + 8 * (t >> 7), k, rb);
+            return;
+        }
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            float a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = As[kk][tm + i];
-                b[i] = Bs[kk][tn + i];
+        for (int e = 0; e < 8; ++e) {
+            if (!TA) {
+                const int64_t gm = m0 + (t & 127), gk = k0 + 8 * (t >> 7) + e;
+                ra[e] = (gm < m && gk < k) ? A[gm * lda + gk] : 0.0f;
+            } else {
+                const int64_t gk = k0 + (t >> 4), gm = m0 + 8 * (t & 15) + e;
+                ra[e] = (gm < m && gk < k) ? A[gk * lda + gm] : 0.0f;
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) acc[i][jj] = fmaf(a[i], b[jj], acc[i][jj]);
+            if (!TB) {
+                const int64_t gk = k0 + (t >> 4), gn = n0 + 8 * (t & 15) + e;
+                rb[e] = (gn < n && gk < k) ? B[gk * ldb + gn] : 0.0f;
+            } else {
+                const int64_t gn = n0 + (t & 127), gk = k0 + 8 * (t >> 7) + e;
+                rb[e] = (gn < n && gk < k) ? B[gn * ldb + gk] : 0.0f;
+            }
         }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (!TA) As[buf][8 * (t >> 7) + e][t & 127] = ra[e];
+            else As[buf][t >> 4][8 * (t & 15) + e] = ra[e];
+            if (!TB) Bs[buf][t >> 4][8 * (t & 15) + e] = rb[e];
+            else Bs[buf][8 * (t >> 7) + e][t & 127] = rb[e];
+        }
+    };
+    const int r = lane & 31, hi = lane >> 5;
+    const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+    floatx16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    const int64_t steps = (k + kGK - 1) / kGK;
+    if (steps > 0) {
+        fetch(0);
+        stash(0);
+    }
+    __syncthreads();
+    for (int64_t st = 0; st < steps; ++st) {
+        const int cur = (int)(st & 1);
+        if (st + 1 < steps) fetch((st + 1) * kGK);
+#pragma unroll
+        for (int kk = 0; kk < kGK / 2; ++kk) {
+            float a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) a[i] = As[cur][2 * kk + hi][wm + 32 * i + r];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) b[j] = Bs[cur][2 * kk + hi][wn + 32 * j + r];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        // the other buffer was last read in step st - 1, before the previous barrier
+        if (st + 1 < steps) stash(cur ^ 1);
         __syncthreads();
     }
+    // lane (r, hi) holds D[wm + 32 i + 8 (q / 4) + 4 hi + q % 4][wn + 32 j + r] in acc[i][j][q]
     double sq = 0.0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t gm = m0 + tm + i;
-        if (gm >= m) continue;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int64_t gn = n0 + tn + jj;
-            if (gn >= n) continue;
-            float v = alpha * acc[i][jj];
-            if (beta != 0.0f) v = fmaf(beta, C[gm * ldc + gn], v);
-            D[gm * ldd + gn] = v;
-            sq += (double)v * v;
+        for (int j = 0; j < 2; ++j) {
+            const int64_t gn = n0 + wn + 32 * j + r;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int64_t gm = m0 + wm + 32 * i + 8 * (q >> 2) + 4 * hi + (q & 3);
+                if (gm >= m || gn >= n) continue;
+                float v = alpha * acc[i][j][q];
+                if (beta != 0.0f) v = fmaf(beta, C[gm * ldc + gn], v);
+                D[gm * ldd + gn] = v;
+                sq += (double)v * v;
+            }
         }
-    }
     if (sumsq) {
         const double s = block_sum(sq);
         if (t == 0) sumsq[blockIdx.x] = s;
@@ -425,7 +489,7 @@ CalibLayout calib_layout(int64_t M, int64_t d, int64_t o) {
     const int64_t nblk = d / 32;
     L.qdq_wg_A = qdq_grid(M, d);
     L.qdq_wg_W = qdq_grid(o, d);
-    L.gemm_wg_E = ((M + 63) / 64) * ((o + 63) / 64);
+    L.gemm_wg_E = ((M + kq::kGT - 1) / kq::kGT) * ((o + kq::kGT - 1) / kq::kGT);
     L.nchA = (M + kChunkRows - 1) / kChunkRows;
     L.nchW = (o + kChunkRows - 1) / kChunkRows;
     int64_t off = 0;
@@ -465,10 +529,15 @@ template <bool TA, bool TB>
 kq_status launch_gemm(int64_t m, int64_t n, int64_t k, float alpha, const float *A, int64_t lda, const float *B,
                       int64_t ldb, float beta, const float *C, int64_t ldc, float *D, int64_t ldd, double *sumsq,
                       hipStream_t s) {
-    const int64_t wg = ((m + 63) / 64) * ((n + 63) / 64);
+    const int64_t wg = ((m + kq::kGT - 1) / kq::kGT) * ((n + kq::kGT - 1) / kq::kGT);
     if (wg > 0x7FFFFFFF) return KQ_ERR_SHAPE;
-    hipLaunchKernelGGL((kq::gemm_f32_kernel<TA, TB>), dim3((unsigned)wg), dim3(256), 0, s, m, n, k, alpha, A, lda, B,
-                       ldb, beta, C, ldc, D, ldd, sumsq);
+    const bool vec = aligned(A, 16) && aligned(B, 16) && lda % 4 == 0 && ldb % 4 == 0;
+    if (vec)
+        hipLaunchKernelGGL((kq::gemm_f32_kernel<TA, TB, true>), dim3((unsigned)wg), dim3(256), 0, s, m, n, k, alpha, A,
+                           lda, B, ldb, beta, C, ldc, D, ldd, sumsq);
+    else
+        hipLaunchKernelGGL((kq::gemm_f32_kernel<TA, TB, false>), dim3((unsigned)wg), dim3(256), 0, s, m, n, k, alpha,
+                           A, lda, B, ldb, beta, C, ldc, D, ldd, sumsq);
     return launched();
 }
 

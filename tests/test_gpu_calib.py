@@ -38,7 +38,7 @@ def kq():
 
 
 @pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)])
-@pytest.mark.parametrize("m,n,k", [(70, 45, 37), (128, 64, 256), (1, 1, 1)])
+@pytest.mark.parametrize("m,n,k", [(70, 45, 37), (128, 64, 256), (1, 1, 1), (200, 136, 100), (257, 129, 64)])
 def test_gemm_f32(torch_dev, kq, ta, tb, m, n, k):
     torch = torch_dev
     case("gemm ta=%d tb=%d %dx%dx%d" % (ta, tb, m, n, k))
