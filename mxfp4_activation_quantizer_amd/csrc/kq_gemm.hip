@@ -43,13 +43,10 @@ struct ProjGeom {
 constexpr int kProjRow = 128 * 2 + 16;  // bytes per staged R column: 128 bf16 + 16 of padding
 constexpr int kProjAhead = 3;            // steps of X in flight per wave
 
-// R16: R arrives already in bf16 ([r][d], e.g. from kq_dequantize_mxfp4_bf16) and
-// is copied into LDS as it is; otherwise the workgroup decodes MXFP4 R itself.
-template <bool R16>
+// The workgroup decodes each step's slice of MXFP4 R into LDS itself.
 __global__ __launch_bounds__(kThreads) void lowrank_project_kernel(const uint16_t *__restrict__ X, ProjGeom g,
                                                                    const uint8_t *__restrict__ cr,
                                                                    const uint8_t *__restrict__ sr,
-                                                                   const uint16_t *__restrict__ r16,
                                                                    float *__restrict__ Z) {
     __shared__ __attribute__((aligned(16))) uint8_t rl[2][128 * kProjRow];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -62,33 +59,17 @@ __global__ __launch_bounds__(kThreads) void lowrank_project_kernel(const uint16_
     struct RRegs {
         uint4 c[2];
         uint32_t s[2];
-        uint4 h[8];  // R16: 64 bf16 of column dc
     };
     // Loads go through per-tile buffer descriptors whose record counts end at the
     // last valid row (rows past m or r read zero), with no branches around them,
     // so the compiler's wait counts stay exact; a load past d gets an offset
     // beyond the record count and reads zero too.
     const int64_t rows_r = g.r - col0 < 128 ? g.r - col0 : 128;
-    const __amdgpu_buffer_rsrc_t rc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(R16 ? nullptr : cr + col0 * (g.d / 2)), (short)0,
-                                          (int)(R16 ? 0 : rows_r * (g.d / 2)), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(R16 ? nullptr : sr + col0 * (g.d / 32)), (short)0,
-                                          (int)(R16 ? 0 : rows_r * (g.d / 32)), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(R16 ? r16 + col0 * g.d : nullptr), (short)0, (int)(R16 ? rows_r * g.d * 2 : 0),
-        0x00020000);
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(cr + col0 * (g.d / 2)), (short)0, (int)(rows_r * (g.d / 2)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(sr + col0 * (g.d / 32)), (short)0, (int)(rows_r * (g.d / 32)), 0x00020000);
     auto fetch_r = [&](int64_t k0, RRegs &R) {
-        if (R16) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int64_t k = k0 + 64 * dh + 8 * i;
-                const uint32_t o = k < g.d ? (uint32_t)((dc * g.d + k) * 2) : 0x80000000u;
-                const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rh, o, 0, 0);
-                R.h[i] = make_uint4(v[0], v[1], v[2], v[3]);
-            }
-            return;
-        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int64_t k = k0 + 64 * dh + 32 * h;  // a 32-k group
@@ -103,11 +84,6 @@ __global__ __launch_bounds__(kThreads) void lowrank_project_kernel(const uint16_
         }
     };
     auto stash_r = [&](uint8_t *buf, const RRegs &R) {
-        if (R16) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4 *>(buf + dc * kProjRow + 128 * dh + 16 * i) = R.h[i];
-            return;
-        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             uint8_t *dst = buf + dc * kProjRow + 128 * dh + 64 * h;
@@ -613,8 +589,8 @@ kq_status kq_lowrank_project(const uint16_t *X16, int64_t m, int64_t d, int64_t 
     if ((int64_t)64 * ldx * 2 >= ((int64_t)1 << 31) || (int64_t)128 * (d / 2) + 128 >= ((int64_t)1 << 31))
         return KQ_ERR_UNSUPPORTED;
     kq::ProjGeom g{m, d, ldx, r, tiles_r};
-    hipLaunchKernelGGL(kq::lowrank_project_kernel<false>, dim3((unsigned)(tiles_m * tiles_r)), dim3(kq::kThreads),
-                       0, (hipStream_t)stream, X16, g, codes_r, scales_r, nullptr, Z);
+    hipLaunchKernelGGL(kq::lowrank_project_kernel, dim3((unsigned)(tiles_m * tiles_r)), dim3(kq::kThreads),
+                       0, (hipStream_t)stream, X16, g, codes_r, scales_r, Z);
     return launched();
 }
 
