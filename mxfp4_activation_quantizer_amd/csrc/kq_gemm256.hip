@@ -49,11 +49,20 @@ namespace kq {
 namespace g256 {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 256;
-constexpr int kCode = kTile * 128;              // code bytes per operand per stage
-constexpr int kScl = kTile * 8;                 // scale bytes per operand per stage
-constexpr int kStage = 2 * kCode + 2 * kScl;    // 68 KB
+constexpr int kTile = 256;                      // output rows per tile; columns TN = 256 or 128
 constexpr int kGroupM = 4;                      // row tiles per band of the tile order
+
+// LDS layout of a stage for TN output columns: A codes [256][128], W codes [TN][128],
+// A scales [256][8], W scales [TN][8] (68 KB for TN = 256, 51 KB for TN = 128)
+template <int TN>
+struct Lay {
+    static constexpr int kOffW = kTile * 128;
+    static constexpr int kOffSA = kOffW + TN * 128;
+    static constexpr int kOffSW = kOffSA + kTile * 8;
+    static constexpr int kStage = kOffSW + TN * 8;
+    static constexpr int NB = TN / 64;   // 32-column W fragments per wave
+    static constexpr int LW = TN / 32;   // W code loads (8 rows each) per wave per stage
+};
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
@@ -67,6 +76,7 @@ struct Geom {
     int tiles_m, tiles_n, nwg;
     int vec_out;  // O 16-byte aligned and ldo % 4 == 0: 16-byte stores
     int r;        // rank of the low-rank term (LR kernels)
+    int tile_base;  // first tile (in the XCD-run order) of this launch
 };
 
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -104,13 +114,15 @@ __device__ __forceinline__ void wait_loads_and_lds_then_barrier() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+template <int NB>
 struct Frag {
-    i32x8_t a[4], b[4];
+    i32x8_t a[4], b[NB];
 };
 
 // a stage's scale dwords of the lane's rows (the same dword serves all four steps)
+template <int NB>
 struct Scl {
-    uint32_t sa[4], sb[4];
+    uint32_t sa[4], sb[NB];
 };
 
 typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
@@ -119,7 +131,12 @@ typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
 // added into the same accumulators (Z fp32 [m][r] split as hi + lo bf16, exact
 // to 2^-16 relative; deq(L) exact in bf16), 64 of r at a time through LDS, on
 // v_mfma_f32_32x32x16_bf16 with the same swapped operands and 32 x 32 layout.
-template <bool LR>
+//
+// TN = 128 is the half-width form for a launch's last partial round: tile t of the
+// XCD-run order split into its two 128-column halves (workgroup 2 i + h takes half h
+// of tile tile_base + i), each output element accumulated by the same instructions in
+// the same k order as in the full tile.
+template <bool LR, int TN>
 __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__restrict__ ca,
                                                            const uint8_t *__restrict__ psa,
                                                            const uint8_t *__restrict__ cw,
@@ -128,11 +145,14 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
                                                            const uint8_t *__restrict__ cl,
                                                            const uint8_t *__restrict__ sl,
                                                            float *__restrict__ O) {
+    static_assert(TN == 256 || (TN == 128 && !LR), "half-width tiles carry no low-rank term");
+    using L = Lay<TN>;
+    constexpr int NB = L::NB, LW = L::LW, kStage = L::kStage;
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
     const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
 
     // tile order: a contiguous run per XCD, bands of kGroupM row tiles, column-major inside a band
-    int tile = blockIdx.x;
+    int tile = g.tile_base + (TN == 256 ? (int)blockIdx.x : (int)(blockIdx.x >> 1));
     {
         const int q = g.nwg / 8, rm = g.nwg % 8, x = tile % 8, loc = tile / 8;
         tile = x < rm ? x * (q + 1) + loc : rm * (q + 1) + (x - rm) * q + loc;
@@ -140,8 +160,9 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
     const int band = tile / (kGroupM * g.tiles_n), within = tile % (kGroupM * g.tiles_n);
     const int gm = min(kGroupM, g.tiles_m - band * kGroupM);
     const int tm = band * kGroupM + within % gm, tn = within / gm;
-    const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
-    const int rows_a = (int)min<int64_t>(kTile, g.m - m0), rows_w = (int)min<int64_t>(kTile, g.n - n0);
+    const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile + (TN == 256 ? 0 : 128 * (int)(blockIdx.x & 1));
+    const int rows_a = (int)min<int64_t>(kTile, g.m - m0), rows_w = (int)min<int64_t>(TN, g.n - n0);
+    if (rows_w <= 0) return;  // the right half of a tile narrower than 129 columns (whole workgroup)
 
     // codes: rows past m or n are past the record count and read zero
     const i32x4_t dca = sdesc(ca + m0 * g.kbytes, (uint32_t)(rows_a * g.kbytes));
@@ -153,44 +174,53 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
     const i32x4_t dsw = sdesc(psw, (uint32_t)(g.stages * 8 * g.n));
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-    // code load j (0..7) of wave w: rows 64 w + 8 j + (lane >> 3), slot lane & 7
-    uint32_t cvoff[8];
+    // code load j of wave w: A rows 64 w + 8 j + (lane >> 3) (j < 8), W rows
+    // (TN / 4) w + 8 j + (lane >> 3) (j < LW); slot lane & 7
+    uint32_t cvoff[8], cvoffw[LW];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int row = 64 * w + 8 * j + (lane >> 3);
         cvoff[j] = (uint32_t)(row * g.kbytes) + 16u * (uint32_t)((lane & 7) ^ swz8(row & 15));
     }
-    // loads of stage s: i in 0..7 A codes, 8..15 W codes
+#pragma unroll
+    for (int j = 0; j < LW; ++j) {
+        const int row = (TN / 4) * w + 8 * j + (lane >> 3);
+        cvoffw[j] = (uint32_t)(row * g.kbytes) + 16u * (uint32_t)((lane & 7) ^ swz8(row & 15));
+    }
+    // loads of stage s: i in 0..7 A codes, 8..8 + LW - 1 W codes
     auto issue_code = [&](int s, int i) {
         const uint32_t st = lds0 + (uint32_t)((s & 1) * kStage);
         const uint32_t kb = 128u * (uint32_t)s;
         if (i < 8) dma16(dca, st + (64 * w + 8 * i) * 128, cvoff[i], kb);
-        else dma16(dcw, st + kCode + (64 * w + 8 * (i - 8)) * 128, cvoff[i - 8], kb);
+        else dma16(dcw, st + L::kOffW + ((TN / 4) * w + 8 * (i - 8)) * 128, cvoffw[i - 8], kb);
     };
-    // scales of stage s: 1 KB per wave (w < 2: A rows 128 w .., else W rows 128 (w - 2) ..)
+    // scales of stage s, 1 KB per load: A rows 128 (w & 1) .. by waves 0 and 1, W rows
+    // 128 (w & 1) .. by waves 2 and 3 (TN = 256) or all TN rows by wave 2 (TN = 128)
     const int srow = 128 * (w & 1) + 2 * lane;
     auto issue_scl = [&](int s) {
-        const uint32_t st = lds0 + (uint32_t)((s & 1) * kStage) + 2 * kCode + 1024 * (w & 1);
-        if (w < 2) dma16(dsa, st, (uint32_t)(8 * (m0 + srow)), (uint32_t)(8 * g.m) * (uint32_t)s);
-        else dma16(dsw, st + kScl, (uint32_t)(8 * (n0 + srow)), (uint32_t)(8 * g.n) * (uint32_t)s);
+        const uint32_t st = lds0 + (uint32_t)((s & 1) * kStage);
+        if (w < 2)
+            dma16(dsa, st + L::kOffSA + 1024 * (w & 1), (uint32_t)(8 * (m0 + srow)), (uint32_t)(8 * g.m) * (uint32_t)s);
+        else if (TN == 256 || w == 2)
+            dma16(dsw, st + L::kOffSW + 1024 * (w & 1), (uint32_t)(8 * (n0 + srow)), (uint32_t)(8 * g.n) * (uint32_t)s);
     };
 
     const int r = lane & 31, hi = lane >> 5;
-    const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
+    const int wm = (w >> 1) * 128, wn = (w & 1) * (TN / 2);
     int rdo[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) rdo[j] = r * 128 + 16 * ((2 * j + hi) ^ swz8(r & 15));
 
     // stage s: the scale dword of the lane's block parity hi (byte j is block 2 j + hi)
-    auto read_scl = [&](int s, Scl &S) {
-        const uint8_t *sc = smem + (s & 1) * kStage + 2 * kCode + 4 * hi + 8 * r;
+    auto read_scl = [&](int s, Scl<NB> &S) {
+        const uint8_t *sc = smem + (s & 1) * kStage + 4 * hi + 8 * r;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) S.sa[a] = *reinterpret_cast<const uint32_t *>(sc + 8 * (wm + 32 * a));
+        for (int a = 0; a < 4; ++a) S.sa[a] = *reinterpret_cast<const uint32_t *>(sc + L::kOffSA + 8 * (wm + 32 * a));
 #pragma unroll
-        for (int b = 0; b < 4; ++b) S.sb[b] = *reinterpret_cast<const uint32_t *>(sc + kScl + 8 * (wn + 32 * b));
+        for (int b = 0; b < NB; ++b) S.sb[b] = *reinterpret_cast<const uint32_t *>(sc + L::kOffSW + 8 * (wn + 32 * b));
     };
     // step j of stage s: 16-byte fragments (k group 2 j + hi)
-    auto read_frags = [&](int s, int j, Frag &F) {
+    auto read_frags = [&](int s, int j, Frag<NB> &F) {
         const uint8_t *st = smem + (s & 1) * kStage;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
@@ -198,32 +228,32 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
             F.a[a] = i32x8_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
         }
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const uint4 q = *reinterpret_cast<const uint4 *>(st + kCode + (wn + 32 * b) * 128 + rdo[j]);
+        for (int b = 0; b < NB; ++b) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(st + L::kOffW + (wn + 32 * b) * 128 + rdo[j]);
             F.b[b] = i32x8_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
         }
     };
 
-    floatx16_t acc[4][4];
+    floatx16_t acc[4][NB];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
     // the scale of group 2 j + hi is byte j of the lane's scale dword: the byte
     // select (op_sel) of the instruction's scale operands, uniform across lanes
-    auto mma = [&](const Frag &F, const Scl &S, auto jc, int a, int b) {
+    auto mma = [&](const Frag<NB> &F, const Scl<NB> &S, auto jc, int a, int b) {
         constexpr int j = decltype(jc)::value;
         acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[b], F.a[a], acc[a][b], 4, 4, j, (int)S.sb[b],
                                                                     j, (int)S.sa[a]);
     };
-    auto step = [&](const Frag &F, const Scl &S, auto jc) {
+    auto step = [&](const Frag<NB> &F, const Scl<NB> &S, auto jc) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) mma(F, S, jc, a, b);
+            for (int b = 0; b < NB; ++b) mma(F, S, jc, a, b);
     };
     using J0 = std::integral_constant<int, 0>;
     using J1 = std::integral_constant<int, 1>;
@@ -233,10 +263,10 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
     if (g.stages > 0) {  // k == 0: O = 0
     issue_scl(0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) issue_code(0, i);
+    for (int i = 0; i < 8 + LW; ++i) issue_code(0, i);
     wait_loads_and_lds_then_barrier();
-    Frag F0, F1;
-    Scl S, Sn;
+    Frag<NB> F0, F1;
+    Scl<NB> S, Sn;
     read_scl(0, S);
     read_frags(0, 0, F0);
 
@@ -247,13 +277,17 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
     for (int s = 0; s + 1 < g.stages; ++s) {
         read_frags(s, 1, F1);
         __builtin_amdgcn_sched_barrier(0);
+        // the 8 + LW code loads and the scale load of stage s + 1 spread over the
+        // 4 NB matrix instructions of step 0
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
+            for (int b = 0; b < NB; ++b) {
+                const int slot = NB * a + b;
                 mma(F0, S, J0(), a, b);
-                issue_code(s + 1, 4 * a + b);
-                if (a == 1 && b == 3) issue_scl(s + 1);
+                issue_code(s + 1, slot);
+                if (slot + 4 * NB < 8 + LW) issue_code(s + 1, slot + 4 * NB);
+                if (slot == 7) issue_scl(s + 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
         read_frags(s, 2, F0);
@@ -360,12 +394,12 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
     // rows past m are past the record count and dropped, columns checked
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         O + m0 * g.ldo + n0, (short)0, (int)(((int64_t)(rows_a - 1) * g.ldo + (g.n - n0)) * 4), 0x00020000);
-    const bool full_n = g.vec_out && n0 + kTile <= g.n;
+    const bool full_n = g.vec_out && n0 + TN <= g.n;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int row = wm + 32 * a + r;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int col = wn + 32 * b + 8 * q + 4 * hi;
@@ -381,6 +415,19 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
                 }
             }
     }
+}
+
+// Compute units of the current device (cached per device; 256 on MI355X).
+static int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 // scales [rows][kblocks] -> [kblocks / 8][rows][8], even blocks first: one 8-byte run per thread
@@ -450,9 +497,23 @@ kq_status kq_mxfp4_gemm_packed(const uint8_t *codes_a, const uint8_t *packed_sca
     g.nwg = (int)(tiles_m * tiles_n);
     g.vec_out = aligned(O, 16) && ldo % 4 == 0;
     g.r = 0;
-    hipLaunchKernelGGL(kq::g256::gemm256_kernel<false>, dim3((unsigned)g.nwg), dim3(kq::g256::kThreads), 0,
-                       (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, nullptr, nullptr,
-                       nullptr, O);
+    // Whole rounds of full tiles, then the last partial round as half-width tiles when
+    // twice its tile count still fits one round of CUs (e.g. 864 tiles on 256 CUs: 768
+    // full, then 96 tiles as 192 halves, about half a round instead of a whole one).
+    const int ncu = kq::g256::cu_count();
+    const int rem = g.nwg % ncu;
+    const int nfull = (rem > 0 && 2 * rem <= ncu) ? g.nwg - rem : g.nwg;
+    g.tile_base = 0;
+    if (nfull > 0)
+        hipLaunchKernelGGL((kq::g256::gemm256_kernel<false, 256>), dim3((unsigned)nfull), dim3(kq::g256::kThreads), 0,
+                           (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, nullptr,
+                           nullptr, nullptr, O);
+    if (nfull < g.nwg) {
+        g.tile_base = nfull;
+        hipLaunchKernelGGL((kq::g256::gemm256_kernel<false, 128>), dim3((unsigned)(2 * (g.nwg - nfull))),
+                           dim3(kq::g256::kThreads), 0, (hipStream_t)stream, codes_a, packed_scales_a, codes_w,
+                           packed_scales_w, g, nullptr, nullptr, nullptr, O);
+    }
     return launched();
 }
 
@@ -483,7 +544,8 @@ kq_status kq_mxfp4_gemm_packed_lowrank(const uint8_t *codes_a, const uint8_t *pa
     g.nwg = (int)(tiles_m * tiles_n);
     g.vec_out = aligned(O, 16) && ldo % 4 == 0;
     g.r = (int)r;
-    hipLaunchKernelGGL(kq::g256::gemm256_kernel<true>, dim3((unsigned)g.nwg), dim3(kq::g256::kThreads), 0,
+    g.tile_base = 0;
+    hipLaunchKernelGGL((kq::g256::gemm256_kernel<true, 256>), dim3((unsigned)g.nwg), dim3(kq::g256::kThreads), 0,
                        (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, Z, codes_l,
                        scales_l, O);
     return launched();
