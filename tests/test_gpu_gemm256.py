@@ -97,11 +97,12 @@ def test_packed_gemm_matches_oracle(torch_dev, kq, orc, m, n, k, seed):
     assert np.all(np.abs(got - O_old) <= 2 * bound(orc, ca, sa, cw, sw, k))
 
 
-@pytest.mark.parametrize("m,n,k,seed", [(300, 600, 3072, 7), (513, 257, 1024, 8)])
+@pytest.mark.parametrize("m,n,k,seed", [(300, 600, 3072, 7), (513, 257, 1024, 8), (6400, 3072, 512, 10)])
 def test_packed_gemm_exact_sums_bit_identical(torch_dev, kq, orc, m, n, k, seed):
     """Scales in 2^-1 .. 2^1: every product is a multiple of 2^-4 below 144 in magnitude,
     so for k <= 3072 every fp32 partial sum is exact and all summation orders agree:
-    the packed kernel, kq_mxfp4_gemm and the fp64 oracle give the same fp32 values."""
+    the packed kernel, kq_mxfp4_gemm and the fp64 oracle give the same fp32 values.
+    6400 x 3072 is 300 tiles: whole rounds of full tiles plus the rest as half tiles."""
     torch = torch_dev
     case("packed gemm exact sums m=%d n=%d k=%d" % (m, n, k))
     ca, sa, cw, sw = operands(np.random.default_rng(seed), m, n, k, 126, 129)
