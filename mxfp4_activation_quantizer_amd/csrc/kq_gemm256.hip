@@ -132,7 +132,8 @@ typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
 // to 2^-16 relative; deq(L) exact in bf16), 64 of r at a time through LDS, on
 // v_mfma_f32_32x32x16_bf16 with the same swapped operands and 32 x 32 layout.
 //
-// TN = 128 is the half-width form for a launch's last partial round: tile t of the
+// TN = 128 is the half-width form for a launch's last partial round (with or
+// without the low-rank term; its staging, 96 KB, fits the smaller LDS): tile t of the
 // XCD-run order split into its two 128-column halves (workgroup 2 i + h takes half h
 // of tile tile_base + i), each output element accumulated by the same instructions in
 // the same k order as in the full tile.
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
                                                            const uint8_t *__restrict__ cl,
                                                            const uint8_t *__restrict__ sl,
                                                            float *__restrict__ O) {
-    static_assert(TN == 256 || (TN == 128 && !LR), "half-width tiles carry no low-rank term");
+    static_assert(TN == 256 || TN == 128, "tile width");
     using L = Lay<TN>;
     constexpr int NB = L::NB, LW = L::LW, kStage = L::kStage;
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
@@ -372,16 +373,16 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const int off = 16 * ((2 * kk + hi) ^ swz8(r & 15));
-                bf16x8v_t lf[4];
+                bf16x8v_t lf[NB];
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
+                for (int b = 0; b < NB; ++b)
                     lf[b] = *reinterpret_cast<const bf16x8v_t *>(ll + (wn + 32 * b + r) * 128 + off);
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     const bf16x8v_t hf = *reinterpret_cast<const bf16x8v_t *>(zh + (wm + 32 * a + r) * 128 + off);
                     const bf16x8v_t lo = *reinterpret_cast<const bf16x8v_t *>(zl + (wm + 32 * a + r) * 128 + off);
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) {
+                    for (int b = 0; b < NB; ++b) {
                         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[b], hf, acc[a][b], 0, 0, 0);
                         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[b], lo, acc[a][b], 0, 0, 0);
                     }
@@ -544,10 +545,22 @@ kq_status kq_mxfp4_gemm_packed_lowrank(const uint8_t *codes_a, const uint8_t *pa
     g.nwg = (int)(tiles_m * tiles_n);
     g.vec_out = aligned(O, 16) && ldo % 4 == 0;
     g.r = (int)r;
+    // whole rounds of full tiles, then the last partial round as half tiles (as in
+    // kq_mxfp4_gemm_packed)
+    const int ncu = kq::g256::cu_count();
+    const int rem = g.nwg % ncu;
+    const int nfull = (rem > 0 && 2 * rem <= ncu) ? g.nwg - rem : g.nwg;
     g.tile_base = 0;
-    hipLaunchKernelGGL((kq::g256::gemm256_kernel<true, 256>), dim3((unsigned)g.nwg), dim3(kq::g256::kThreads), 0,
-                       (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, Z, codes_l,
-                       scales_l, O);
+    if (nfull > 0)
+        hipLaunchKernelGGL((kq::g256::gemm256_kernel<true, 256>), dim3((unsigned)nfull), dim3(kq::g256::kThreads), 0,
+                           (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, Z, codes_l,
+                           scales_l, O);
+    if (nfull < g.nwg) {
+        g.tile_base = nfull;
+        hipLaunchKernelGGL((kq::g256::gemm256_kernel<true, 128>), dim3((unsigned)(2 * (g.nwg - nfull))),
+                           dim3(kq::g256::kThreads), 0, (hipStream_t)stream, codes_a, packed_scales_a, codes_w,
+                           packed_scales_w, g, Z, codes_l, scales_l, O);
+    }
     return launched();
 }
 
