@@ -51,11 +51,10 @@ __global__ __launch_bounds__(kThreads) void lowrank_project_kernel(const uint16_
     __shared__ __attribute__((aligned(16))) uint8_t rl[2][128 * kProjRow];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int64_t tm = blockIdx.x / g.tiles_r, tr = blockIdx.x % g.tiles_r;
-    const int64_t row = tm * 64 + wave * 16 + (lane & 15), col0 = tr * 128;
+    const int64_t col0 = tr * 128;
     const int grp = lane >> 4;
     // this thread's share of an R slice: column dc, k half dh (64 k = 32 code bytes, 2 scales)
     const int dc = t >> 1, dh = t & 1;
-    const int64_t rn = col0 + dc;
     struct RRegs {
         uint4 c[2];
         uint32_t s[2];

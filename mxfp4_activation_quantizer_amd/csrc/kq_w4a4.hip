@@ -164,7 +164,7 @@ __device__ __forceinline__ void derive_coefs(const float *__restrict__ factors, 
     for (int k = 0; k < 5; ++k) {
         const float p = f[4 * k + 1] * __builtin_amdgcn_rcpf(f[4 * k + 3]);
         const float q = f[4 * k + 2] * __builtin_amdgcn_rcpf(f[4 * k]);
-        ok = ok & (fabsf(p) <= lim) & (fabsf(q) <= lim);
+        ok = (int)ok & (int)(fabsf(p) <= lim) & (int)(fabsf(q) <= lim);  // false for inf and NaN
         if (k == 0) dst[0] = b4 ? p : q;
         else if (k == 1) dst[1] = b3 ? p : q;
         else {
