@@ -33,7 +33,9 @@
  * Conventions for every entry point that takes a stream:
  *   - Pointers named "device" point to GPU memory that the caller allocates,
  *     owns and keeps alive until the enqueued work has finished. The library
- *     allocates nothing, keeps no state between calls and never synchronizes.
+ *     allocates nothing and never synchronizes; the only state it keeps
+ *     between calls is a per-device cache of the compute-unit count (read once
+ *     with hipDeviceGetAttribute by the packed GEMMs to size their launches).
  *   - Work is enqueued on `stream` (NULL = the default stream) and runs
  *     asynchronously; results are valid once the stream has reached it.
  *   - Arguments are checked on the host before anything is enqueued; on an
