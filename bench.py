@@ -248,11 +248,15 @@ def extras(torch, kq, synth, flux_sets, reps=100, warmup=20):
     psw = kq.pack_mxfp4_scales(sw)
     d_pk = _events_us(torch, lambda: kq.pack_mxfp4_scales(sa, out=psa), 20, 3)
     d_gp = _events_us(torch, lambda: kq.mxfp4_gemm_packed(ca, psa, cw, psw, out=O), 20, 3)
-    med_pk, med_gp = float(np.median(d_pk)), float(np.median(d_gp))
+    Ob = torch.empty((A.shape[0], 3072), dtype=torch.bfloat16, device="cuda")
+    d_gb = _events_us(torch, lambda: kq.mxfp4_gemm_packed(ca, psa, cw, psw, out=Ob, bf16=True), 20, 3)
+    med_pk, med_gp, med_gb = float(np.median(d_pk)), float(np.median(d_gp)), float(np.median(d_gb))
     out["w4a4_gemm_18432x3072x3072"].update({
         "packed_median_us": round(med_gp, 1), "packed_TFLOPs": round(flops / (med_gp * 1e-6) / 1e12, 1),
         "packed_pct_fp4_peak": round(100 * flops / (med_gp * 1e-6) / 10.1e15, 2),
-        "pack_a_scales_us": round(med_pk, 2)})
+        "pack_a_scales_us": round(med_pk, 2),
+        "packed_bf16_out_median_us": round(med_gb, 1),
+        "packed_bf16_out_pct_fp4_peak": round(100 * flops / (med_gb * 1e-6) / 10.1e15, 2)})
     log("weight side / gemm: %s %s" % (out["weight_fold_3072x3072"], out["w4a4_gemm_18432x3072x3072"]))
     # the same product on the 128 x 512-tile kernel, and the layer with the transform and
     # quantizer in the product's prologue against the two launches it replaces

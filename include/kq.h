@@ -195,6 +195,19 @@ kq_status kq_mxfp4_gemm_packed(const uint8_t *codes_a, const uint8_t *packed_sca
                                int64_t ldo, kq_stream_t stream);
 
 /*
+ * kq_mxfp4_gemm_packed with O written in bf16: each fp32 result of
+ * kq_mxfp4_gemm_packed rounded to the nearest bf16 (ties to even), bit for bit
+ * (for the bf16 activations a transformer layer passes on; half the output
+ * bytes of the fp32 form).
+ *   O   device, bf16 bits [m][ldo], ldo >= n, 2-byte aligned; written
+ * Other arguments and rules as kq_mxfp4_gemm_packed (256 rows of O must span
+ * fewer than 2^31 bytes).
+ */
+kq_status kq_mxfp4_gemm_packed_bf16(const uint8_t *codes_a, const uint8_t *packed_scales_a,
+                                    const uint8_t *codes_w, const uint8_t *packed_scales_w, int64_t m, int64_t n,
+                                    int64_t k, uint16_t *O, int64_t ldo, kq_stream_t stream);
+
+/*
  * The layer of Sec. 3.4 Eq. 11 on the packed-scale GEMM: O = deq(A) deq(W)^T +
  * Z deq(L)^T, the low-rank term added after the product in the same kernel (Z
  * split into two bf16 terms, exact to 2^-16 relative; deq(L) exact in bf16),

@@ -33,6 +33,7 @@ EXPORTS = (
     "kq_lowrank_project_bf16",
     "kq_dequantize_mxfp4_bf16",
     "kq_mxfp4_gemm_packed",
+    "kq_mxfp4_gemm_packed_bf16",
     "kq_mxfp4_gemm_packed_lowrank",
     "kq_transform_quantize_mxfp4_gemm",
     "kq_hadamard_quantize_mxfp4",
@@ -81,6 +82,7 @@ def lib():
             "kq_lowrank_project_bf16": [p, i64, i64, i64, p, i64, p, p],
             "kq_dequantize_mxfp4_bf16": [p, p, i64, i64, p, p],
             "kq_mxfp4_gemm_packed": [p, p, p, p, i64, i64, i64, p, i64, p],
+            "kq_mxfp4_gemm_packed_bf16": [p, p, p, p, i64, i64, i64, p, i64, p],
             "kq_mxfp4_gemm_packed_lowrank": [p, p, p, p, i64, i64, i64, p, p, p, i64, p, i64, p],
             "kq_transform_quantize_mxfp4_gemm": [p, i64, i64, i64, p, p, p, i64, p, i64, p],
             "kq_hadamard_quantize_mxfp4": [p, i64, i64, i64, i64, p, p, p, p],
@@ -412,8 +414,9 @@ def pack_mxfp4_scales(scales, out=None, stream=None):
     return out
 
 
-def mxfp4_gemm_packed(codes_a, packed_scales_a, codes_w, packed_scales_w, out=None, stream=None):
-    """O = deq(A) deq(W)^T in fp32, scales packed by pack_mxfp4_scales (k % 256 == 0)."""
+def mxfp4_gemm_packed(codes_a, packed_scales_a, codes_w, packed_scales_w, out=None, stream=None, bf16=False):
+    """O = deq(A) deq(W)^T in fp32 (bf16=True: rounded to bf16, half the output bytes), scales
+    packed by pack_mxfp4_scales (k % 256 == 0)."""
     torch = _torch()
     for t, nm in ((codes_a, "codes_a"), (packed_scales_a, "packed_scales_a"), (codes_w, "codes_w"),
                   (packed_scales_w, "packed_scales_w")):
@@ -426,13 +429,14 @@ def mxfp4_gemm_packed(codes_a, packed_scales_a, codes_w, packed_scales_w, out=No
     if tuple(codes_w.shape) != (n, kb) or packed_scales_a.numel() != m * (k // 32) or \
             packed_scales_w.numel() != n * (k // 32):
         raise ValueError("operand shapes do not match")
+    odt = torch.bfloat16 if bf16 else torch.float32
     if out is None:
-        out = torch.empty((m, n), dtype=torch.float32, device=codes_a.device)
-    _dev(out, "out", (torch.float32,))
+        out = torch.empty((m, n), dtype=odt, device=codes_a.device)
+    _dev(out, "out", (odt,))
     if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
-        raise ValueError("out must be fp32 [m][n] with unit column stride")
-    _check("kq_mxfp4_gemm_packed",
-           lib().kq_mxfp4_gemm_packed(_p(codes_a), _p(packed_scales_a), _p(codes_w), _p(packed_scales_w), m, n, k,
+        raise ValueError("out must be %s [m][n] with unit column stride" % ("bf16" if bf16 else "fp32"))
+    name = "kq_mxfp4_gemm_packed_bf16" if bf16 else "kq_mxfp4_gemm_packed"
+    _check(name, getattr(lib(), name)(_p(codes_a), _p(packed_scales_a), _p(codes_w), _p(packed_scales_w), m, n, k,
                                       _p(out), out.stride(0), _stream_ptr(stream)))
     return out
 

@@ -137,7 +137,9 @@ typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
 // XCD-run order split into its two 128-column halves (workgroup 2 i + h takes half h
 // of tile tile_base + i), each output element accumulated by the same instructions in
 // the same k order as in the full tile.
-template <bool LR, int TN>
+//
+// B16: O is written in bf16 (each fp32 sum rounded to nearest even) instead of fp32.
+template <bool LR, int TN, bool B16 = false>
 __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__restrict__ ca,
                                                            const uint8_t *__restrict__ psa,
                                                            const uint8_t *__restrict__ cw,
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
                                                            const float *__restrict__ Z,
                                                            const uint8_t *__restrict__ cl,
                                                            const uint8_t *__restrict__ sl,
-                                                           float *__restrict__ O) {
+                                                           void *__restrict__ O) {
     static_assert(TN == 256 || TN == 128, "tile width");
     using L = Lay<TN>;
     constexpr int NB = L::NB, LW = L::LW, kStage = L::kStage;
@@ -393,8 +395,10 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
 
     // lane (r, hi) holds O row wm + 32 a + r, columns wn + 32 b + 8 q + 4 hi + 0..3;
     // rows past m are past the record count and dropped, columns checked
+    constexpr int esz = B16 ? 2 : 4;
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-        O + m0 * g.ldo + n0, (short)0, (int)(((int64_t)(rows_a - 1) * g.ldo + (g.n - n0)) * 4), 0x00020000);
+        static_cast<char *>(O) + (m0 * g.ldo + n0) * esz, (short)0,
+        (int)(((int64_t)(rows_a - 1) * g.ldo + (g.n - n0)) * esz), 0x00020000);
     const bool full_n = g.vec_out && n0 + TN <= g.n;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -404,15 +408,31 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int col = wn + 32 * b + 8 * q + 4 * hi;
-                const uint32_t off = (uint32_t)((row * g.ldo + col) * 4);
-                const u32x4_t v = {__float_as_uint(acc[a][b][4 * q]), __float_as_uint(acc[a][b][4 * q + 1]),
-                                   __float_as_uint(acc[a][b][4 * q + 2]), __float_as_uint(acc[a][b][4 * q + 3])};
-                if (full_n) {
-                    __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, 0);
-                } else {
+                const uint32_t off = (uint32_t)((row * g.ldo + col) * esz);
+                if (B16) {
+                    uint32_t h[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n0 + col + e < g.n) __builtin_amdgcn_raw_buffer_store_b32(v[e], ro, off + 4 * e, 0, 0);
+                    for (int e = 0; e < 4; ++e) h[e] = bf16_rne_bits(acc[a][b][4 * q + e]);
+                    if (full_n) {
+                        typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+                        const u32x2_t v = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+                        __builtin_amdgcn_raw_buffer_store_b64(v, ro, off, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n0 + col + e < g.n)
+                                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)h[e], ro, off + 2 * e, 0, 0);
+                    }
+                } else {
+                    const u32x4_t v = {__float_as_uint(acc[a][b][4 * q]), __float_as_uint(acc[a][b][4 * q + 1]),
+                                       __float_as_uint(acc[a][b][4 * q + 2]), __float_as_uint(acc[a][b][4 * q + 3])};
+                    if (full_n) {
+                        __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n0 + col + e < g.n) __builtin_amdgcn_raw_buffer_store_b32(v[e], ro, off + 4 * e, 0, 0);
+                    }
                 }
             }
     }
@@ -472,20 +492,30 @@ kq_status kq_pack_mxfp4_scales(const uint8_t *scales, int64_t rows, int64_t k, u
     return launched();
 }
 
-kq_status kq_mxfp4_gemm_packed(const uint8_t *codes_a, const uint8_t *packed_scales_a, const uint8_t *codes_w,
-                               const uint8_t *packed_scales_w, int64_t m, int64_t n, int64_t k, float *O,
-                               int64_t ldo, kq_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// kq_mxfp4_gemm_packed and its bf16-output form: checks, then whole rounds of full
+// tiles and the last partial round as half-width tiles when twice its tile count
+// still fits one round of CUs (e.g. 864 tiles on 256 CUs: 768 full, then 96 tiles as
+// 192 halves, about half a round instead of a whole one).
+template <bool B16>
+kq_status gemm_packed(const uint8_t *codes_a, const uint8_t *packed_scales_a, const uint8_t *codes_w,
+                      const uint8_t *packed_scales_w, int64_t m, int64_t n, int64_t k, void *O, int64_t ldo,
+                      kq_stream_t stream) {
+    constexpr int esz = B16 ? 2 : 4;
     if (m < 0 || n < 0 || k < 0 || k % 256 != 0 || ldo < n) return KQ_ERR_SHAPE;
     if (m == 0 || n == 0) return KQ_OK;
     if (!O || (k > 0 && (!codes_a || !packed_scales_a || !codes_w || !packed_scales_w))) return KQ_ERR_NULL;
     if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || !aligned(packed_scales_a, 16) ||
-        !aligned(packed_scales_w, 16) || !aligned(O, 4))
+        !aligned(packed_scales_w, 16) || !aligned(O, esz))
         return KQ_ERR_ALIGN;
     // buffer record counts and offsets are 32-bit
     const int64_t lim = (int64_t)1 << 31;
     const int64_t tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
     if ((int64_t)256 * (k / 2) >= lim || m * (k / 32) >= lim || n * (k / 32) >= lim ||
-        ((int64_t)255 * ldo + n) * 4 >= lim || tiles_m * tiles_n >= lim)
+        ((int64_t)255 * ldo + n) * esz >= lim || tiles_m * tiles_n >= lim)
         return KQ_ERR_UNSUPPORTED;
     kq::g256::Geom g;
     g.m = m;
@@ -496,26 +526,39 @@ kq_status kq_mxfp4_gemm_packed(const uint8_t *codes_a, const uint8_t *packed_sca
     g.tiles_m = (int)tiles_m;
     g.tiles_n = (int)tiles_n;
     g.nwg = (int)(tiles_m * tiles_n);
-    g.vec_out = aligned(O, 16) && ldo % 4 == 0;
+    g.vec_out = aligned(O, 4 * esz) && ldo % 4 == 0;
     g.r = 0;
-    // Whole rounds of full tiles, then the last partial round as half-width tiles when
-    // twice its tile count still fits one round of CUs (e.g. 864 tiles on 256 CUs: 768
-    // full, then 96 tiles as 192 halves, about half a round instead of a whole one).
     const int ncu = kq::g256::cu_count();
     const int rem = g.nwg % ncu;
     const int nfull = (rem > 0 && 2 * rem <= ncu) ? g.nwg - rem : g.nwg;
     g.tile_base = 0;
     if (nfull > 0)
-        hipLaunchKernelGGL((kq::g256::gemm256_kernel<false, 256>), dim3((unsigned)nfull), dim3(kq::g256::kThreads), 0,
-                           (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, nullptr,
-                           nullptr, nullptr, O);
+        hipLaunchKernelGGL((kq::g256::gemm256_kernel<false, 256, B16>), dim3((unsigned)nfull),
+                           dim3(kq::g256::kThreads), 0, (hipStream_t)stream, codes_a, packed_scales_a, codes_w,
+                           packed_scales_w, g, nullptr, nullptr, nullptr, O);
     if (nfull < g.nwg) {
         g.tile_base = nfull;
-        hipLaunchKernelGGL((kq::g256::gemm256_kernel<false, 128>), dim3((unsigned)(2 * (g.nwg - nfull))),
+        hipLaunchKernelGGL((kq::g256::gemm256_kernel<false, 128, B16>), dim3((unsigned)(2 * (g.nwg - nfull))),
                            dim3(kq::g256::kThreads), 0, (hipStream_t)stream, codes_a, packed_scales_a, codes_w,
                            packed_scales_w, g, nullptr, nullptr, nullptr, O);
     }
     return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+kq_status kq_mxfp4_gemm_packed(const uint8_t *codes_a, const uint8_t *packed_scales_a, const uint8_t *codes_w,
+                               const uint8_t *packed_scales_w, int64_t m, int64_t n, int64_t k, float *O,
+                               int64_t ldo, kq_stream_t stream) {
+    return gemm_packed<false>(codes_a, packed_scales_a, codes_w, packed_scales_w, m, n, k, O, ldo, stream);
+}
+
+kq_status kq_mxfp4_gemm_packed_bf16(const uint8_t *codes_a, const uint8_t *packed_scales_a,
+                                    const uint8_t *codes_w, const uint8_t *packed_scales_w, int64_t m, int64_t n,
+                                    int64_t k, uint16_t *O, int64_t ldo, kq_stream_t stream) {
+    return gemm_packed<true>(codes_a, packed_scales_a, codes_w, packed_scales_w, m, n, k, O, ldo, stream);
 }
 
 kq_status kq_mxfp4_gemm_packed_lowrank(const uint8_t *codes_a, const uint8_t *packed_scales_a,

@@ -100,6 +100,12 @@ GOOD = P(0x10000)  # never dereferenced: every case below fails before a launch
     ("kq_mxfp4_gemm_packed", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, P(0x10002), 4, None), kq.KQ_ERR_ALIGN),
     ("kq_mxfp4_gemm_packed", (GOOD, GOOD, GOOD, GOOD, 4, 4, 1 << 24, GOOD, 4, None), kq.KQ_ERR_UNSUPPORTED),
     ("kq_mxfp4_gemm_packed", (None, None, None, None, 0, 4, 256, None, 4, None), kq.KQ_OK),
+    ("kq_mxfp4_gemm_packed_bf16", (GOOD, GOOD, GOOD, GOOD, 4, 4, 128, GOOD, 4, None), kq.KQ_ERR_SHAPE),
+    ("kq_mxfp4_gemm_packed_bf16", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, GOOD, 3, None), kq.KQ_ERR_SHAPE),
+    ("kq_mxfp4_gemm_packed_bf16", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, None, 4, None), kq.KQ_ERR_NULL),
+    ("kq_mxfp4_gemm_packed_bf16", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, P(0x10001), 4, None), kq.KQ_ERR_ALIGN),
+    ("kq_mxfp4_gemm_packed_bf16", (GOOD, GOOD, GOOD, GOOD, 4, 4, 1 << 24, GOOD, 4, None), kq.KQ_ERR_UNSUPPORTED),
+    ("kq_mxfp4_gemm_packed_bf16", (None, None, None, None, 4, 0, 256, None, 4, None), kq.KQ_OK),
     ("kq_mxfp4_gemm_packed_lowrank", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, GOOD, GOOD, GOOD, 48, GOOD, 4, None),
      kq.KQ_ERR_SHAPE),
     ("kq_mxfp4_gemm_packed_lowrank", (GOOD, GOOD, GOOD, GOOD, 4, 4, 128, GOOD, GOOD, GOOD, 32, GOOD, 4, None),

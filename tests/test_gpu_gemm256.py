@@ -157,6 +157,27 @@ def test_packed_gemm_lowrank_matches_oracle(torch_dev, kq, orc, m, n, k, r):
     assert np.all(np.abs(O.cpu().numpy().astype(np.float64) - ref) <= b)
 
 
+@pytest.mark.parametrize("m,n,k,pad,seed", [(1000, 700, 512, 0, 21), (300, 1100, 768, 3, 22), (257, 513, 256, 1, 23),
+                                            (18432, 3072, 3072, 0, 24)])
+def test_packed_gemm_bf16_is_rounded_fp32(torch_dev, kq, m, n, k, pad, seed):
+    """The bf16-output form equals the fp32 form rounded to nearest even, bit for bit, for
+    aligned (8-byte stores) and odd-stride (2-byte stores) outputs; padding stays untouched."""
+    torch = torch_dev
+    case("packed gemm bf16 m=%d n=%d k=%d ldo=%d" % (m, n, k, n + pad))
+    ca, sa, cw, sw = operands(np.random.default_rng(seed), m, n, k)
+    O32, (dca, dsa, dcw, dsw) = run_packed(torch, kq, ca, sa, cw, sw)
+    psa, psw = kq.pack_mxfp4_scales(dsa), kq.pack_mxfp4_scales(dsw)
+    ldo = n + pad
+    buf = torch.full((m * ldo + 16,), -5.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[:m * ldo].view(m, ldo)[:, :n]
+    kq.mxfp4_gemm_packed(dca, psa, dcw, psw, out=out, bf16=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, O32.to(torch.bfloat16))
+    whole = buf.float().cpu().numpy()
+    assert np.all(whole[m * ldo:] == -5.0)
+    assert np.all(whole[:m * ldo].reshape(m, ldo)[:, n:] == -5.0)
+
+
 def test_packed_gemm_k0_and_empty(torch_dev, kq):
     torch = torch_dev
     case("packed gemm k=0 and empty")
