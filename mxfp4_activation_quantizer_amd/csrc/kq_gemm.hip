@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "kq.h"
+#include "kq_cvt.hpp"
 #include "kq_device.hpp"
 #include "kq_host.hpp"
 
@@ -17,12 +18,12 @@ constexpr int kThreads = 256;
 // Low-rank branch helpers (Eq. 11's A T R^T L^T with MXFP4 L and R)
 // ---------------------------------------------------------------------------
 
-// MXFP4 -> bf16, exact (see decode_fp4x8_bf16): one thread per 8 codes.
+// MXFP4 -> bf16, exact (see decode_fp4x8_bf16_cvt): one thread per 8 codes.
 __global__ __launch_bounds__(kThreads) void dequantize_bf16_kernel(const uint32_t *__restrict__ codes,
                                                                    const uint8_t *__restrict__ scales, int64_t n8,
                                                                    bf16x8_t *__restrict__ out) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x)
-        out[i] = decode_fp4x8_bf16(codes[i], scales[i / 4]);
+        out[i] = decode_fp4x8_bf16_cvt(codes[i], scales[i / 4]);
 }
 
 // Z = X Q(R)^T: X bf16 [m][ldx] (the branch's 16-bit activations), R MXFP4
@@ -86,10 +87,10 @@ __global__ __launch_bounds__(kThreads) void lowrank_project_kernel(const uint16_
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             uint8_t *dst = buf + dc * kProjRow + 128 * dh + 64 * h;
-            *reinterpret_cast<bf16x8_t *>(dst) = decode_fp4x8_bf16(R.c[h].x, R.s[h]);
-            *reinterpret_cast<bf16x8_t *>(dst + 16) = decode_fp4x8_bf16(R.c[h].y, R.s[h]);
-            *reinterpret_cast<bf16x8_t *>(dst + 32) = decode_fp4x8_bf16(R.c[h].z, R.s[h]);
-            *reinterpret_cast<bf16x8_t *>(dst + 48) = decode_fp4x8_bf16(R.c[h].w, R.s[h]);
+            *reinterpret_cast<bf16x8_t *>(dst) = decode_fp4x8_bf16_cvt(R.c[h].x, R.s[h]);
+            *reinterpret_cast<bf16x8_t *>(dst + 16) = decode_fp4x8_bf16_cvt(R.c[h].y, R.s[h]);
+            *reinterpret_cast<bf16x8_t *>(dst + 32) = decode_fp4x8_bf16_cvt(R.c[h].z, R.s[h]);
+            *reinterpret_cast<bf16x8_t *>(dst + 48) = decode_fp4x8_bf16_cvt(R.c[h].w, R.s[h]);
         }
     };
     const int64_t rows_x = g.m - tm * 64 < 64 ? g.m - tm * 64 : 64;
@@ -490,14 +491,14 @@ __global__ __launch_bounds__(kThreads) void mxfp4_gemm_kernel(
                 const float z8[8] = {zv[2 * q].x, zv[2 * q].y, zv[2 * q].z, zv[2 * q].w,
                                      zv[2 * q + 1].x, zv[2 * q + 1].y, zv[2 * q + 1].z, zv[2 * q + 1].w};
                 bf16x8_t h, l;
-                split_bf16x8(z8, h, l);
+                split_bf16x8_cvt(z8, h, l);
                 *reinterpret_cast<bf16x8_t *>(zh_lds + sr_ * SR + 64 * sh + 16 * q) = h;
                 *reinterpret_cast<bf16x8_t *>(zl_lds + sr_ * SR + 64 * sh + 16 * q) = l;
             }
             const uint32_t lw[4] = {lc.x, lc.y, lc.z, lc.w};
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<bf16x8_t *>(l_lds + sr_ * SR + 64 * sh + 16 * q) = decode_fp4x8_bf16(lw[q], ls);
+                *reinterpret_cast<bf16x8_t *>(l_lds + sr_ * SR + 64 * sh + 16 * q) = decode_fp4x8_bf16_cvt(lw[q], ls);
             __syncthreads();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {

@@ -42,6 +42,7 @@
 #include <type_traits>
 
 #include "kq.h"
+#include "kq_cvt.hpp"
 #include "kq_device.hpp"
 #include "kq_host.hpp"
 
@@ -126,33 +127,6 @@ struct Scl {
 };
 
 typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
-
-// fp32 x = hi + lo + e with hi = bf16(x), lo = bf16(x - hi), both rounded to nearest
-// even by the hardware convert (x - hi is exact in fp32): the same split as the
-// shift-and-round form, one convert per pair instead of the integer rounding steps.
-__device__ __forceinline__ void split_bf16x8_cvt(const float x[8], bf16x8_t &hi, bf16x8_t &lo) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const __bf16 h = (__bf16)x[i];
-        hi[i] = h;
-        lo[i] = (__bf16)(x[i] - (float)h);
-    }
-}
-
-// deq of 8 E2M1 codes (element i in nibble i) under E8M0 scale byte sbyte, in bf16.
-// Every value is lvl * 2^(sbyte - 127) with lvl in {0, 0.5, ..., 6}, a normal bf16
-// (so exact in the scaled convert) for scale bytes 2..252; the rest (sub-normal,
-// overflowing and NaN scales) take the general decode.
-__device__ __forceinline__ bf16x8_t decode_fp4x8_bf16_cvt(uint32_t c8, uint32_t sbyte) {
-    if (sbyte < 2u || sbyte > 252u) return decode_fp4x8_bf16(c8, sbyte);
-    const float scale = __uint_as_float(sbyte << 23);
-    const bf16x2v_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c8, scale, 0);
-    const bf16x2v_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c8, scale, 1);
-    const bf16x2v_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c8, scale, 2);
-    const bf16x2v_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c8, scale, 3);
-    return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
 
 // LR: after the product, the low-rank term Z deq(L)^T of Sec. 3.4 Eq. 11 is
 // added into the same accumulators (Z fp32 [m][r] split as hi + lo bf16, exact

@@ -88,6 +88,25 @@ def test_dequantize_bf16_is_exact(torch_dev, kq, orc, rows, k, seed):
     assert np.array_equal(got, orc.dequantize(c, sc, k))
 
 
+def test_dequantize_bf16_every_code_and_scale(torch_dev, kq, orc):
+    """All 16 E2M1 codes under every finite E8M0 scale byte 0 .. 254: exact where the
+    value fits bf16 (subnormal at byte 0, largest normal at 252), +-inf past its
+    largest finite value (6 * 2^126 and up); both sides of the converts' range."""
+    torch = torch_dev
+    case("dequantize bf16 every code x scale byte")
+    row = np.array([(j << 4) | j for j in range(16)], dtype=np.uint8)
+    c = np.tile(row, (255, 1))
+    sc = np.arange(255, dtype=np.uint8).reshape(255, 1)
+    out = kq.dequantize_mxfp4_bf16(torch.from_numpy(c).cuda(), torch.from_numpy(sc).cuda())
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref = orc.dequantize(c, sc, 32)
+    big = np.abs(ref) > float(torch.finfo(torch.bfloat16).max)
+    assert big.sum() == 24  # codes 4 and 6 (both signs, twice each) at byte 253; 2, 3, 4, 6 at 254
+    assert np.array_equal(got[~big], ref[~big])
+    assert np.array_equal(got[big], np.sign(ref[big]) * np.inf)
+
+
 @pytest.mark.parametrize("m,d,r", [(100, 96, 32), (300, 3072, 128), (64, 512, 160), (1, 32, 32), (79, 800, 96),
                                    (81, 1152, 256), (241, 4608, 128), (18432, 3072, 128)])
 def test_lowrank_project_bf16_matches(torch_dev, kq, orc, m, d, r):
