@@ -411,18 +411,25 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
                 const int col = wn + 32 * b + 8 * q + 4 * hi;
                 const uint32_t off = (uint32_t)((row * g.ldo + col) * esz);
                 if (B16) {
-                    uint32_t h[4];
+                    // round to nearest even in the hardware convert, one per pair; plain
+                    // stores under the bounds a buffer descriptor would apply (rows below
+                    // rows_a, columns below n): with 2- and 8-byte buffer stores the
+                    // compiler kept the descriptor in vector registers and looped over it
+                    const bf16x2_t p0 = {(__bf16)acc[a][b][4 * q], (__bf16)acc[a][b][4 * q + 1]};
+                    const bf16x2_t p1 = {(__bf16)acc[a][b][4 * q + 2], (__bf16)acc[a][b][4 * q + 3]};
+                    const uint32_t w0 = __builtin_bit_cast(uint32_t, p0), w1 = __builtin_bit_cast(uint32_t, p1);
+                    uint16_t *o16 = static_cast<uint16_t *>(O) + (m0 + row) * g.ldo + n0 + col;
+                    if (row < rows_a) {
+                        if (full_n) {
+                            typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+                            *reinterpret_cast<u32x2_t *>(o16) = u32x2_t{w0, w1};
+                        } else {
+                            const uint16_t h[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1,
+                                                   (uint16_t)(w1 >> 16)};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) h[e] = bf16_rne_bits(acc[a][b][4 * q + e]);
-                    if (full_n) {
-                        typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-                        const u32x2_t v = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-                        __builtin_amdgcn_raw_buffer_store_b64(v, ro, off, 0, 0);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n0 + col + e < g.n)
-                                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)h[e], ro, off + 2 * e, 0, 0);
+                            for (int e = 0; e < 4; ++e)
+                                if (n0 + col + e < g.n) o16[e] = h[e];
+                        }
                     }
                 } else {
                     const u32x4_t v = {__float_as_uint(acc[a][b][4 * q]), __float_as_uint(acc[a][b][4 * q + 1]),
