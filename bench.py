@@ -100,6 +100,8 @@ def run_kernel(kq, kind, s: Sets, stream, k=None):
     A, c, sc = s.next() if k is None else s.get(k)
     if kind == "fused":
         kq.transform_quantize_mxfp4(A, s.factors, codes=c, scales=sc, stream=stream)
+    elif kind.startswith("fused_"):
+        kq.transform_quantize_mxfp4(A, s.factors, codes=c, scales=sc, stream=stream, form=kind[len("fused_"):])
     elif kind == "smoothquant":
         kq.smoothquant_quantize_mxfp4(A, s.inv, codes=c, scales=sc, stream=stream)
     elif kind == "hadamard32":
@@ -205,18 +207,10 @@ def extras(torch, kq, synth, flux_sets, reps=100, warmup=20):
         out["other_configs"][name] = per
         log("%s: %s" % (name, per))
         del s
-    old = os.environ.get("KQ_TRANSFORM_FORM")
-    try:
-        for form in ("mfma", "mfma_lds"):
-            os.environ["KQ_TRANSFORM_FORM"] = form
-            _, d = time_kernel(torch, kq, "fused", flux_sets, reps, warmup)
-            out["fused_%s_form" % form] = [summarize(x, s) for x, s in zip(d, flux_sets)]
-            log("%s form: %s" % (form, out["fused_%s_form" % form]))
-    finally:
-        if old is None:
-            del os.environ["KQ_TRANSFORM_FORM"]
-        else:
-            os.environ["KQ_TRANSFORM_FORM"] = old
+    for form in ("mfma", "mfma_lds"):
+        _, d = time_kernel(torch, kq, "fused_" + form, flux_sets, reps, warmup)
+        out["fused_%s_form" % form] = [summarize(x, s) for x, s in zip(d, flux_sets)]
+        log("%s form: %s" % (form, out["fused_%s_form" % form]))
     # weight side: fold and fp32 quantize of a 3072 x 3072 fp32 weight
     W = torch.from_numpy(synth.weights(3072, 3072, 1004)).cuda()
     fac = flux_sets[0].factors

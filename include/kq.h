@@ -87,25 +87,64 @@ kq_status kq_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda
  *   y_debug  device or NULL; if given, fp32 [m][d] receives y (check mode),
  *            16-byte aligned. Codes and scales do not depend on it.
  * Other arguments as kq_quantize_mxfp4.
+ *
+ * Range. y is evaluated in fp32 as five stages in the factored form
+ * G = [[1, p], [q, 1]] diag(G[0][0], G[1][1]) (p = G[0][1] / G[1][1],
+ * q = G[1][0] / G[0][0]; Sec. 3.2's mixed-product rule collects the diagonals
+ * into one per-channel multiply). A stage grows a block's largest magnitude by
+ * at most 1 + max(|p|, |q|), so a block's scale and codes are as specified
+ * when max|a| prod_k (1 + max(|p_k|, |q_k|)) < 2^128 (Hadamard factors: 2^5,
+ * i.e. any |a| < 2^123). For a block that breaks it, an fp32 intermediate may
+ * overflow and its scale and codes are unspecified (the fp64 definition above
+ * would keep y finite and clamp e at 127). Blocks of a 16-block segment
+ * containing a factor with |p| or |q| > 2^20 run the plain 2x2 stages
+ * instead, where the growth per stage is max_c (|G[0][c]| + |G[1][c]|).
  */
 kq_status kq_transform_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
                                       const float *factors, uint8_t *codes, uint8_t *scales,
                                       float *y_debug, kq_stream_t stream);
 
 /*
+ * Forms of the fused transform (Sec. 3.5.1 "Kernel variants": the block product
+ * y = a K as a dense 32x32 product with K materialized from Eq. 12, or, this
+ * library's default, as stages of the 2x2 factors):
+ *   KQ_FORM_BUTTERFLY  five in-register 2x2 stages (what kq_transform_quantize_mxfp4 runs)
+ *   KQ_FORM_MFMA       K materialized per block as three bf16 terms (exact for
+ *                      fp32 K) on bf16 matrix instructions, operands loaded directly
+ *   KQ_FORM_MFMA_LDS   the same through LDS-staged row-major tiles; needs
+ *                      d % 512 == 0, otherwise the butterfly form runs
+ * The matrix forms accumulate in fp32 in another order: the same tolerance
+ * against the exact transform, not bit-identical to the butterfly form. Their
+ * range condition: max|a| prod_k max_c (|G_k[0][c]| + |G_k[1][c]|) < 2^128.
+ */
+typedef enum { KQ_FORM_BUTTERFLY = 0, KQ_FORM_MFMA = 1, KQ_FORM_MFMA_LDS = 2 } kq_transform_form;
+
+/*
+ * kq_transform_quantize_mxfp4 in a chosen form (a kq_transform_form value;
+ * any other value: KQ_ERR_UNSUPPORTED). Arguments and rules otherwise as
+ * kq_transform_quantize_mxfp4.
+ */
+kq_status kq_transform_quantize_mxfp4_form(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
+                                           const float *factors, uint8_t *codes, uint8_t *scales,
+                                           float *y_debug, int form, kq_stream_t stream);
+
+/*
  * SmoothQuant baseline (KroQuant Appendix D.2; Sec. 4.4 "Scale" kernel):
  * T = diag(1 / gamma), i.e. y_c = fl32(a_c * inv_scale[c]) (one fp32 multiply),
  * then quantize as above.
  *   inv_scale  device, fp32 [d] = 1 / gamma_c, 16-byte aligned
- * Other arguments as kq_quantize_mxfp4. Bit-exact.
+ * Other arguments as kq_quantize_mxfp4. Bit-exact whenever every product
+ * fl32(a_c * inv_scale[c]) is finite (an overflowing product: unspecified codes).
  */
 kq_status kq_smoothquant_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
                                         const float *inv_scale, uint8_t *codes, uint8_t *scales,
                                         kq_stream_t stream);
 
 /*
- * Quantize-only on fp32 input (for folded weights before the W4A4 GEMM).
- *   X  device, fp32 [m][ldx], 16-byte aligned, ldx >= d, ldx % 4 == 0
+ * Quantize-only on fp32 input: the blockwise MXFP4 quantizer of Sec. 3.1
+ * (format as above) applied to fp32 values, e.g. the folded weights W T^{-T}
+ * of Eq. 1 before the W4A4 product of Eq. 2.
+ *   X  device, fp32 [m][ldx], 16-byte aligned, ldx >= d, ldx % 4 == 0, finite
  * Other arguments as kq_quantize_mxfp4. Bit-exact.
  */
 kq_status kq_quantize_mxfp4_f32(const float *X, int64_t m, int64_t d, int64_t ldx,

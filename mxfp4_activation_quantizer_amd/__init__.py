@@ -24,6 +24,7 @@ KQ_OK, KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_HIP, KQ_ERR_UNSUPPORTED =
 EXPORTS = (
     "kq_quantize_mxfp4",
     "kq_transform_quantize_mxfp4",
+    "kq_transform_quantize_mxfp4_form",
     "kq_smoothquant_quantize_mxfp4",
     "kq_quantize_mxfp4_f32",
     "kq_inverse_fold_weights",
@@ -72,6 +73,7 @@ def lib():
         for name, args in {
             "kq_quantize_mxfp4": [p, i64, i64, i64, p, p, p],
             "kq_transform_quantize_mxfp4": [p, i64, i64, i64, p, p, p, p, p],
+            "kq_transform_quantize_mxfp4_form": [p, i64, i64, i64, p, p, p, p, st, p],
             "kq_smoothquant_quantize_mxfp4": [p, i64, i64, i64, p, p, p, p],
             "kq_quantize_mxfp4_f32": [p, i64, i64, i64, p, p, p],
             "kq_inverse_fold_weights": [p, i64, i64, p, p, p],
@@ -172,10 +174,14 @@ def quantize_mxfp4(A, codes=None, scales=None, stream=None):
     return codes, scales
 
 
-def transform_quantize_mxfp4(A, factors, codes=None, scales=None, y_debug=None, stream=None):
+FORMS = {"butterfly": 0, "mfma": 1, "mfma_lds": 2}  # kq_transform_form
+
+
+def transform_quantize_mxfp4(A, factors, codes=None, scales=None, y_debug=None, stream=None, form=None):
     """Fused y = A T (per-block Kronecker factors fp32 [d/32][5][2][2]) then MXFP4.
 
     ``y_debug``: optional fp32 [m][d] tensor that receives y (check mode).
+    ``form``: None (the library's default, the butterfly form) or one of FORMS.
     """
     torch = _torch()
     m, d, lda = _bf16_input(A)
@@ -187,9 +193,14 @@ def transform_quantize_mxfp4(A, factors, codes=None, scales=None, y_debug=None, 
         if tuple(y_debug.shape) != (m, d) or not y_debug.is_contiguous():
             raise ValueError("y_debug must be a contiguous fp32 [m][d] tensor")
     codes, scales = _outputs(m, d, A.device, codes, scales)
-    _check("kq_transform_quantize_mxfp4",
-           lib().kq_transform_quantize_mxfp4(_p(A), m, d, lda, _p(factors), _p(codes), _p(scales),
-                                             _p(y_debug), _stream_ptr(stream)))
+    if form is None:
+        _check("kq_transform_quantize_mxfp4",
+               lib().kq_transform_quantize_mxfp4(_p(A), m, d, lda, _p(factors), _p(codes), _p(scales),
+                                                 _p(y_debug), _stream_ptr(stream)))
+    else:
+        _check("kq_transform_quantize_mxfp4_form",
+               lib().kq_transform_quantize_mxfp4_form(_p(A), m, d, lda, _p(factors), _p(codes), _p(scales),
+                                                      _p(y_debug), FORMS[form], _stream_ptr(stream)))
     return codes, scales
 
 

@@ -171,9 +171,11 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
     // codes: rows past m or n are past the record count and read zero
     const i32x4_t dca = sdesc(ca + m0 * g.kbytes, (uint32_t)(rows_a * g.kbytes));
     const i32x4_t dcw = sdesc(cw + n0 * g.kbytes, (uint32_t)(rows_w * g.kbytes));
-    // packed scales: stage s of row i at 8 (s rows + i); a padding row past m or n
-    // reads some other row's bytes, harmless because its codes are zero and its
-    // outputs are never stored
+    // packed scales: stage s of row i at 8 (s rows + i), the whole offset in the
+    // range-checked vector offset (the scalar offset is not checked), so every
+    // read stays inside the packed array: a padding row past m or n reads a
+    // later stage's bytes (harmless: its codes are zero and its outputs are
+    // never stored), or zero on the last stage
     const i32x4_t dsa = sdesc(psa, (uint32_t)(g.stages * 8 * g.m));
     const i32x4_t dsw = sdesc(psw, (uint32_t)(g.stages * 8 * g.n));
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
@@ -204,9 +206,11 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
     auto issue_scl = [&](int s) {
         const uint32_t st = lds0 + (uint32_t)((s & 1) * kStage);
         if (w < 2)
-            dma16(dsa, st + L::kOffSA + 1024 * (w & 1), (uint32_t)(8 * (m0 + srow)), (uint32_t)(8 * g.m) * (uint32_t)s);
+            dma16(dsa, st + L::kOffSA + 1024 * (w & 1), (uint32_t)(8 * (m0 + srow)) + (uint32_t)(8 * g.m) * (uint32_t)s,
+                  0u);
         else if (TN == 256 || w == 2)
-            dma16(dsw, st + L::kOffSW + 1024 * (w & 1), (uint32_t)(8 * (n0 + srow)), (uint32_t)(8 * g.n) * (uint32_t)s);
+            dma16(dsw, st + L::kOffSW + 1024 * (w & 1), (uint32_t)(8 * (n0 + srow)) + (uint32_t)(8 * g.n) * (uint32_t)s,
+                  0u);
     };
 
     const int r = lane & 31, hi = lane >> 5;

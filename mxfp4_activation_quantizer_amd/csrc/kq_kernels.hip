@@ -18,8 +18,6 @@
 // carries nothing else.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
-#include <string.h>
 
 #include "kq.h"
 #include "kq_device.hpp"
@@ -141,7 +139,7 @@ __device__ __forceinline__ void setup_ratios(const float f[20], SetupLane &S) {
     for (int k = 0; k < 5; ++k) {
         S.p[k] = f[4 * k + 1] * __builtin_amdgcn_rcpf(f[4 * k + 3]);
         S.q[k] = f[4 * k + 2] * __builtin_amdgcn_rcpf(f[4 * k]);
-        S.shear = S.shear & (fabsf(S.p[k]) <= lim) & (fabsf(S.q[k]) <= lim);  // false for inf and NaN
+        S.shear = S.shear && fabsf(S.p[k]) <= lim && fabsf(S.q[k]) <= lim;  // false for inf and NaN
     }
 }
 
@@ -670,26 +668,16 @@ kq_status launch_mfma_lds(const uint16_t *A, int64_t m, int64_t d, int64_t lda, 
     return launched();
 }
 
-// Which form of the transform the fused entry point runs (KQ_TRANSFORM_FORM,
-// read at every call): "butterfly" = five in-register 2x2 stages in shear
-// form (default); "mfma" = the materialized 32x32 block on MFMA, operands
-// loaded directly; "mfma_lds" = the same through LDS-staged row-major tiles
-// (needs d a multiple of 512, else the butterfly runs).
-enum Form { kFormButterfly, kFormMfma, kFormMfmaLds };
-Form transform_form() {
-    const char *v = getenv("KQ_TRANSFORM_FORM");
-    if (v && strcmp(v, "mfma") == 0) return kFormMfma;
-    if (v && strcmp(v, "mfma_lds") == 0) return kFormMfmaLds;
-    return kFormButterfly;
-}
-
+// The form of the transform a fused call runs (kq_transform_form): five
+// in-register 2x2 stages in shear form (the default), or the materialized 32x32
+// block on MFMA with operands loaded directly or through LDS-staged row-major
+// tiles (that one needs d a multiple of 512, else the butterfly runs).
 template <bool DEBUG>
 kq_status launch_fused(const uint16_t *A, int64_t m, int64_t d, int64_t lda, const float *factors,
-                       uint8_t *codes, uint8_t *scales, float *ydbg, kq_stream_t stream) {
-    const Form f = transform_form();
-    if (f == kFormMfmaLds && (d / 32) % 16 == 0)
+                       uint8_t *codes, uint8_t *scales, float *ydbg, int form, kq_stream_t stream) {
+    if (form == KQ_FORM_MFMA_LDS && (d / 32) % 16 == 0)
         return launch_mfma_lds<DEBUG>(A, m, d, lda, factors, codes, scales, ydbg, stream);
-    if (f != kFormMfma)
+    if (form != KQ_FORM_MFMA)
         return launch_rowwave<kq::kKron, DEBUG ? kq::kYF32 : kq::kYNone>(A, m, d, lda, factors, codes, scales, ydbg,
                                                                           stream);
     if ((d / 32) % 2 == 0)
@@ -701,17 +689,25 @@ kq_status launch_fused(const uint16_t *A, int64_t m, int64_t d, int64_t lda, con
 
 extern "C" {
 
-kq_status kq_transform_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
-                                      const float *factors, uint8_t *codes, uint8_t *scales,
-                                      float *y_debug, kq_stream_t stream) {
+kq_status kq_transform_quantize_mxfp4_form(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
+                                           const float *factors, uint8_t *codes, uint8_t *scales,
+                                           float *y_debug, int form, kq_stream_t stream) {
+    if (form != KQ_FORM_BUTTERFLY && form != KQ_FORM_MFMA && form != KQ_FORM_MFMA_LDS) return KQ_ERR_UNSUPPORTED;
     kq_status s = check_shape(m, d, lda);
     if (s != KQ_OK) return s;
     if (m == 0 || d == 0) return KQ_OK;
     if ((s = check_bf16_io(A, lda, codes, scales)) != KQ_OK) return s;
     if (!factors) return KQ_ERR_NULL;
     if (!aligned(factors, 16) || (y_debug && !aligned(y_debug, 16))) return KQ_ERR_ALIGN;
-    if (y_debug) return launch_fused<true>(A, m, d, lda, factors, codes, scales, y_debug, stream);
-    return launch_fused<false>(A, m, d, lda, factors, codes, scales, nullptr, stream);
+    if (y_debug) return launch_fused<true>(A, m, d, lda, factors, codes, scales, y_debug, form, stream);
+    return launch_fused<false>(A, m, d, lda, factors, codes, scales, nullptr, form, stream);
+}
+
+kq_status kq_transform_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
+                                      const float *factors, uint8_t *codes, uint8_t *scales,
+                                      float *y_debug, kq_stream_t stream) {
+    return kq_transform_quantize_mxfp4_form(A, m, d, lda, factors, codes, scales, y_debug, KQ_FORM_BUTTERFLY,
+                                            stream);
 }
 
 kq_status kq_transform_quantize_mxfp4_y16(const uint16_t *A, int64_t m, int64_t d, int64_t lda,

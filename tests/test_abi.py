@@ -51,6 +51,11 @@ GOOD = P(0x10000)  # never dereferenced: every case below fails before a launch
     ("kq_transform_quantize_mxfp4", (GOOD, 4, 64, 64, P(0x10008), GOOD, GOOD, None, None), kq.KQ_ERR_ALIGN),
     ("kq_transform_quantize_mxfp4", (GOOD, 4, 64, 64, GOOD, GOOD, GOOD, P(0x10004), None), kq.KQ_ERR_ALIGN),
     ("kq_transform_quantize_mxfp4", (GOOD, 4, 48, 64, GOOD, GOOD, GOOD, None, None), kq.KQ_ERR_SHAPE),
+    ("kq_transform_quantize_mxfp4_form", (GOOD, 4, 64, 64, GOOD, GOOD, GOOD, None, 3, None), kq.KQ_ERR_UNSUPPORTED),
+    ("kq_transform_quantize_mxfp4_form", (GOOD, 4, 64, 64, GOOD, GOOD, GOOD, None, -1, None), kq.KQ_ERR_UNSUPPORTED),
+    ("kq_transform_quantize_mxfp4_form", (GOOD, 4, 64, 64, None, GOOD, GOOD, None, 1, None), kq.KQ_ERR_NULL),
+    ("kq_transform_quantize_mxfp4_form", (GOOD, 4, 48, 64, GOOD, GOOD, GOOD, None, 2, None), kq.KQ_ERR_SHAPE),
+    ("kq_transform_quantize_mxfp4_form", (None, 0, 64, 64, None, None, None, None, 0, None), kq.KQ_OK),
     ("kq_smoothquant_quantize_mxfp4", (GOOD, 4, 64, 64, None, GOOD, GOOD, None), kq.KQ_ERR_NULL),
     ("kq_smoothquant_quantize_mxfp4", (GOOD, 4, 64, 64, P(0x10004), GOOD, GOOD, None), kq.KQ_ERR_ALIGN),
     ("kq_quantize_mxfp4_f32", (GOOD, 4, 64, 66, GOOD, GOOD, None), kq.KQ_ERR_ALIGN),

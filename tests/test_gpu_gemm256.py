@@ -157,6 +157,46 @@ def test_packed_gemm_lowrank_matches_oracle(torch_dev, kq, orc, m, n, k, r):
     assert np.all(np.abs(O.cpu().numpy().astype(np.float64) - ref) <= b)
 
 
+def launch_split(torch, m, n):
+    """(full-tile workgroups, half-tile pairs) of a packed GEMM launch: whole rounds of
+    256 x 256 tiles (one per compute unit), then the last partial round as halves when
+    it is at most half a round."""
+    tiles = ((m + 255) // 256) * ((n + 255) // 256)
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    rem = tiles % ncu
+    nfull = tiles - rem if (rem > 0 and 2 * rem <= ncu) else tiles
+    return nfull, tiles - nfull
+
+
+@pytest.mark.parametrize("m,n,k,r", [(6400, 3072, 512, 128), (6400, 3072, 512, 96), (4096, 2560, 256, 128)])
+def test_packed_gemm_lowrank_full_tiles_matches_oracle(torch_dev, kq, orc, m, n, k, r):
+    """The full-tile low-rank kernel on more than one round of tiles, every element
+    against the oracle's fp64 Eq. 11 (product plus Z deq(L)^T): 6400 x 3072 is 300
+    tiles, i.e. a round of 256 full tiles and 44 as half tiles; 4096 x 2560 is 160
+    tiles, all full. r = 96 leaves a partial last 64-wide chunk of the branch."""
+    torch = torch_dev
+    nfull, nhalf = launch_split(torch, m, n)
+    case("packed gemm lowrank full tiles %dx%dx%d r=%d (%d full, %d as halves)" % (m, n, k, r, nfull, nhalf))
+    assert nfull > 0
+    rng = np.random.default_rng(m + n + k + r + 1)
+    ca, sa, cw, sw = operands(rng, m, n, k)
+    cl = rng.integers(0, 256, (n, r // 2), dtype=np.uint8)
+    sl = rng.integers(120, 128, (n, r // 32), dtype=np.uint8)
+    Z = (rng.standard_normal((m, r)) * 3.0).astype(np.float32)
+    dca, dsa, dcw, dsw = (dev(torch, x) for x in (ca, sa, cw, sw))
+    O = kq.mxfp4_gemm_packed_lowrank(dca, kq.pack_mxfp4_scales(dsa), dcw, kq.pack_mxfp4_scales(dsw), dev(torch, Z),
+                                     dev(torch, cl), dev(torch, sl))
+    torch.cuda.synchronize()
+    Lq = orc.dequantize(cl, sl, r)
+    Z64 = Z.astype(np.float64)
+    ref = orc.gemm_dequant(ca, sa, cw, sw, k) + Z64 @ Lq.T
+    b = bound(orc, ca, sa, cw, sw, k) + (2.0 ** -15 + r * 2.0 ** -23) * (np.abs(Z64) @ np.abs(Lq).T) + \
+        2.0 ** -20 * np.abs(ref)
+    got = O.cpu().numpy().astype(np.float64)
+    bad = np.abs(got - ref) > b
+    assert not bad.any(), "%d elements outside the bound, first at %s" % (bad.sum(), np.argwhere(bad)[0])
+
+
 @pytest.mark.parametrize("m,n,k,pad,seed", [(1000, 700, 512, 0, 21), (300, 1100, 768, 3, 22), (257, 513, 256, 1, 23),
                                             (18432, 3072, 3072, 0, 24)])
 def test_packed_gemm_bf16_is_rounded_fp32(torch_dev, kq, m, n, k, pad, seed):

@@ -168,15 +168,14 @@ def test_gemm_lowrank_epilogue(torch_dev, kq, orc, m, n, k, r):
     assert np.allclose(O.cpu().numpy() - low, O0.cpu().numpy(), rtol=0, atol=1e-4 * np.abs(low).max())
 
 
-def test_lowrank_layer_flux(torch_dev, kq, orc):
+@pytest.fixture(scope="module")
+def flux_layer(torch_dev, kq, orc):
     """Eq. 11 on the FLUX 18432x3072 activations with the 3072x3072 weights and the
     workload's factors; L, R (rank 128) are the top singular pairs of W T^{-T},
-    computed offline on the host. GPU: fold, residual W~ - L R (fp32 GEMM),
-    quantize residual, L and R, fused transform + quantize with the bf16 output,
-    projection, GEMM with the low-rank epilogue. Checked against the oracle's layer
-    on sampled rows; the output error with and without the branch is reported."""
+    computed offline on the host. GPU side shared by both routes: fold, residual
+    W~ - L R (fp32 GEMM), MXFP4 of the residual, of L and of R, the fused transform
+    + quantize with the bf16 output. Oracle: the layer on 96 sampled rows."""
     torch = torch_dev
-    case("lowrank layer 18432x3072x3072 r=128")
     w = synth.workload("flux_18432x3072")
     W = synth.weights(3072, 3072, 1004)
     fac = w.factors
@@ -194,19 +193,60 @@ def test_lowrank_layer_flux(torch_dev, kq, orc):
     cr, sr = kq.quantize_mxfp4_f32(Rd)
     cl, sl = kq.quantize_mxfp4_f32(Ld)
     ca, sa, y16 = kq.transform_quantize_mxfp4_y16(A, facd)
-    Z = kq.lowrank_project(y16, cr, sr)
-    O = kq.mxfp4_gemm_lowrank(ca, sa, cw, sw, Z, cl, sl)
     cw0, sw0 = kq.quantize_mxfp4_f32(Wtd)
-    O0 = kq.mxfp4_gemm(ca, sa, cw0, sw0)
     torch.cuda.synchronize()
     rows = np.sort(np.random.default_rng(13).choice(w.m, 96, replace=False))
-    idx = torch.from_numpy(rows).cuda()
-    og = O.index_select(0, idx).cpu().numpy().astype(np.float64)
     ref, _ = lowrank.layer(w.A[rows], W, fac, L.astype(np.float64), R.astype(np.float64), orc)
-    rel = np.linalg.norm(og - ref) / np.linalg.norm(ref)
     exact = synth.bf16_bits_to_f32(w.A[rows]).astype(np.float64) @ W.astype(np.float64).T
-    e_lr = np.linalg.norm(og - exact)
-    e_plain = np.linalg.norm(O0.index_select(0, idx).cpu().numpy().astype(np.float64) - exact)
-    print("[lowrank] rel(gpu layer vs oracle) %.2e; |O - A W^T|: with the rank-%d branch %.2f, "
-          "without %.2f" % (rel, r, e_lr, e_plain), flush=True)
+    return dict(r=r, rows=rows, idx=torch.from_numpy(rows).cuda(), ref=ref, exact=exact, ca=ca, sa=sa, y16=y16,
+                cw=cw, sw=sw, cr=cr, sr=sr, cl=cl, sl=sl, cw0=cw0, sw0=sw0)
+
+
+def _report(torch, F, O, route):
+    og = O.index_select(0, F["idx"]).cpu().numpy().astype(np.float64)
+    rel = np.linalg.norm(og - F["ref"]) / np.linalg.norm(F["ref"])
+    print("[lowrank] %s: rel(gpu layer vs oracle) %.2e; |O - A W^T| with the rank-%d branch %.2f" % (
+        route, rel, F["r"], np.linalg.norm(og - F["exact"])), flush=True)
+    return rel
+
+
+def test_lowrank_layer_flux(torch_dev, kq, flux_layer):
+    """The check-GEMM route: projection with in-kernel decoding of R, then the
+    16x16x128-instruction GEMM with the low-rank epilogue."""
+    torch, F = torch_dev, flux_layer
+    case("lowrank layer 18432x3072x3072 r=128, check-GEMM route")
+    Z = kq.lowrank_project(F["y16"], F["cr"], F["sr"])
+    O = kq.mxfp4_gemm_lowrank(F["ca"], F["sa"], F["cw"], F["sw"], Z, F["cl"], F["sl"])
+    O0 = kq.mxfp4_gemm(F["ca"], F["sa"], F["cw0"], F["sw0"])
+    torch.cuda.synchronize()
+    rel = _report(torch, F, O, "check route")
+    e_plain = np.linalg.norm(O0.index_select(0, F["idx"]).cpu().numpy().astype(np.float64) - F["exact"])
+    print("[lowrank] |O - A W^T| without the branch %.2f" % e_plain, flush=True)
     assert rel <= 1e-3
+
+
+def test_lowrank_layer_flux_packed_route(torch_dev, kq, flux_layer):
+    """The route the layer timing measures: R decoded once to bf16, the projection on
+    bf16 R, the activation scales packed, and the packed-scale GEMM with the low-rank
+    epilogue (whole rounds of 256 x 256 tiles, then the last partial round as half
+    tiles). Sampled rows against the oracle's layer; every element against the check
+    route (the same sum in another order)."""
+    torch, F = torch_dev, flux_layer
+    case("lowrank layer 18432x3072x3072 r=128, packed route")
+    r16 = kq.dequantize_mxfp4_bf16(F["cr"], F["sr"])
+    Z = kq.lowrank_project_bf16(F["y16"], r16)
+    psa, psw = kq.pack_mxfp4_scales(F["sa"]), kq.pack_mxfp4_scales(F["sw"])
+    O = kq.mxfp4_gemm_packed_lowrank(F["ca"], psa, F["cw"], psw, Z, F["cl"], F["sl"])
+    Zc = kq.lowrank_project(F["y16"], F["cr"], F["sr"])
+    Oc = kq.mxfp4_gemm_lowrank(F["ca"], F["sa"], F["cw"], F["sw"], Zc, F["cl"], F["sl"])
+    torch.cuda.synchronize()
+    assert torch.equal(Z, Zc)
+    rel = _report(torch, F, O, "packed route")
+    assert rel <= 1e-3
+    # the two GEMMs differ only in fp32 rounding of partial sums: bound each output by
+    # the row's largest |term| sums (codes of A times the largest |W~| and |L| per k)
+    d = (O - Oc).abs()
+    scale = Oc.abs().amax(dim=1, keepdim=True) + 1.0
+    worst = float((d / scale).max())
+    print("[lowrank] packed vs check route: max |diff| / (row max + 1) %.3g" % worst, flush=True)
+    assert worst <= 1e-4

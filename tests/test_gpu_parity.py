@@ -102,11 +102,15 @@ def test_smoothquant_bit_exact(torch_dev, kq, orc, name):
 # fused Kronecker transform + quantize
 # ---------------------------------------------------------------------------
 
-@pytest.fixture(params=["butterfly", "mfma", "mfma_lds"])
-def form(request, monkeypatch):
-    """Transform form the library runs (read by libkq.so at every call)."""
-    monkeypatch.setenv("KQ_TRANSFORM_FORM", request.param)  # "butterfly" is the default form
+@pytest.fixture(params=["default", "butterfly", "mfma", "mfma_lds"])
+def form(request):
+    """Transform form of the fused calls (kq_transform_quantize_mxfp4_form); "default"
+    calls kq_transform_quantize_mxfp4 itself."""
     return request.param
+
+
+def fused(kq, A, fac, form, **kw):
+    return kq.transform_quantize_mxfp4(A, fac, form=None if form == "default" else form, **kw)
 
 
 @pytest.mark.parametrize("name", FULL + SAMPLED)
@@ -117,8 +121,8 @@ def test_fused_against_oracle(torch_dev, kq, orc, name, form):
     A = dev_bf16(torch, w.A)
     fac = torch.from_numpy(w.factors).cuda()
     y = torch.empty((w.m, w.d), dtype=torch.float32, device="cuda")
-    codes, scales = kq.transform_quantize_mxfp4(A, fac, y_debug=y)
-    codes_fast, scales_fast = kq.transform_quantize_mxfp4(A, fac)
+    codes, scales = fused(kq, A, fac, form, y_debug=y)
+    codes_fast, scales_fast = fused(kq, A, fac, form)
     torch.cuda.synchronize()
     # rule 4: fast mode writes the same bytes as check mode
     assert torch.equal(codes, codes_fast) and torch.equal(scales, scales_fast)
@@ -135,7 +139,7 @@ def test_fused_exact_factors_reduce_to_quantizer(torch_dev, kq, orc, kind, form)
     w = workload("pixart_attn_4096x1152")
     f = synth.special_factors(w.d // 32, kind)
     A = dev_bf16(torch, w.A)
-    codes, scales = kq.transform_quantize_mxfp4(A, torch.from_numpy(f).cuda())
+    codes, scales = fused(kq, A, torch.from_numpy(f).cuda(), form)
     torch.cuda.synchronize()
     c_ref, s_ref, _ = orc.transform_quantize(w.A, f, want_y=False)
     assert np.array_equal(scales.cpu().numpy(), s_ref)
@@ -158,8 +162,8 @@ def test_fused_segments_with_a_nonshear_block(torch_dev, kq, orc, form):
     for blk in (5, 21, 35):  # segments 0, 1 and the 4-block tail segment 2
         fac[blk, 1] = np.array([[0.0, 1.0], [1.0, 0.0]], np.float32)
     y = torch.empty((m, d), dtype=torch.float32, device="cuda")
-    codes, scales = kq.transform_quantize_mxfp4(dev_bf16(torch, A_full), torch.from_numpy(fac).cuda(), y_debug=y)
-    codes_fast, scales_fast = kq.transform_quantize_mxfp4(dev_bf16(torch, A_full), torch.from_numpy(fac).cuda())
+    codes, scales = fused(kq, dev_bf16(torch, A_full), torch.from_numpy(fac).cuda(), form, y_debug=y)
+    codes_fast, scales_fast = fused(kq, dev_bf16(torch, A_full), torch.from_numpy(fac).cuda(), form)
     assert torch.equal(codes, codes_fast) and torch.equal(scales, scales_fast)
     rep = parity.fused_report(orc, A_full, fac, codes.cpu().numpy(), scales.cpu().numpy(), y.cpu().numpy())
     print("[parity] non-shear blocks %s %s" % (form, rep), flush=True)
@@ -171,8 +175,7 @@ def test_fused_hadamard_worked_example(torch_dev, kq, orc, form):
     A = np.zeros((4, 64), np.uint16)
     A[:, 3] = synth.to_bf16_bits(np.array([80.0]))[0]
     A[1, 32 + 7] = synth.to_bf16_bits(np.array([-3.0]))[0]
-    codes, scales = kq.transform_quantize_mxfp4(dev_bf16(torch, A),
-                                                torch.from_numpy(synth.hadamard_factors(2)).cuda())
+    codes, scales = fused(kq, dev_bf16(torch, A), torch.from_numpy(synth.hadamard_factors(2)).cuda(), form)
     n = parity.unpack(codes.cpu().numpy())
     assert scales.cpu().numpy()[0, 0] == 128
     for c in range(32):
@@ -273,7 +276,7 @@ def test_ragged_shapes_and_padded_rows(torch_dev, kq, orc, m, d, pad, form):
     c_ref, s_ref = orc.smoothquant_quantize(A_full, inv, d=d)
     assert np.array_equal(codes.cpu().numpy(), c_ref) and np.array_equal(scales.cpu().numpy(), s_ref)
     y = torch.empty((m, d), dtype=torch.float32, device="cuda")
-    codes, scales = kq.transform_quantize_mxfp4(A, torch.from_numpy(fac).cuda(), y_debug=y)
+    codes, scales = fused(kq, A, torch.from_numpy(fac).cuda(), form, y_debug=y)
     parity.fused_report(orc, np.ascontiguousarray(A_full[:, :d]), fac, codes.cpu().numpy(),
                         scales.cpu().numpy(), y.cpu().numpy())
 
@@ -292,10 +295,10 @@ def test_guard_bytes_determinism_and_side_stream(torch_dev, kq, form):
     scales = sbuf[: m * d // 32].view(m, d // 32)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        kq.transform_quantize_mxfp4(A, fac, codes=codes, scales=scales, stream=s)
+        fused(kq, A, fac, form, codes=codes, scales=scales, stream=s)
     s.synchronize()
     assert bool((cbuf[m * d // 2:] == 0xA5).all()) and bool((sbuf[m * d // 32:] == 0x5A).all())
-    c2, s2 = kq.transform_quantize_mxfp4(A, fac)
+    c2, s2 = fused(kq, A, fac, form)
     torch.cuda.synchronize()
     assert torch.equal(c2, codes) and torch.equal(s2, scales)
 
@@ -314,9 +317,73 @@ def test_fused_tiny_and_mixed_magnitudes(torch_dev, kq, orc, form):
     A = synth.to_bf16_bits(X)
     fac = synth.lu_perturbed_factors(d // 32, 77)
     y = torch.empty((m, d), dtype=torch.float32, device="cuda")
-    codes, scales = kq.transform_quantize_mxfp4(dev_bf16(torch, A), torch.from_numpy(fac).cuda(), y_debug=y)
+    codes, scales = fused(kq, dev_bf16(torch, A), torch.from_numpy(fac).cuda(), form, y_debug=y)
     rep = parity.fused_report(orc, A, fac, codes.cpu().numpy(), scales.cpu().numpy(), y.cpu().numpy())
     print("[parity] tiny %s %s" % (form, rep), flush=True)
+
+
+def shear_growth(fac):
+    """Per block and factor, max(|G01 / G11|, |G10 / G00|): the ratios of the fused
+    entry point's fp32 shear stages, which set its range condition."""
+    g = fac.astype(np.float64)
+    return np.maximum(np.abs(g[:, :, 0, 1] / g[:, :, 1, 1]), np.abs(g[:, :, 1, 0] / g[:, :, 0, 0]))
+
+
+@pytest.mark.parametrize("kind", ["hadamard", "lu"])
+def test_fused_top_of_range(torch_dev, kq, orc, kind, form):
+    """Blocks near the top of the exponent range, inside the fused entry point's
+    stated range condition (max|a| prod_k (1 + r_k) < 2^128, r_k the shear ratios):
+    dense blocks scaled to just inside it, and blocks of one nonzero element, whose
+    stages grow it only by prod_k max(1, r_k), up to the largest finite bf16 (for
+    Hadamard factors that is y = 2^125.5, scale byte 250). Checked by the same rules
+    as every fused run."""
+    torch = torch_dev
+    case("fused top of range %s form=%s" % (kind, form))
+    rng = np.random.default_rng(31 if kind == "hadamard" else 32)
+    m, d = 64, 512
+    nblk = d // 32
+    fac = synth.hadamard_factors(nblk) if kind == "hadamard" else synth.lu_perturbed_factors(nblk, 33)
+    r = shear_growth(fac)
+    dense = np.log2(np.prod(1.0 + r, axis=1))           # [nblk]
+    spike = np.log2(np.prod(np.maximum(1.0, r), axis=1))
+    X = np.zeros((m, d))
+    z = np.clip(rng.standard_normal((32, d)), -4.0, 4.0)
+    e = np.floor(126.5 - 2.0 - dense)[None, :] - rng.integers(0, 4, (32, nblk))
+    X[:32] = z * np.repeat(2.0 ** e, 32, axis=1)
+    for i in range(32, m):
+        for b in range(nblk):
+            lim = min(127.99, 127.9 - spike[b])
+            X[i, 32 * b + (i * 7 + b) % 32] = (-1) ** (i + b) * 2.0 ** (lim - rng.uniform(0, 2) * (i % 2))
+    A = synth.to_bf16_bits(X)
+    y = torch.empty((m, d), dtype=torch.float32, device="cuda")
+    codes, scales = fused(kq, dev_bf16(torch, A), torch.from_numpy(fac).cuda(), form, y_debug=y)
+    torch.cuda.synchronize()
+    rep = parity.fused_report(orc, A, fac, codes.cpu().numpy(), scales.cpu().numpy(), y.cpu().numpy())
+    top_byte = int(scales.cpu().numpy().max())
+    print("[parity] top of range %s %s: largest scale byte %d, %s" % (kind, form, top_byte, rep), flush=True)
+    assert top_byte >= (250 if kind == "hadamard" else 245)
+
+
+def test_smoothquant_top_of_range(torch_dev, kq, orc):
+    """SmoothQuant with inputs up to the largest finite bf16 and per-channel factors in
+    [1/2, 1]: every product is finite, scale bytes reach 254 (e = 127); bit-exact."""
+    torch = torch_dev
+    case("smoothquant top of range")
+    rng = np.random.default_rng(34)
+    m, d = 256, 256
+    X = rng.uniform(-1.0, 1.0, (m, d)) * 2.0 ** rng.integers(100, 128, (m, 1))
+    X = np.clip(X, -3.3e38, 3.3e38)
+    A = synth.to_bf16_bits(X)
+    A[0, :] = 0x7F7F  # the largest finite bf16, 2^127 (2 - 2^-7)
+    A[1, 1::2] = 0xFF7F
+    inv = rng.uniform(0.5, 1.0, d).astype(np.float32)
+    inv[:8] = 1.0
+    codes, scales = kq.smoothquant_quantize_mxfp4(dev_bf16(torch, A), torch.from_numpy(inv).cuda())
+    torch.cuda.synchronize()
+    c_ref, s_ref = orc.smoothquant_quantize(A, inv)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert int(s_ref.max()) == 254
 
 
 @pytest.mark.parametrize("kind", ["fused", "smoothquant", "quantize"])
