@@ -52,14 +52,15 @@ __device__ __forceinline__ void flat_coords(const Geom &g, int &j, int &sub, int
 enum YOut { kYNone = 0, kYF32 = 1, kYBF16 = 2 };
 
 // Row-wave strips (see the file header). Workgroup b takes segment b % nseg
-// (blocks 16 seg .. 16 seg + 15) and rows NW iters (b / nseg) + w + NW k for
-// its waves w and k < iters. The last segment of a row may be partial (nblk %
-// 16 != 0): each buffer resource's record count is the valid bytes from the
-// segment start to the end of the row's d channels, so lanes past the last
-// block read zeros and their stores are dropped by the hardware range check.
+// (blocks 16 seg .. 16 seg + 15) and rows NW U (b / nseg) + w + NW u for its
+// waves w and u < U: each wave issues its U row loads at once and handles
+// them as one group. The last segment of a row may be partial (nblk % 16 !=
+// 0): each buffer resource's record count is the valid bytes from the segment
+// start to the end of the row's d channels, so lanes past the last block read
+// zeros and their stores are dropped by the hardware range check.
 struct RGeom {
     int64_t m, lda, d;  // elements
-    int nblk, nseg, iters;
+    int nblk, nseg;
 };
 
 // Buffer resource over `bytes` bytes from `base` (raw addressing, no stride).
@@ -74,12 +75,19 @@ struct RowOut {
     uint32_t codes_bytes, scales_bytes, y_bytes;
 };
 
+// Per-lane byte offsets of a row's stores, computed once (kept in registers
+// rather than recomputed per row).
+struct LaneOff {
+    uint32_t y32, y16, code, scale;
+    bool scale_lane;  // lane 0 of its quad
+};
+
 // Quantize the quad-held fp32 block and store codes, scale and y as YOUT asks.
 template <int YOUT>
-__device__ __forceinline__ void store_row(const float y[8], RowOut &o, int lane) {
+__device__ __forceinline__ void store_row(const float y[8], RowOut &o, const LaneOff &lo) {
     if (YOUT == kYF32) {
         const auto r = buf_rsrc(o.y, o.y_bytes);
-        const uint32_t off = (uint32_t)lane * 32;
+        const uint32_t off = lo.y32;
         __builtin_amdgcn_raw_buffer_store_b128(
             (u32x4_t){__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])}, r,
             off, 0, 0);
@@ -91,14 +99,15 @@ __device__ __forceinline__ void store_row(const float y[8], RowOut &o, int lane)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             w[i] = (uint32_t)bf16_rne_bits(y[2 * i]) | ((uint32_t)bf16_rne_bits(y[2 * i + 1]) << 16);
-        __builtin_amdgcn_raw_buffer_store_b128(w, buf_rsrc(o.y, o.y_bytes), (uint32_t)lane * 16, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(w, buf_rsrc(o.y, o.y_bytes), lo.y16, 0, 0);
     }
     uint32_t sbyte;
     const uint32_t packed = quantize_quad_f32(y, sbyte);
-    __builtin_amdgcn_raw_buffer_store_b32(packed, buf_rsrc(o.codes, o.codes_bytes), (uint32_t)lane * 4, 0, 0);
-    if ((lane & 3) == 0)
-        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, buf_rsrc(o.scales, o.scales_bytes), (uint32_t)lane >> 2,
-                                             0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(packed, buf_rsrc(o.codes, o.codes_bytes), lo.code, 0, 0);
+    // one lane per quad stores the block's scale byte (four lanes storing the
+    // same byte measured slower)
+    if (lo.scale_lane)
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, buf_rsrc(o.scales, o.scales_bytes), lo.scale, 0, 0);
     o.codes += o.codes_step;
     o.scales += o.scales_step;
     o.y += o.y_step;
@@ -201,8 +210,8 @@ __device__ __forceinline__ void apply_coefs(float y[8], const float c[16]) {
 }
 
 // bf16 input, row-wave strips: SmoothQuant (T = diag(inv_scale)) or the
-// Kronecker transform. U rows' loads are issued at once; for the transform the
-// first U rows' loads are in flight while wave 0 derives the segment's
+// Kronecker transform. Each wave's U row loads are issued at once; for the
+// transform they are in flight while wave 0 derives the segment's
 // coefficients (factor loads, reciprocals, LDS writes, barrier).
 template <int MODE, int YOUT, int NW, int U>
 __global__ __launch_bounds__(NW * 64) void rowwave_kernel(const uint16_t *__restrict__ A, RGeom g,
@@ -214,18 +223,20 @@ __global__ __launch_bounds__(NW * 64) void rowwave_kernel(const uint16_t *__rest
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane & 3;
     const int seg = (int)(blockIdx.x % (unsigned)g.nseg);
-    const int64_t row0 = (int64_t)(blockIdx.x / (unsigned)g.nseg) * NW * g.iters + wave;
+    const int64_t row0 = (int64_t)(blockIdx.x / (unsigned)g.nseg) * NW * U + wave;
     const int j = seg * 16 + (lane >> 2);
     const bool active = j < g.nblk;
     const int64_t c_seg = (int64_t)seg * 512;  // first channel of the segment
-    // rows of this wave: row0 + NW k for k < nr
+    // rows of this wave: row0 + NW u for u < nr
     const int64_t left = row0 < g.m ? (g.m - row0 + NW - 1) / NW : 0;
-    const int nr = (int)(left < g.iters ? left : g.iters);
+    const int nr = (int)(left < U ? left : U);
 
     const char *a_row = reinterpret_cast<const char *>(A + row0 * g.lda + c_seg);
     const int64_t a_step = (int64_t)NW * g.lda * 2;
     const uint32_t a_bytes = (uint32_t)((g.d - c_seg) * 2);
     const uint32_t a_off = (uint32_t)lane * 16;
+    LaneOff lo{(uint32_t)lane * 32, (uint32_t)lane * 16, (uint32_t)lane * 4, (uint32_t)lane >> 2, (lane & 3) == 0};
+    asm volatile("" : "+v"(lo.y32), "+v"(lo.code), "+v"(lo.scale));  // opaque: not rematerialized per row
     RowOut o;
     o.codes = reinterpret_cast<char *>(codes + row0 * (g.d / 2) + c_seg / 2);
     o.scales = reinterpret_cast<char *>(scales + row0 * g.nblk + seg * 16);
@@ -238,45 +249,34 @@ __global__ __launch_bounds__(NW * 64) void rowwave_kernel(const uint16_t *__rest
     o.y_step = (int64_t)NW * g.d * ysize;
     o.y_bytes = (uint32_t)((g.d - c_seg) * ysize);
 
-    // Every load of a group is issued; a row past the wave's last one gets a
-    // buffer of zero records, so it reads zeros without touching memory (and
-    // the compiler's wait counts stay exact).
+    // Every load is issued; a row past the wave's last one gets a buffer of
+    // zero records, so it reads zeros without touching memory (and the
+    // compiler's wait counts stay exact).
     uint4 q[U];
-    auto load_group = [&](int k0) {
-        const char *p = a_row + (int64_t)k0 * a_step;
+    auto load_rows = [&]() {
+        const char *p = a_row;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const u32x4_t v =
-                __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(p, k0 + u < nr ? a_bytes : 0u), a_off, 0, 2);
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(p, u < nr ? a_bytes : 0u), a_off, 0, 2);
             q[u] = make_uint4(v[0], v[1], v[2], v[3]);
             p += a_step;
         }
     };
-    // A group consumes all of its loads at once, before its first store:
-    // stores count in the same vector-memory counter as loads, so a wait for
-    // row u > 1 issued after the stores of earlier rows would also wait for
-    // those stores to be acknowledged. The empty asm statement reads every
-    // loaded register of the group, so the compiler places one wait for all of
-    // them before it and none inside the group. The first group is peeled off
-    // the row loop; with 4 rows per wave it is the only one.
-    auto group = [&](int k, auto per_row) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) asm volatile("" : "+v"(q[u].x), "+v"(q[u].y), "+v"(q[u].z), "+v"(q[u].w));
+    // All rows' loads are waited for at once, before the first store: stores
+    // count in the same vector-memory counter as loads, so a wait for row u > 1
+    // issued after the stores of earlier rows would also wait for those stores
+    // to be acknowledged. One s_waitcnt vmcnt(0) (encoding: vmcnt 0, expcnt and
+    // lgkmcnt left at their maxima) ahead of the stores; the compiler's own
+    // per-row waits after it are then already satisfied.
+    auto rows = [&](auto per_row) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (k + u >= nr) break;
+            if (u >= nr) break;
             float y[8];
             widen8(q[u], y);
             per_row(y);
-            store_row<YOUT>(y, o, lane);
-        }
-    };
-    auto rows = [&](auto per_row, bool preloaded) {
-        if (!preloaded) load_group(0);
-        group(0, per_row);
-        for (int k = U; k < nr; k += U) {
-            load_group(k);
-            group(k, per_row);
+            store_row<YOUT>(y, o, lo);
         }
     };
     if (MODE == kSmooth) {
@@ -285,23 +285,24 @@ __global__ __launch_bounds__(NW * 64) void rowwave_kernel(const uint16_t *__rest
         const float4 hi = active ? *reinterpret_cast<const float4 *>(params + j * 32 + sub * 8 + 4) : make_float4(0, 0, 0, 0);
         sq[0] = lo.x; sq[1] = lo.y; sq[2] = lo.z; sq[3] = lo.w;
         sq[4] = hi.x; sq[5] = hi.y; sq[6] = hi.z; sq[7] = hi.w;
+        load_rows();
         rows([&](float y[8]) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) y[i] = y[i] * sq[i];
-        }, false);
+        });
         return;
     }
 
     // Kronecker transform: wave 0 (one lane per block and channel group)
     // derives the coefficients; a ballot picks one form for the workgroup, so
-    // the branch below is uniform and the row loop carries no divergence. Wave
-    // 0 issues its factor loads before its row loads, so waiting for the
+    // the branch below is uniform and the rows carry no divergence. Wave 0
+    // issues its factor loads before its row loads, so waiting for the
     // factors leaves the rows in flight.
     __shared__ float coef[64][17];
     __shared__ int all_shear;
     float f[20];
     if (wave == 0 && active) load_factors20(params + (int64_t)j * 20, f);
-    load_group(0);
+    load_rows();
     if (wave == 0) {
         SetupLane S;
         if (active) setup_ratios(f, S);
@@ -321,9 +322,9 @@ __global__ __launch_bounds__(NW * 64) void rowwave_kernel(const uint16_t *__rest
 #pragma unroll
     for (int i = 0; i < 16; ++i) c[i] = coef[lane][i];
     if (__builtin_amdgcn_readfirstlane(all_shear)) {
-        rows([&](float y[8]) { apply_coefs<true>(y, c); }, true);
+        rows([&](float y[8]) { apply_coefs<true>(y, c); });
     } else {
-        rows([&](float y[8]) { apply_coefs<false>(y, c); }, true);
+        rows([&](float y[8]) { apply_coefs<false>(y, c); });
     }
 }
 
@@ -589,8 +590,8 @@ bool make_mgeom(int64_t m, int64_t d, int64_t lda, int nb, int unroll, kq::MGeom
 }
 
 // Row-wave geometry: 16-block segments (the last one partial when nblk % 16 !=
-// 0), workgroups of NW waves on NW consecutive rows, `iters` row groups each.
-bool make_rgeom(int64_t m, int64_t d, int64_t lda, int nw, int iters, kq::RGeom &g, unsigned &nwg) {
+// 0), workgroups of NW waves with U rows each (NW U consecutive rows).
+bool make_rgeom(int64_t m, int64_t d, int64_t lda, int nw, int u, kq::RGeom &g, unsigned &nwg) {
     // buffer records and offsets are 32-bit: a row's bytes (fp32 y in check
     // mode: 4 d) must fit
     if (d > ((int64_t)1 << 29)) return false;
@@ -599,8 +600,7 @@ bool make_rgeom(int64_t m, int64_t d, int64_t lda, int nw, int iters, kq::RGeom 
     g.lda = lda;
     g.nblk = (int)(d / 32);
     g.nseg = (g.nblk + 15) / 16;
-    g.iters = iters;
-    const int64_t slabs = (m + (int64_t)nw * iters - 1) / ((int64_t)nw * iters);
+    const int64_t slabs = (m + (int64_t)nw * u - 1) / ((int64_t)nw * u);
     const int64_t total = slabs * g.nseg;
     if (total > 0x7FFFFFFF) return false;
     nwg = (unsigned)total;
