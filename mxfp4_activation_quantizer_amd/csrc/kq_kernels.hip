@@ -265,11 +265,13 @@ __global__ __launch_bounds__(NW * 64) void rowwave_kernel(const uint16_t *__rest
     // All rows' loads are waited for at once, before the first store: stores
     // count in the same vector-memory counter as loads, so a wait for row u > 1
     // issued after the stores of earlier rows would also wait for those stores
-    // to be acknowledged. One s_waitcnt vmcnt(0) (encoding: vmcnt 0, expcnt and
-    // lgkmcnt left at their maxima) ahead of the stores; the compiler's own
-    // per-row waits after it are then already satisfied.
+    // to be acknowledged. An empty asm statement that reads one register of
+    // every row's load makes the compiler wait for all of them at that point
+    // (an input, not an output, so no register copies), and the loads cannot
+    // be moved past it.
     auto rows = [&](auto per_row) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);
+#pragma unroll
+        for (int u = 0; u < U; ++u) asm volatile("" ::"v"(q[u].x));
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (u >= nr) break;
