@@ -141,39 +141,52 @@ def time_kernel(torch, kq, kind, sets, steps, warmup):
     return wall_ms, per
 
 
-def time_step_graphs(torch, kq, kind, sets, steps, warmup):
-    """Wall time per step with each step replayed as one captured HIP graph.
+class StepGraphs:
+    """One captured HIP graph per rotation index r: the step's launches (one per
+    tensor of the workload) on buffer set r, replayed in turn so the rotation
+    past the Infinity Cache is kept."""
 
-    One graph per rotation index r (the step's launches on buffer set r of every
-    tensor), replayed in turn, so the rotation past the Infinity Cache is kept.
-    Returns ms per step (synchronize on both sides of the timed replays).
-    """
-    nrot = 1
-    for s in sets:
-        nrot = nrot * s.n // math.gcd(nrot, s.n)
-    graphs = []
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):  # one eager pass on the capture stream first
+    def __init__(self, torch, kq, kind, sets):
+        self.torch = torch
+        nrot = 1
+        for s in sets:
+            nrot = nrot * s.n // math.gcd(nrot, s.n)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # one eager pass on the capture stream first
+            for r in range(nrot):
+                for s in sets:
+                    run_kernel(kq, kind, s, side, k=r)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graphs = []
         for r in range(nrot):
-            for s in sets:
-                run_kernel(kq, kind, s, side, k=r)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    for r in range(nrot):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for s in sets:
-                run_kernel(kq, kind, s, torch.cuda.current_stream(), k=r)
-        graphs.append(g)
-    for i in range(warmup):
-        graphs[i % nrot].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % nrot].replay()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for s in sets:
+                    run_kernel(kq, kind, s, torch.cuda.current_stream(), k=r)
+            self.graphs.append(g)
+        self.i = 0
+
+    def replay(self, n):
+        for _ in range(n):
+            self.graphs[self.i % len(self.graphs)].replay()
+            self.i += 1
+
+    def time(self, steps, warmup):
+        """W untimed replays, then exactly `steps` timed ones bracketed by
+        synchronize; returns ms per step."""
+        self.replay(warmup)
+        self.torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        self.replay(steps)
+        self.torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_step_graphs(torch, kq, kind, sets, steps, warmup):
+    """Wall time per step with each step replayed as one captured HIP graph."""
+    return StepGraphs(torch, kq, kind, sets).time(steps, warmup)
 
 
 def _events_us(torch, fn, reps, warmup):
@@ -197,6 +210,8 @@ def extras(torch, kq, synth, flux_sets, reps=100, warmup=20):
     the weight fold and fp32 quantizer on 3072 x 3072 weights, and the W4A4 GEMM."""
     out = {"other_configs": {}}
     out["kernel_table_pow2"] = kernel_table(torch, kq, synth, reps, warmup)
+    out["production_shapes_table4"] = production_table(torch, kq, synth, reps, warmup)
+    out["m_sweep_d4096_fig4"] = m_sweep(torch, kq, synth, reps, warmup)
     for name in ("pixart_attn_4096x1152", "pixart_ffn_8192x4608"):
         w = synth.workload(name)
         s = Sets(torch, w)
@@ -345,21 +360,52 @@ def kernel_table(torch, kq, synth, reps, warmup):
     quantize-only (Q4), SmoothQuant (Scale), the fused Kronecker kernel (K2),
     block Hadamard-32 and the full-width Walsh-Hadamard transform (FWHT), each
     fused with the MXFP4 quantizer, at the table's power-of-two shapes."""
+    names = ("pow2_4096x1024", "pow2_4096x4096", "pow2_4096x16384", "pow2_512x4096", "pow2_512x16384")
+    return shape_table(torch, kq, synth, names, ("quantize", "smoothquant", "fused", "hadamard32", "fwht"), reps,
+                       warmup)
+
+
+def shape_table(torch, kq, synth, names, kinds, reps, warmup, m_override=None):
+    """Per-shape medians of each kind (same rotation rules), plus SmoothQuant over
+    fused and FWHT over fused where both were timed."""
     table = {}
-    for name in ("pow2_4096x1024", "pow2_4096x4096", "pow2_4096x16384", "pow2_512x4096",
-                 "pow2_512x16384"):
-        w = synth.workload(name)
+    for name in names:
+        w = synth.workload(name, m=m_override)
         s = Sets(torch, w)
         per = {}
-        for kind in ("quantize", "smoothquant", "fused", "hadamard32", "fwht"):
+        for kind in kinds:
+            if kind == "fwht" and (w.d & (w.d - 1)) != 0:
+                continue
             _, d = time_kernel(torch, kq, kind, [s], reps, warmup)
             per[kind] = summarize(d[0], s)
-        per["scale_over_fused"] = round(per["smoothquant"]["median_us"] / per["fused"]["median_us"], 3)
-        per["fwht_over_fused"] = round(per["fwht"]["median_us"] / per["fused"]["median_us"], 3)
-        table[name] = per
-        log("%s: %s" % (name, {k: (v["median_us"] if isinstance(v, dict) else v) for k, v in per.items()}))
+        if "smoothquant" in per and "fused" in per:
+            per["scale_over_fused"] = round(per["smoothquant"]["median_us"] / per["fused"]["median_us"], 3)
+        if "fwht" in per and "fused" in per:
+            per["fwht_over_fused"] = round(per["fwht"]["median_us"] / per["fused"]["median_us"], 3)
+        key = name if m_override is None else "m%d_d%d" % (w.m, w.d)
+        table[key] = per
+        log("%s: %s" % (key, {k: (v["median_us"] if isinstance(v, dict) else v) for k, v in per.items()}))
         del s
     return table
+
+
+def production_table(torch, kq, synth, reps, warmup):
+    """The paper's production-shape latency table (Appendix A, Table 4) on this GPU:
+    quantize-only (Q4), SmoothQuant (Scale) and the fused Kronecker kernel at the
+    FLUX.1 / PixArt-Sigma linear-layer shapes it lists."""
+    names = ("prod_512x3072", "prod_512x12288", "pixart_attn_4096x1152", "prod_4096x3072", "prod_4096x3456",
+             "pow2_4096x4096", "prod_4096x4608", "prod_4096x12288")
+    return shape_table(torch, kq, synth, names, ("quantize", "smoothquant", "fused"), reps, warmup)
+
+
+def m_sweep(torch, kq, synth, reps, warmup):
+    """Latency against the token count m at d = 4096 (the paper's Sec. 4.4, Fig. 4):
+    m = 2^7 .. 2^14, quantize-only, SmoothQuant, fused and the full-width FWHT."""
+    out = {}
+    for lg in range(7, 15):
+        out.update(shape_table(torch, kq, synth, ("pow2_4096x4096",), ("quantize", "smoothquant", "fused", "fwht"),
+                               reps, warmup, m_override=1 << lg))
+    return out
 
 
 def summarize(d_us, s: Sets):
@@ -513,6 +559,18 @@ def main():
     sets = [Sets(torch, w) for w in ws]
     log("buffer sets per tensor: %s" % [s.n for s in sets])
     kinds = [args.only] if args.only else ["fused", "smoothquant", "quantize"]
+    # Process warm-up, outside every timed region: the first graph replays and
+    # launches of a process pay one-time costs (and a cold clock) that a timed
+    # region must not include; every kind's step runs here a few times.
+    graphs = {}
+    for kind in kinds:
+        if not args.eager:
+            graphs[kind] = StepGraphs(torch, kq, kind, sets)
+            graphs[kind].replay(20)
+        for _ in range(10):
+            for s in sets:
+                run_kernel(kq, kind, s, torch.cuda.current_stream())
+    torch.cuda.synchronize()
     res = {}
     for kind in kinds:
         log("timing %s: %d warmup + %d steps, eager launches with HIP events" % (kind, args.warmup, args.steps))
@@ -520,11 +578,22 @@ def main():
         wall_ms = eager_ms
         if not args.eager:
             log("timing %s: %d warmup + %d steps, one HIP graph per step" % (kind, args.warmup, args.steps))
-            wall_ms = time_step_graphs(torch, kq, kind, sets, args.steps, args.warmup)
+            wall_ms = graphs[kind].time(args.steps, args.warmup)
         res[kind] = {"wall_ms_per_step": wall_ms, "eager_ms_per_step": eager_ms,
                      "per_tensor": [summarize(d, s) for d, s in zip(per, sets)],
                      "per_tensor_mean_us": [float(d.mean()) for d in per]}
         log("%s: %.4f ms/step (eager %.4f); %s" % (kind, wall_ms, eager_ms, res[kind]["per_tensor"]))
+    # fused against SmoothQuant on the same inputs: alternating blocks of the same
+    # K graph-replayed steps (neither kernel always runs first or warmer)
+    cmp = None
+    if not args.eager and "fused" in kinds and "smoothquant" in kinds:
+        blocks = {"fused": [], "smoothquant": []}
+        for _ in range(3):
+            for kind in ("fused", "smoothquant"):
+                blocks[kind].append(graphs[kind].time(args.steps, args.warmup))
+        cmp = {k: [round(x, 5) for x in v] for k, v in blocks.items()}
+        cmp["speedup"] = round(float(np.median(blocks["smoothquant"]) / np.median(blocks["fused"])), 4)
+        log("fused vs smoothquant, alternating blocks of %d steps: %s" % (args.steps, cmp))
     head = res[kinds[0]]
     step_bytes = sum(s.bytes for s in sets)
     step_elems = sum(s.elems for s in sets)
@@ -561,7 +630,10 @@ def main():
                      "kernel": "%s on %dx%d" % (KERNEL_NAMES[kinds[0]], sets[big].m, sets[big].d)},
         "kernels": {k: v["per_tensor"] for k, v in res.items()},
     }
-    if "fused" in res and "smoothquant" in res:
+    if cmp is not None:
+        out["fused_vs_smoothquant_speedup"] = cmp["speedup"]
+        out["fused_vs_smoothquant_blocks_ms"] = {k: cmp[k] for k in ("fused", "smoothquant")}
+    elif "fused" in res and "smoothquant" in res:
         out["fused_vs_smoothquant_speedup"] = round(
             res["smoothquant"]["wall_ms_per_step"] / res["fused"]["wall_ms_per_step"], 3)
     if not args.only and not args.no_extras:

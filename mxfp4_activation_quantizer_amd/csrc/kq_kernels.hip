@@ -82,32 +82,62 @@ struct LaneOff {
     bool scale_lane;  // lane 0 of its quad
 };
 
-// Quantize the quad-held fp32 block and store codes, scale and y as YOUT asks.
+// widen8 as one asm statement (the same eight shifts and masks): reading the
+// load's registers makes the compiler wait for that load right there, and the
+// dependence on `after` (a previous row's result) keeps the statement, and so
+// the wait, after that row's work.
+__device__ __forceinline__ void widen8_ordered(const uint4 &q, float x[8], uint32_t after) {
+    asm volatile(
+        "v_lshlrev_b32 %0, 16, %8\n\t"
+        "v_and_b32 %1, 0xffff0000, %8\n\t"
+        "v_lshlrev_b32 %2, 16, %9\n\t"
+        "v_and_b32 %3, 0xffff0000, %9\n\t"
+        "v_lshlrev_b32 %4, 16, %10\n\t"
+        "v_and_b32 %5, 0xffff0000, %10\n\t"
+        "v_lshlrev_b32 %6, 16, %11\n\t"
+        "v_and_b32 %7, 0xffff0000, %11"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
+        : "v"(q.x), "v"(q.y), "v"(q.z), "v"(q.w), "v"(after));
+}
+
+// One row's results as a lane holds them until the stores: codes dword, scale
+// byte and, as YOUT asks, y (fp32) or y rounded to bf16 (four packed dwords).
 template <int YOUT>
-__device__ __forceinline__ void store_row(const float y[8], RowOut &o, const LaneOff &lo) {
+struct RowRes {
+    uint32_t packed, sbyte;
+    uint32_t y[YOUT == kYF32 ? 8 : (YOUT == kYBF16 ? 4 : 1)];
+};
+
+// Quantize the quad-held fp32 block (and keep y as YOUT asks).
+template <int YOUT>
+__device__ __forceinline__ void finish_row(const float y[8], RowRes<YOUT> &r) {
     if (YOUT == kYF32) {
-        const auto r = buf_rsrc(o.y, o.y_bytes);
-        const uint32_t off = lo.y32;
-        __builtin_amdgcn_raw_buffer_store_b128(
-            (u32x4_t){__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])}, r,
-            off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(
-            (u32x4_t){__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]), __float_as_uint(y[7])}, r,
-            off + 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r.y[i] = __float_as_uint(y[i]);
     } else if (YOUT == kYBF16) {
-        u32x4_t w;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            w[i] = (uint32_t)bf16_rne_bits(y[2 * i]) | ((uint32_t)bf16_rne_bits(y[2 * i + 1]) << 16);
-        __builtin_amdgcn_raw_buffer_store_b128(w, buf_rsrc(o.y, o.y_bytes), lo.y16, 0, 0);
+            r.y[i] = (uint32_t)bf16_rne_bits(y[2 * i]) | ((uint32_t)bf16_rne_bits(y[2 * i + 1]) << 16);
     }
-    uint32_t sbyte;
-    const uint32_t packed = quantize_quad_f32(y, sbyte);
-    __builtin_amdgcn_raw_buffer_store_b32(packed, buf_rsrc(o.codes, o.codes_bytes), lo.code, 0, 0);
+    r.packed = quantize_quad_f32(y, r.sbyte);
+}
+
+// Store one row's results and advance the output pointers by NW rows.
+template <int YOUT>
+__device__ __forceinline__ void store_row(const RowRes<YOUT> &r, RowOut &o, const LaneOff &lo) {
+    if (YOUT == kYF32) {
+        const auto d = buf_rsrc(o.y, o.y_bytes);
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4_t){r.y[0], r.y[1], r.y[2], r.y[3]}, d, lo.y32, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4_t){r.y[4], r.y[5], r.y[6], r.y[7]}, d, lo.y32 + 16, 0, 0);
+    } else if (YOUT == kYBF16) {
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4_t){r.y[0], r.y[1], r.y[2], r.y[3]}, buf_rsrc(o.y, o.y_bytes),
+                                               lo.y16, 0, 0);
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(r.packed, buf_rsrc(o.codes, o.codes_bytes), lo.code, 0, 0);
     // one lane per quad stores the block's scale byte (four lanes storing the
     // same byte measured slower)
     if (lo.scale_lane)
-        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, buf_rsrc(o.scales, o.scales_bytes), lo.scale, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)r.sbyte, buf_rsrc(o.scales, o.scales_bytes), lo.scale, 0, 0);
     o.codes += o.codes_step;
     o.scales += o.scales_step;
     o.y += o.y_step;
@@ -262,23 +292,31 @@ __global__ __launch_bounds__(NW * 64) void rowwave_kernel(const uint16_t *__rest
             p += a_step;
         }
     };
-    // All rows' loads are waited for at once, before the first store: stores
-    // count in the same vector-memory counter as loads, so a wait for row u > 1
-    // issued after the stores of earlier rows would also wait for those stores
-    // to be acknowledged. An empty asm statement that reads one register of
-    // every row's load makes the compiler wait for all of them at that point
-    // (an input, not an output, so no register copies), and the loads cannot
-    // be moved past it.
+    // Each row is transformed and quantized as soon as its load is back, and
+    // every store waits until all rows are done: stores count in the same
+    // vector-memory counter as loads, so a wait for a later row's load issued
+    // after earlier rows' stores would also wait for those stores to be
+    // acknowledged. Row u is widened by widen8_ordered, which reads the load's
+    // registers (so the compiler waits for exactly that load there) and takes
+    // row u-1's codes dword as an operand (so neither the widening nor its wait
+    // is hoisted above row u-1's work, nor merged across the two forms of the
+    // transform). Rows past the wave's last one hold zeros; they are computed
+    // (no branch) but not stored.
     auto rows = [&](auto per_row) {
+        RowRes<YOUT> res[U];
+        uint32_t chain = 0;
 #pragma unroll
-        for (int u = 0; u < U; ++u) asm volatile("" ::"v"(q[u].x));
+        for (int u = 0; u < U; ++u) {
+            float y[8];
+            widen8_ordered(q[u], y, chain);
+            per_row(y);
+            finish_row<YOUT>(y, res[u]);
+            chain = res[u].packed;
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (u >= nr) break;
-            float y[8];
-            widen8(q[u], y);
-            per_row(y);
-            store_row<YOUT>(y, o, lo);
+            store_row<YOUT>(res[u], o, lo);
         }
     };
     if (MODE == kSmooth) {

@@ -295,6 +295,14 @@ WORKLOADS = {
     "pow2_4096x16384": dict(m=4096, d=16384, seed=1023, kind="pixart"),
     "pow2_512x4096": dict(m=512, d=4096, seed=1024, kind="pixart"),
     "pow2_512x16384": dict(m=512, d=16384, seed=1025, kind="pixart"),
+    # Production linear-layer shapes of FLUX.1 and PixArt-Sigma the paper times
+    # (Appendix A, Table 4); 4096x1152 is the PixArt attention input above.
+    "prod_512x3072": dict(m=512, d=3072, seed=1031, kind="pixart"),
+    "prod_512x12288": dict(m=512, d=12288, seed=1032, kind="pixart"),
+    "prod_4096x3072": dict(m=4096, d=3072, seed=1033, kind="pixart"),
+    "prod_4096x3456": dict(m=4096, d=3456, seed=1034, kind="pixart"),
+    "prod_4096x4608": dict(m=4096, d=4608, seed=1035, kind="pixart"),
+    "prod_4096x12288": dict(m=4096, d=12288, seed=1036, kind="pixart"),
 }
 
 
