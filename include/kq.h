@@ -414,6 +414,27 @@ kq_status kq_calib_step(const float *W, int64_t M, int64_t d, int64_t o, float *
                         float *losses, float *grad_theta, void *workspace, int64_t workspace_bytes,
                         kq_stream_t stream);
 
+/*
+ * Allocation-free calibration step, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): kq_calib_init followed by kq_calib_step in one call, on a
+ * workspace the library holds in a device array of its own instead of a
+ * caller-owned one. Results are those of kq_calib_init + kq_calib_step on the
+ * same arguments (the same kernels in the same order). Each call redoes the
+ * init half (A in fp32 and A W^T), so calls are independent of each other.
+ *   A, W, theta ... grad_theta, stream   as kq_calib_init / kq_calib_step
+ * Limit: kq_calib_workspace_bytes(M, d, o) must be at most 64 MiB
+ * (KQ_ERR_UNSUPPORTED otherwise; M = 1024, d = o = 1152 takes 43.5 MiB).
+ * Every call on one GPU uses that GPU's single array: calls that overlap on
+ * one GPU (other streams or host threads) race and must be serialized by the
+ * caller. No hipMalloc or other allocation is made; the first call on a device
+ * looks up the array's address there (hipGetSymbolAddress).
+ */
+kq_status kq_calib_step_noalloc(const uint16_t *A, const float *W, int64_t M, int64_t d, int64_t o, float *theta,
+                                float *adam_m, float *adam_v, int64_t t, float lr, float beta1, float beta2, float eps,
+                                float *lambdas, int auto_lambda, float *losses, float *grad_theta,
+                                kq_stream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *kq_status_string(kq_status s);
 

@@ -45,6 +45,7 @@ EXPORTS = (
     "kq_calib_workspace_bytes",
     "kq_calib_init",
     "kq_calib_step",
+    "kq_calib_step_noalloc",
     "kq_status_string",
     "kq_last_hip_error",
     "kq_factors_from_lu",
@@ -97,6 +98,8 @@ def lib():
             "kq_calib_init": [p, i64, i64, p, i64, p, i64, p],
             "kq_calib_step": [p, i64, i64, i64, p, p, p, i64, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                               ctypes.c_float, p, st, p, p, p, i64, p],
+            "kq_calib_step_noalloc": [p, p, i64, i64, i64, p, p, p, i64, ctypes.c_float, ctypes.c_float,
+                                      ctypes.c_float, ctypes.c_float, p, st, p, p, p],
         }.items():
             fn = getattr(L, name)
             fn.argtypes = args
@@ -604,6 +607,26 @@ class Calibration:
     def factors(self):
         """The current 2x2 factors, fp32 [d/32][5][2][2] (Eq. 6), for the fused quantizer."""
         return factors_from_lu(self.theta.double().cpu().numpy())
+
+
+def calib_step_noalloc(A, W, theta, adam_m, adam_v, t, lambdas, losses, grad=None, lr=1e-2, beta1=0.9,
+                       beta2=0.999, eps=1e-8, auto_lambda=False, stream=None):
+    """One calibration step (kq_calib_init + kq_calib_step) on the library's own
+    device workspace (kq_calib_step_noalloc): nothing is allocated. theta, adam_m,
+    adam_v, lambdas and losses are updated in place, as by Calibration.step."""
+    torch = _torch()
+    _dev(A, "A", (torch.bfloat16, torch.int16, torch.uint16))
+    _dev(W, "W", (torch.float32,))
+    M, d = A.shape
+    o = W.shape[0]
+    for name, x in (("theta", theta), ("adam_m", adam_m), ("adam_v", adam_v), ("lambdas", lambdas),
+                    ("losses", losses)):
+        _dev(x, name, (torch.float32,))
+    _check("kq_calib_step_noalloc",
+           lib().kq_calib_step_noalloc(_p(A), _p(W), M, d, o, _p(theta), _p(adam_m), _p(adam_v), int(t), float(lr),
+                                       float(beta1), float(beta2), float(eps), _p(lambdas), int(bool(auto_lambda)),
+                                       _p(losses), _p(grad) if grad is not None else None, _stream_ptr(stream)))
+    return losses
 
 
 def factors_from_lu(abc):

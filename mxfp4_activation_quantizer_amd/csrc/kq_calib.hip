@@ -28,6 +28,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kq.h"
 #include "kq_device.hpp"
 #include "kq_host.hpp"
@@ -541,6 +543,38 @@ kq_status launch_gemm(int64_t m, int64_t n, int64_t k, float alpha, const float 
     return launched();
 }
 
+// The allocation-free step's workspace: a device array of the library, one copy
+// per GPU (each device holds it, at its own address, until the process ends).
+// Host code never uses its name as an address: the per-device address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+constexpr int64_t kScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];
+
+kq_status scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        kqhost::g_last_hip_error = (int)e;
+        return KQ_ERR_HIP;
+    }
+    if (dev < 0 || dev >= 64) return KQ_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            kqhost::g_last_hip_error = (int)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            return KQ_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -650,6 +684,28 @@ kq_status kq_calib_step(const float *W, int64_t M, int64_t d, int64_t o, float *
     hipLaunchKernelGGL(kq::calib_update_kernel, dim3((unsigned)nblk), dim3(256), 0, s, F(L.fac), F(L.facit), F(L.dKA),
                        (int)L.nchA, F(L.dPW), (int)L.nchW, nblk, theta, adam_m, adam_v, ad, grad_theta);
     return launched();
+}
+
+kq_status kq_calib_step_noalloc(const uint16_t *A, const float *W, int64_t M, int64_t d, int64_t o, float *theta,
+                                float *adam_m, float *adam_v, int64_t t, float lr, float beta1, float beta2, float eps,
+                                float *lambdas, int auto_lambda, float *losses, float *grad_theta,
+                                kq_stream_t stream) {
+    kq_status st = calib_shape(M, d, o);
+    if (st != KQ_OK) return st;
+    if (calib_layout(M, d, o).total > kScratchBytes) return KQ_ERR_UNSUPPORTED;
+    if (!A || !W || !theta || !adam_m || !adam_v || !lambdas || !losses) return KQ_ERR_NULL;
+    if (!aligned(A, 16) || !aligned(W, 16)) return KQ_ERR_ALIGN;
+    if (t < 1 || !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps >= 0.0f) ||
+        !(lr >= 0.0f))
+        return KQ_ERR_SHAPE;
+    void *ws = nullptr;
+    if ((st = scratch_address(&ws)) != KQ_OK) return st;
+    // every part of the workspace the step reads is written first in this call
+    // (A in fp32 and A W^T by the init half, the rest by the step's own kernels),
+    // so nothing of an earlier call's contents is used and nothing needs clearing
+    if ((st = kq_calib_init(A, M, d, W, o, ws, kScratchBytes, stream)) != KQ_OK) return st;
+    return kq_calib_step(W, M, d, o, theta, adam_m, adam_v, t, lr, beta1, beta2, eps, lambdas, auto_lambda, losses,
+                         grad_theta, ws, kScratchBytes, stream);
 }
 
 }  // extern "C"

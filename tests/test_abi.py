@@ -178,6 +178,16 @@ GOOD = P(0x10000)  # never dereferenced: every case below fails before a launch
                        GOOD, 1 << 30, None), kq.KQ_ERR_NULL),
     ("kq_calib_step", (GOOD, 64, 64, 16, GOOD, GOOD, GOOD, 1, 1e-3, 0.9, 0.999, 1e-8, GOOD, 1, GOOD, None,
                        GOOD, 4096, None), kq.KQ_ERR_SHAPE),
+    ("kq_calib_step_noalloc", (GOOD, GOOD, 4096, 1152, 1152, GOOD, GOOD, GOOD, 1, 1e-3, 0.9, 0.999, 1e-8, GOOD, 1,
+                               GOOD, None, None), kq.KQ_ERR_UNSUPPORTED),
+    ("kq_calib_step_noalloc", (None, GOOD, 256, 256, 128, GOOD, GOOD, GOOD, 1, 1e-3, 0.9, 0.999, 1e-8, GOOD, 1,
+                               GOOD, None, None), kq.KQ_ERR_NULL),
+    ("kq_calib_step_noalloc", (GOOD, GOOD, 256, 250, 128, GOOD, GOOD, GOOD, 1, 1e-3, 0.9, 0.999, 1e-8, GOOD, 1,
+                               GOOD, None, None), kq.KQ_ERR_SHAPE),
+    ("kq_calib_step_noalloc", (GOOD, GOOD, 256, 256, 128, GOOD, GOOD, GOOD, 0, 1e-3, 0.9, 0.999, 1e-8, GOOD, 1,
+                               GOOD, None, None), kq.KQ_ERR_SHAPE),
+    ("kq_calib_step_noalloc", (P(0x10008), GOOD, 256, 256, 128, GOOD, GOOD, GOOD, 1, 1e-3, 0.9, 0.999, 1e-8, GOOD,
+                               1, GOOD, None, None), kq.KQ_ERR_ALIGN),
 ])
 def test_host_argument_checks(L, fn, args, status):
     assert getattr(L, fn)(*args) == status
