@@ -583,6 +583,7 @@ kq_status kq_gemm_f32(int transa, int transb, int64_t m, int64_t n, int64_t k, f
                       int64_t lda, const float *B, int64_t ldb, float beta, const float *C, int64_t ldc, float *D,
                       int64_t ldd, kq_stream_t stream) {
     if (m < 0 || n < 0 || k < 0) return KQ_ERR_SHAPE;
+    if (!kqhost::sizes_fit({m, n, k, lda, ldb, ldc, ldd})) return KQ_ERR_UNSUPPORTED;
     if (m == 0 || n == 0) return KQ_OK;
     if (!A || !B || !D || (beta != 0.0f && !C)) return KQ_ERR_NULL;
     if (lda < (transa ? m : k) || ldb < (transb ? k : n) || ldd < n || (beta != 0.0f && ldc < n) || lda < 1 ||

@@ -547,6 +547,7 @@ kq_status kq_mxfp4_gemm(const uint8_t *codes_a, const uint8_t *scales_a, const u
                         const uint8_t *scales_w, int64_t m, int64_t n, int64_t k, float *O, int64_t ldo,
                         kq_stream_t stream) {
     if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || ldo < n) return KQ_ERR_SHAPE;
+    if (!kqhost::sizes_fit({m, n, k, ldo})) return KQ_ERR_UNSUPPORTED;
     if (m == 0 || n == 0) return KQ_OK;
     if (!codes_a || !scales_a || !codes_w || !scales_w || !O) return KQ_ERR_NULL;
     if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || (k / 2) % 16 != 0) return KQ_ERR_ALIGN;
@@ -563,6 +564,7 @@ kq_status kq_mxfp4_gemm_lowrank(const uint8_t *codes_a, const uint8_t *scales_a,
                                 const uint8_t *codes_l, const uint8_t *scales_l, int64_t r, float *O, int64_t ldo,
                                 kq_stream_t stream) {
     if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || ldo < n || r <= 0 || r % 32 != 0) return KQ_ERR_SHAPE;
+    if (!kqhost::sizes_fit({m, n, k, ldo, r})) return KQ_ERR_UNSUPPORTED;
     if (m == 0 || n == 0) return KQ_OK;
     if (!codes_a || !scales_a || !codes_w || !scales_w || !O || !Z || !codes_l || !scales_l) return KQ_ERR_NULL;
     if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || (k / 2) % 16 != 0 || !aligned(Z, 16) ||
@@ -580,6 +582,7 @@ kq_status kq_mxfp4_gemm_lowrank(const uint8_t *codes_a, const uint8_t *scales_a,
 kq_status kq_lowrank_project(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint8_t *codes_r,
                              const uint8_t *scales_r, int64_t r, float *Z, kq_stream_t stream) {
     if (m < 0 || d < 0 || d % 32 != 0 || ldx < d || r <= 0 || r % 32 != 0) return KQ_ERR_SHAPE;
+    if (!kqhost::sizes_fit({m, d, ldx, r})) return KQ_ERR_UNSUPPORTED;
     if (m == 0 || d == 0) return KQ_OK;
     if (!X16 || !codes_r || !scales_r || !Z) return KQ_ERR_NULL;
     if (!aligned(X16, 16) || ldx % 8 != 0 || !aligned(codes_r, 16) || !aligned(Z, 16)) return KQ_ERR_ALIGN;
@@ -597,6 +600,7 @@ kq_status kq_lowrank_project(const uint16_t *X16, int64_t m, int64_t d, int64_t 
 kq_status kq_lowrank_project_bf16(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint16_t *R16,
                                   int64_t r, float *Z, kq_stream_t stream) {
     if (m < 0 || d < 0 || d % 32 != 0 || ldx < d || r <= 0 || r % 32 != 0) return KQ_ERR_SHAPE;
+    if (!kqhost::sizes_fit({m, d, ldx, r})) return KQ_ERR_UNSUPPORTED;
     if (m == 0 || d == 0) return KQ_OK;
     if (!X16 || !R16 || !Z) return KQ_ERR_NULL;
     if (!aligned(X16, 16) || ldx % 8 != 0 || !aligned(R16, 16) || !aligned(Z, 16)) return KQ_ERR_ALIGN;
@@ -613,6 +617,7 @@ kq_status kq_lowrank_project_bf16(const uint16_t *X16, int64_t m, int64_t d, int
 kq_status kq_dequantize_mxfp4_bf16(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t k,
                                    uint16_t *out, kq_stream_t stream) {
     if (rows < 0 || k < 0 || k % 32 != 0) return KQ_ERR_SHAPE;
+    if (!kqhost::sizes_fit({rows, k})) return KQ_ERR_UNSUPPORTED;
     if (rows == 0 || k == 0) return KQ_OK;
     if (!codes || !scales || !out) return KQ_ERR_NULL;
     if (!aligned(codes, 4) || !aligned(out, 16)) return KQ_ERR_ALIGN;

@@ -493,6 +493,7 @@ extern "C" {
 kq_status kq_pack_mxfp4_scales(const uint8_t *scales, int64_t rows, int64_t k, uint8_t *packed,
                                kq_stream_t stream) {
     if (rows < 0 || k < 0 || k % 256 != 0) return KQ_ERR_SHAPE;
+    if (!kqhost::sizes_fit({rows, k})) return KQ_ERR_UNSUPPORTED;
     if (rows == 0 || k == 0) return KQ_OK;
     if (!scales || !packed) return KQ_ERR_NULL;
     if (!aligned(packed, 8)) return KQ_ERR_ALIGN;
@@ -518,6 +519,7 @@ kq_status gemm_packed(const uint8_t *codes_a, const uint8_t *packed_scales_a, co
                       kq_stream_t stream) {
     constexpr int esz = B16 ? 2 : 4;
     if (m < 0 || n < 0 || k < 0 || k % 256 != 0 || ldo < n) return KQ_ERR_SHAPE;
+    if (!kqhost::sizes_fit({m, n, k, ldo})) return KQ_ERR_UNSUPPORTED;
     if (m == 0 || n == 0) return KQ_OK;
     if (!O || (k > 0 && (!codes_a || !packed_scales_a || !codes_w || !packed_scales_w))) return KQ_ERR_NULL;
     if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || !aligned(packed_scales_a, 16) ||
@@ -578,6 +580,7 @@ kq_status kq_mxfp4_gemm_packed_lowrank(const uint8_t *codes_a, const uint8_t *pa
                                        int64_t k, const float *Z, const uint8_t *codes_l, const uint8_t *scales_l,
                                        int64_t r, float *O, int64_t ldo, kq_stream_t stream) {
     if (m < 0 || n < 0 || k < 0 || k % 256 != 0 || ldo < n || r <= 0 || r % 32 != 0) return KQ_ERR_SHAPE;
+    if (!kqhost::sizes_fit({m, n, k, ldo, r})) return KQ_ERR_UNSUPPORTED;
     if (m == 0 || n == 0) return KQ_OK;
     if (!O || !Z || !codes_l || !scales_l || (k > 0 && (!codes_a || !packed_scales_a || !codes_w || !packed_scales_w)))
         return KQ_ERR_NULL;

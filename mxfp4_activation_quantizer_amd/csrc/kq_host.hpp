@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "kq.h"
 
 namespace kqhost {
@@ -29,6 +31,15 @@ inline kq_status check_bf16_io(const uint16_t *A, int64_t lda, const uint8_t *co
     if (!A || !codes || !scales) return KQ_ERR_NULL;
     if (!aligned(A, 16) || lda % 8 != 0 || !aligned(codes, 16)) return KQ_ERR_ALIGN;
     return KQ_OK;
+}
+
+// Sizes the GEMM-family launches multiply together: each must be below 2^31,
+// so that any product of two of them (times a small constant) stays far
+// inside int64 before the finer limits are checked.
+inline bool sizes_fit(std::initializer_list<int64_t> v) {
+    for (const int64_t x : v)
+        if (x >= ((int64_t)1 << 31)) return false;
+    return true;
 }
 
 // Status of the launch just enqueued.

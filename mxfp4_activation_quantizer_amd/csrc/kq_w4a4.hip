@@ -368,6 +368,7 @@ bool make_w4geom(int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldo, kq::
 kq_status check_w(const uint8_t *codes_w, const uint8_t *scales_w, int64_t m, int64_t n, int64_t k, const float *O,
                   int64_t ldo) {
     if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || ldo < n) return KQ_ERR_SHAPE;
+    if (!kqhost::sizes_fit({m, n, k, ldo})) return KQ_ERR_UNSUPPORTED;
     if (m > 0 && n > 0 && (!codes_w || !scales_w || !O)) return KQ_ERR_NULL;
     if (!aligned(codes_w, 16)) return KQ_ERR_ALIGN;
     if ((k / 32) % 4 == 0 && !aligned(scales_w, 4)) return KQ_ERR_ALIGN;
@@ -400,6 +401,7 @@ kq_status kq_transform_quantize_mxfp4_gemm(const uint16_t *A, int64_t m, int64_t
     kq_status s = check_w(codes_w, scales_w, m, n, k, O, ldo);
     if (s != KQ_OK) return s;
     if (lda < k) return KQ_ERR_SHAPE;
+    if (!kqhost::sizes_fit({lda})) return KQ_ERR_UNSUPPORTED;
     if (m == 0 || n == 0) return KQ_OK;
     if (!A || !factors) return KQ_ERR_NULL;
     if (!aligned(A, 16) || lda % 8 != 0 || !aligned(factors, 16)) return KQ_ERR_ALIGN;
