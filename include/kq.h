@@ -46,6 +46,10 @@
  *     is returned.
  *   - Inputs must be finite; NaN or Inf inputs give unspecified codes.
  *   - Outputs must not overlap inputs.
+ *   - The GEMM-family entry points (kq_mxfp4_gemm*, kq_lowrank_project*,
+ *     kq_dequantize_mxfp4_bf16, kq_pack_mxfp4_scales, kq_gemm_f32,
+ *     kq_transform_quantize_mxfp4_gemm) refuse any size or leading dimension
+ *     of 2^31 or more with KQ_ERR_UNSUPPORTED, before their finer limits.
  */
 #ifndef KQ_H
 #define KQ_H
