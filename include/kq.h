@@ -219,9 +219,11 @@ kq_status kq_pack_mxfp4_scales(const uint8_t *scales, int64_t rows, int64_t k, u
  * on 256 x 256 output tiles with the 32 x 32 x 64 instruction (64 k per
  * instruction, increasing k), so its results agree with kq_mxfp4_gemm to fp32
  * rounding of the partial sums, and bit-for-bit whenever the fp32 sums are
- * exact. It may enqueue two launches on the stream: whole rounds of tiles (one
- * per compute unit at a time), then the last partial round as 256 x 128 halves;
- * every output element gets the same instructions either way.
+ * exact. One launch: whole rounds of tiles (one per compute unit at a time),
+ * and a last partial round of at most half the compute units as 256 x 128
+ * halves (computed first on half the units when the counts allow, so that the
+ * units' output stores do not all coincide); every output element gets the
+ * same instructions either way. At most 2^30 tiles (KQ_ERR_UNSUPPORTED).
  *   codes_a          device, [m][k/2] bytes, 16-byte aligned
  *   packed_scales_a  device, packed [k/256][m][8], 16-byte aligned
  *   codes_w          device, [n][k/2] bytes, 16-byte aligned

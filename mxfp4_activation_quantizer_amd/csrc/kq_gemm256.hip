@@ -23,7 +23,12 @@
 //    picks it, with no per-lane shift;
 //  - tiles are numbered so that each XCD (workgroups are dealt to the eight XCDs
 //    round robin) gets a contiguous run, walked in bands of 4 row tiles, which
-//    keeps the operand rows a run shares in that XCD's L2.
+//    keeps the operand rows a run shares in that XCD's L2; one launch covers
+//    whole tiles and half tiles in the order of kq_tileorder.hpp;
+//  - the output leaves through LDS: each store instruction writes 4 whole rows
+//    of 256 bytes (8 full cache lines) rather than 32 rows x 32 bytes, which
+//    the store path serves several times faster (the fp32 epilogue of a tile,
+//    256 KB per CU, had taken as long as 4 of its 12 k stages at k = 3072).
 //
 // LDS layout of a stage: A codes [256 rows][128 bytes], W codes likewise, A
 // scales [256 rows][8 bytes], W scales likewise. Code rows are stored with
@@ -45,6 +50,7 @@
 #include "kq_cvt.hpp"
 #include "kq_device.hpp"
 #include "kq_host.hpp"
+#include "kq_tileorder.hpp"
 
 namespace kq {
 namespace g256 {
@@ -75,9 +81,9 @@ struct Geom {
     int kbytes;  // k / 2
     int stages;  // k / 256
     int tiles_m, tiles_n, nwg;
-    int vec_out;  // O 16-byte aligned and ldo % 4 == 0: 16-byte stores
+    int rows16;   // O 16-byte aligned and ldo esz % 16 == 0: output rows staged through LDS
     int r;        // rank of the low-rank term (LR kernels)
-    int tile_base;  // first tile (in the XCD-run order) of this launch
+    TileOrder order;  // which tile, or half tile, each workgroup computes
 };
 
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -127,44 +133,40 @@ struct Scl {
 };
 
 typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 // LR: after the product, the low-rank term Z deq(L)^T of Sec. 3.4 Eq. 11 is
 // added into the same accumulators (Z fp32 [m][r] split as hi + lo bf16, exact
 // to 2^-16 relative; deq(L) exact in bf16), 64 of r at a time through LDS, on
 // v_mfma_f32_32x32x16_bf16 with the same swapped operands and 32 x 32 layout.
 //
-// TN = 128 is the half-width form for a launch's last partial round (with or
-// without the low-rank term; its staging, 96 KB, fits the smaller LDS): tile t of the
-// XCD-run order split into its two 128-column halves (workgroup 2 i + h takes half h
-// of tile tile_base + i), each output element accumulated by the same instructions in
-// the same k order as in the full tile.
+// TN = 128 is the half-width form (with or without the low-rank term): half h of
+// a tile, its 128 columns at 128 h, each output element accumulated by the same
+// instructions in the same k order as in the full tile.
 //
 // B16: O is written in bf16 (each fp32 sum rounded to nearest even) instead of fp32.
-template <bool LR, int TN, bool B16 = false>
-__global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__restrict__ ca,
-                                                           const uint8_t *__restrict__ psa,
-                                                           const uint8_t *__restrict__ cw,
-                                                           const uint8_t *__restrict__ psw, Geom g,
-                                                           const float *__restrict__ Z,
-                                                           const uint8_t *__restrict__ cl,
-                                                           const uint8_t *__restrict__ sl,
-                                                           void *__restrict__ O) {
+//
+// One tile (run-order number u; half h of it when TN = 128) of one workgroup;
+// smem holds 2 stages of the full-width layout plus 1 KB.
+template <bool LR, int TN, bool B16>
+__device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, const uint8_t *__restrict__ psa,
+                                             const uint8_t *__restrict__ cw, const uint8_t *__restrict__ psw,
+                                             const Geom g, const float *__restrict__ Z,
+                                             const uint8_t *__restrict__ cl, const uint8_t *__restrict__ sl,
+                                             void *__restrict__ O, int u, int h, uint8_t *smem) {
     static_assert(TN == 256 || TN == 128, "tile width");
     using L = Lay<TN>;
-    constexpr int NB = L::NB, LW = L::LW, kStage = L::kStage;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+    constexpr int NB = L::NB, LW = L::LW;
+    // stage buffers at kStage of the full-width layout (the spare 1 KB after two
+    // of them takes the dummy scale load of wave 3 at TN = 128)
+    constexpr int kStage = Lay<256>::kStage;
     const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
 
-    // tile order: a contiguous run per XCD, bands of kGroupM row tiles, column-major inside a band
-    int tile = g.tile_base + (TN == 256 ? (int)blockIdx.x : (int)(blockIdx.x >> 1));
-    {
-        const int q = g.nwg / 8, rm = g.nwg % 8, x = tile % 8, loc = tile / 8;
-        tile = x < rm ? x * (q + 1) + loc : rm * (q + 1) + (x - rm) * q + loc;
-    }
-    const int band = tile / (kGroupM * g.tiles_n), within = tile % (kGroupM * g.tiles_n);
+    // run-order tile u: bands of kGroupM row tiles, column-major inside a band
+    const int band = u / (kGroupM * g.tiles_n), within = u % (kGroupM * g.tiles_n);
     const int gm = min(kGroupM, g.tiles_m - band * kGroupM);
     const int tm = band * kGroupM + within % gm, tn = within / gm;
-    const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile + (TN == 256 ? 0 : 128 * (int)(blockIdx.x & 1));
+    const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile + (TN == 256 ? 0 : 128 * h);
     const int rows_a = (int)min<int64_t>(kTile, g.m - m0), rows_w = (int)min<int64_t>(TN, g.n - n0);
     if (rows_w <= 0) return;  // the right half of a tile narrower than 129 columns (whole workgroup)
 
@@ -201,16 +203,18 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
         else dma16(dcw, st + L::kOffW + ((TN / 4) * w + 8 * (i - 8)) * 128, cvoffw[i - 8], kb);
     };
     // scales of stage s, 1 KB per load: A rows 128 (w & 1) .. by waves 0 and 1, W rows
-    // 128 (w & 1) .. by waves 2 and 3 (TN = 256) or all TN rows by wave 2 (TN = 128)
+    // 128 (w & 1) .. by waves 2 and 3 (TN = 256) or all TN rows by wave 2 (TN = 128;
+    // wave 3's load is then past the record count and lands in the spare LDS).
+    // Written without branches (the wave index is uniform: scalar selects), so
+    // that the loop body stays one block and the order fixed below holds.
     const int srow = 128 * (w & 1) + 2 * lane;
+    const bool sw_a = w < 2, sw_none = TN == 128 && w == 3;
+    const i32x4_t dss = sw_a ? dsa : dsw;
+    const uint32_t srow_off = (uint32_t)(8 * ((sw_a ? m0 : n0) + srow)), s_stride = (uint32_t)(8 * (sw_a ? g.m : g.n));
+    const uint32_t s_lds = sw_none ? (uint32_t)(2 * kStage) : (uint32_t)((sw_a ? L::kOffSA : L::kOffSW) + 1024 * (w & 1));
     auto issue_scl = [&](int s) {
-        const uint32_t st = lds0 + (uint32_t)((s & 1) * kStage);
-        if (w < 2)
-            dma16(dsa, st + L::kOffSA + 1024 * (w & 1), (uint32_t)(8 * (m0 + srow)) + (uint32_t)(8 * g.m) * (uint32_t)s,
-                  0u);
-        else if (TN == 256 || w == 2)
-            dma16(dsw, st + L::kOffSW + 1024 * (w & 1), (uint32_t)(8 * (n0 + srow)) + (uint32_t)(8 * g.n) * (uint32_t)s,
-                  0u);
+        const uint32_t voff = sw_none ? 0x80000000u : srow_off + s_stride * (uint32_t)s;
+        dma16(dss, lds0 + (uint32_t)((s & 1) * kStage) * !sw_none + s_lds, voff, 0u);
     };
 
     const int r = lane & 31, hi = lane >> 5;
@@ -257,6 +261,10 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
         acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[b], F.a[a], acc[a][b], 4, 4, j, (int)S.sb[b],
                                                                     j, (int)S.sa[a]);
     };
+    // ties the matrix instruction that wrote acc[a][b] to this point of the
+    // program: it emits nothing, but the accumulator is an operand of a volatile
+    // statement, so the instruction cannot drift past the loads issued after it
+    auto pin = [&](int a, int b) { asm volatile("" : "+a"(acc[a][b])); };
     auto step = [&](const Frag<NB> &F, const Scl<NB> &S, auto jc) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
@@ -293,6 +301,7 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
             for (int b = 0; b < NB; ++b) {
                 const int slot = NB * a + b;
                 mma(F0, S, J0(), a, b);
+                pin(a, b);
                 issue_code(s + 1, slot);
                 if (slot + 4 * NB < 8 + LW) issue_code(s + 1, slot + 4 * NB);
                 if (slot == 7) issue_scl(s + 1);
@@ -398,56 +407,92 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
         }
     }
 
-    // lane (r, hi) holds O row wm + 32 a + r, columns wn + 32 b + 8 q + 4 hi + 0..3;
-    // rows past m are past the record count and dropped, columns checked
+    // Output through LDS, so that a store instruction writes whole rows (4 rows
+    // of 256 bytes: 8 full cache lines) instead of 32 rows x 32 bytes. Lane (r,
+    // hi) holds O row wm + 32 a + r, columns wn + 32 b + 8 q + 4 hi + 0..3. Wave w
+    // stages its 128 x 128 block (fp32: 64 columns per pass) in its own 32 KB at
+    // 32 KB w, rows of 256 bytes with 16-byte chunk c at c ^ (row & 15). Every
+    // wave is done with the operand stages (and the branch's staging) first.
     constexpr int esz = B16 ? 2 : 4;
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<char *>(O) + (m0 * g.ldo + n0) * esz, (short)0,
         (int)(((int64_t)(rows_a - 1) * g.ldo + (g.n - n0)) * esz), 0x00020000);
-    const bool full_n = g.vec_out && n0 + TN <= g.n;
+    // whole 16-byte pieces: columns inside n and aligned rows; otherwise element by
+    // element, columns checked (rows past m are past the record count, or checked)
+    const bool whole = g.rows16 && n0 + TN <= g.n;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    uint8_t *reg = smem + 32768 * w;
+    constexpr int kPasses = B16 ? 1 : NB / 2, kPerPass = NB / kPasses;
+    // 16-byte chunks per staged row (bf16 at TN = 128: 8), rows per store
+    constexpr int kCpr = B16 ? 4 * NB : 16, kRpi = 64 / kCpr;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int row = wm + 32 * a + r;
+    for (int pass = 0; pass < kPasses; ++pass) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int col = wn + 32 * b + 8 * q + 4 * hi;
-                const uint32_t off = (uint32_t)((row * g.ldo + col) * esz);
-                if (B16) {
-                    // round to nearest even in the hardware convert, one per pair; plain
-                    // stores under the bounds a buffer descriptor would apply (rows below
-                    // rows_a, columns below n): with 2- and 8-byte buffer stores the
-                    // compiler kept the descriptor in vector registers and looped over it
-                    const bf16x2_t p0 = {(__bf16)acc[a][b][4 * q], (__bf16)acc[a][b][4 * q + 1]};
-                    const bf16x2_t p1 = {(__bf16)acc[a][b][4 * q + 2], (__bf16)acc[a][b][4 * q + 3]};
-                    const uint32_t w0 = __builtin_bit_cast(uint32_t, p0), w1 = __builtin_bit_cast(uint32_t, p1);
-                    uint16_t *o16 = static_cast<uint16_t *>(O) + (m0 + row) * g.ldo + n0 + col;
-                    if (row < rows_a) {
-                        if (full_n) {
-                            typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-                            *reinterpret_cast<u32x2_t *>(o16) = u32x2_t{w0, w1};
-                        } else {
-                            const uint16_t h[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1,
-                                                   (uint16_t)(w1 >> 16)};
+            for (int bb = 0; bb < kPerPass; ++bb)
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (n0 + col + e < g.n) o16[e] = h[e];
-                        }
-                    }
-                } else {
-                    const u32x4_t v = {__float_as_uint(acc[a][b][4 * q]), __float_as_uint(acc[a][b][4 * q + 1]),
-                                       __float_as_uint(acc[a][b][4 * q + 2]), __float_as_uint(acc[a][b][4 * q + 3])};
-                    if (full_n) {
-                        __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, 0);
+                for (int q = 0; q < 4; ++q) {
+                    const int b = pass * kPerPass + bb, row = 32 * a + r;
+                    if (B16) {
+                        // round to nearest even in the hardware convert, one per pair
+                        const bf16x2_t p0 = {(__bf16)acc[a][b][4 * q], (__bf16)acc[a][b][4 * q + 1]};
+                        const bf16x2_t p1 = {(__bf16)acc[a][b][4 * q + 2], (__bf16)acc[a][b][4 * q + 3]};
+                        typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+                        const int chunk = 4 * b + q;
+                        *reinterpret_cast<u32x2_t *>(reg + row * 256 + 16 * (chunk ^ (row & 15)) + 8 * hi) =
+                            u32x2_t{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
                     } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n0 + col + e < g.n) __builtin_amdgcn_raw_buffer_store_b32(v[e], ro, off + 4 * e, 0, 0);
+                        const int chunk = 8 * bb + 2 * q + hi;
+                        *reinterpret_cast<floatx4_t *>(reg + row * 256 + 16 * (chunk ^ (row & 15))) =
+                            floatx4_t{acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
+                                      acc[a][b][4 * q + 3]};
                     }
                 }
+        // the wave reads back only what it wrote (its LDS operations complete in order)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int c = lane % kCpr;
+#pragma unroll 8
+        for (int i = 0; i < 128 / kRpi; ++i) {
+            const int row = kRpi * i + lane / kCpr;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(reg + row * 256 + 16 * (c ^ (row & 15)));
+            const int col = B16 ? wn + 8 * c : wn + 64 * pass + 4 * c;  // from n0
+            const int orow = wm + row;                                    // from m0
+            if (whole) {
+                __builtin_amdgcn_raw_buffer_store_b128(v, ro, (uint32_t)((orow * g.ldo + col) * esz), 0, 0);
+            } else if (B16) {
+                // plain stores: with 2-byte buffer stores the compiler kept the
+                // descriptor in vector registers and looped over it
+                if (orow < rows_a) {
+                    uint16_t *o16 = static_cast<uint16_t *>(O) + (m0 + orow) * g.ldo + n0 + col;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n0 + col + e < g.n) o16[e] = (uint16_t)(v[e / 2] >> (16 * (e & 1)));
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n0 + col + e < g.n)
+                        __builtin_amdgcn_raw_buffer_store_b32(v[e], ro, (uint32_t)((orow * g.ldo + col + e) * 4), 0, 0);
             }
+        }
     }
+}
+
+// One workgroup per tile (or half tile) in the launch's work order.
+template <bool LR, bool B16>
+__global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__restrict__ ca,
+                                                           const uint8_t *__restrict__ psa,
+                                                           const uint8_t *__restrict__ cw,
+                                                           const uint8_t *__restrict__ psw, Geom g,
+                                                           const float *__restrict__ Z,
+                                                           const uint8_t *__restrict__ cl,
+                                                           const uint8_t *__restrict__ sl,
+                                                           void *__restrict__ O) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Lay<256>::kStage + 1024];
+    const TileWork wk = tile_work((int)blockIdx.x, g.order);
+    if (wk.half < 0) gemm256_tile<LR, 256, B16>(ca, psa, cw, psw, g, Z, cl, sl, O, wk.tile, 0, smem);
+    else gemm256_tile<LR, 128, B16>(ca, psa, cw, psw, g, Z, cl, sl, O, wk.tile, wk.half, smem);
 }
 
 // Compute units of the current device (cached per device; 256 on MI355X).
@@ -529,7 +574,7 @@ kq_status gemm_packed(const uint8_t *codes_a, const uint8_t *packed_scales_a, co
     const int64_t lim = (int64_t)1 << 31;
     const int64_t tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
     if ((int64_t)256 * (k / 2) >= lim || m * (k / 32) >= lim || n * (k / 32) >= lim ||
-        ((int64_t)255 * ldo + n) * esz >= lim || tiles_m * tiles_n >= lim)
+        ((int64_t)255 * ldo + n) * esz >= lim || tiles_m * tiles_n >= (lim >> 1))
         return KQ_ERR_UNSUPPORTED;
     kq::g256::Geom g;
     g.m = m;
@@ -540,22 +585,12 @@ kq_status gemm_packed(const uint8_t *codes_a, const uint8_t *packed_scales_a, co
     g.tiles_m = (int)tiles_m;
     g.tiles_n = (int)tiles_n;
     g.nwg = (int)(tiles_m * tiles_n);
-    g.vec_out = aligned(O, 4 * esz) && ldo % 4 == 0;
+    g.rows16 = aligned(O, 16) && (ldo * esz) % 16 == 0;
     g.r = 0;
-    const int ncu = kq::g256::cu_count();
-    const int rem = g.nwg % ncu;
-    const int nfull = (rem > 0 && 2 * rem <= ncu) ? g.nwg - rem : g.nwg;
-    g.tile_base = 0;
-    if (nfull > 0)
-        hipLaunchKernelGGL((kq::g256::gemm256_kernel<false, 256, B16>), dim3((unsigned)nfull),
-                           dim3(kq::g256::kThreads), 0, (hipStream_t)stream, codes_a, packed_scales_a, codes_w,
-                           packed_scales_w, g, nullptr, nullptr, nullptr, O);
-    if (nfull < g.nwg) {
-        g.tile_base = nfull;
-        hipLaunchKernelGGL((kq::g256::gemm256_kernel<false, 128, B16>), dim3((unsigned)(2 * (g.nwg - nfull))),
-                           dim3(kq::g256::kThreads), 0, (hipStream_t)stream, codes_a, packed_scales_a, codes_w,
-                           packed_scales_w, g, nullptr, nullptr, nullptr, O);
-    }
+    g.order = kq::g256::make_tile_order(g.nwg, kq::g256::cu_count());
+    hipLaunchKernelGGL((kq::g256::gemm256_kernel<false, B16>), dim3((unsigned)kq::g256::tile_order_groups(g.order)),
+                       dim3(kq::g256::kThreads), 0, (hipStream_t)stream, codes_a, packed_scales_a, codes_w,
+                       packed_scales_w, g, nullptr, nullptr, nullptr, O);
     return launched();
 }
 
@@ -590,7 +625,7 @@ kq_status kq_mxfp4_gemm_packed_lowrank(const uint8_t *codes_a, const uint8_t *pa
     const int64_t lim = (int64_t)1 << 31;
     const int64_t tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
     if ((int64_t)256 * (k / 2) >= lim || m * (k / 32) >= lim || n * (k / 32) >= lim ||
-        ((int64_t)255 * ldo + n) * 4 >= lim || tiles_m * tiles_n >= lim || (int64_t)256 * r * 4 + 32 >= lim)
+        ((int64_t)255 * ldo + n) * 4 >= lim || tiles_m * tiles_n >= (lim >> 1) || (int64_t)256 * r * 4 + 32 >= lim)
         return KQ_ERR_UNSUPPORTED;
     kq::g256::Geom g;
     g.m = m;
@@ -601,24 +636,12 @@ kq_status kq_mxfp4_gemm_packed_lowrank(const uint8_t *codes_a, const uint8_t *pa
     g.tiles_m = (int)tiles_m;
     g.tiles_n = (int)tiles_n;
     g.nwg = (int)(tiles_m * tiles_n);
-    g.vec_out = aligned(O, 16) && ldo % 4 == 0;
+    g.rows16 = aligned(O, 16) && ldo % 4 == 0;
     g.r = (int)r;
-    // whole rounds of full tiles, then the last partial round as half tiles (as in
-    // kq_mxfp4_gemm_packed)
-    const int ncu = kq::g256::cu_count();
-    const int rem = g.nwg % ncu;
-    const int nfull = (rem > 0 && 2 * rem <= ncu) ? g.nwg - rem : g.nwg;
-    g.tile_base = 0;
-    if (nfull > 0)
-        hipLaunchKernelGGL((kq::g256::gemm256_kernel<true, 256>), dim3((unsigned)nfull), dim3(kq::g256::kThreads), 0,
-                           (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, Z, codes_l,
-                           scales_l, O);
-    if (nfull < g.nwg) {
-        g.tile_base = nfull;
-        hipLaunchKernelGGL((kq::g256::gemm256_kernel<true, 128>), dim3((unsigned)(2 * (g.nwg - nfull))),
-                           dim3(kq::g256::kThreads), 0, (hipStream_t)stream, codes_a, packed_scales_a, codes_w,
-                           packed_scales_w, g, Z, codes_l, scales_l, O);
-    }
+    g.order = kq::g256::make_tile_order(g.nwg, kq::g256::cu_count());
+    hipLaunchKernelGGL((kq::g256::gemm256_kernel<true, false>), dim3((unsigned)kq::g256::tile_order_groups(g.order)),
+                       dim3(kq::g256::kThreads), 0, (hipStream_t)stream, codes_a, packed_scales_a, codes_w,
+                       packed_scales_w, g, Z, codes_l, scales_l, O);
     return launched();
 }
 

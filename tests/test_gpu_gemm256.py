@@ -83,9 +83,11 @@ def test_pack_scales_is_the_layout(torch_dev, kq, rows, k, seed):
 
 
 @pytest.mark.parametrize("m,n,k,seed", [(1, 1, 256, 1), (37, 70, 256, 2), (257, 513, 512, 3),
-                                        (300, 1100, 768, 4), (256, 256, 2304, 5), (1000, 700, 512, 6)])
+                                        (300, 1100, 768, 4), (256, 256, 2304, 5), (1000, 700, 512, 6),
+                                        (5632, 3000, 512, 9)])
 def test_packed_gemm_matches_oracle(torch_dev, kq, orc, m, n, k, seed):
-    """Seeded random MXFP4 operands (any code byte, scales around 2^0); ragged m and n."""
+    """Seeded random MXFP4 operands (any code byte, scales around 2^0); ragged m and n;
+    5632 x 3000 is 264 tiles, launched in the staggered order on 256 CUs."""
     torch = torch_dev
     case("packed gemm m=%d n=%d k=%d" % (m, n, k))
     ca, sa, cw, sw = operands(np.random.default_rng(seed), m, n, k)
@@ -158,25 +160,31 @@ def test_packed_gemm_lowrank_matches_oracle(torch_dev, kq, orc, m, n, k, r):
 
 
 def launch_split(torch, m, n):
-    """(full-tile workgroups, half-tile pairs) of a packed GEMM launch: whole rounds of
-    256 x 256 tiles (one per compute unit), then the last partial round as halves when
-    it is at most half a round."""
+    """(whole tiles, tiles split into halves, staggered order) of a packed GEMM launch:
+    whole rounds of 256 x 256 tiles (one per compute unit), the last partial round as
+    halves when it is at most half a round; staggered when the counts divide over the
+    eight XCDs (the rule of the library's work order)."""
     tiles = ((m + 255) // 256) * ((n + 255) // 256)
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     rem = tiles % ncu
-    nfull = tiles - rem if (rem > 0 and 2 * rem <= ncu) else tiles
-    return nfull, tiles - nfull
+    split = rem if (rem > 0 and 2 * rem <= ncu) else 0
+    staggered = split > 0 and tiles > rem and tiles % 8 == 0 and rem % 8 == 0 and ncu % 8 == 0
+    return tiles - split, split, staggered
 
 
-@pytest.mark.parametrize("m,n,k,r", [(6400, 3072, 512, 128), (6400, 3072, 512, 96), (4096, 2560, 256, 128)])
+@pytest.mark.parametrize("m,n,k,r", [(6400, 3072, 512, 128), (6400, 3072, 512, 96), (4096, 2560, 256, 128),
+                                     (5632, 3072, 512, 128), (5632, 3000, 256, 96)])
 def test_packed_gemm_lowrank_full_tiles_matches_oracle(torch_dev, kq, orc, m, n, k, r):
     """The full-tile low-rank kernel on more than one round of tiles, every element
     against the oracle's fp64 Eq. 11 (product plus Z deq(L)^T): 6400 x 3072 is 300
-    tiles, i.e. a round of 256 full tiles and 44 as half tiles; 4096 x 2560 is 160
-    tiles, all full. r = 96 leaves a partial last 64-wide chunk of the branch."""
+    tiles, i.e. a round of 256 full tiles and 44 as half tiles (plain order); 4096 x
+    2560 is 160 tiles, all full; 5632 x 3072 and 5632 x 3000 are 264 tiles in the
+    staggered order on 256 CUs (the latter with a partial last column tile). r = 96
+    leaves a partial last 64-wide chunk of the branch."""
     torch = torch_dev
-    nfull, nhalf = launch_split(torch, m, n)
-    case("packed gemm lowrank full tiles %dx%dx%d r=%d (%d full, %d as halves)" % (m, n, k, r, nfull, nhalf))
+    nfull, nsplit, stag = launch_split(torch, m, n)
+    case("packed gemm lowrank full tiles %dx%dx%d r=%d (%d whole, %d as halves, staggered %s)" %
+         (m, n, k, r, nfull, nsplit, stag))
     assert nfull > 0
     rng = np.random.default_rng(m + n + k + r + 1)
     ca, sa, cw, sw = operands(rng, m, n, k)
@@ -198,10 +206,12 @@ def test_packed_gemm_lowrank_full_tiles_matches_oracle(torch_dev, kq, orc, m, n,
 
 
 @pytest.mark.parametrize("m,n,k,pad,seed", [(1000, 700, 512, 0, 21), (300, 1100, 768, 3, 22), (257, 513, 256, 1, 23),
+                                            (5632, 3072, 256, 0, 24), (5632, 3000, 256, 5, 25),
                                             (18432, 3072, 3072, 0, 24)])
 def test_packed_gemm_bf16_is_rounded_fp32(torch_dev, kq, m, n, k, pad, seed):
     """The bf16-output form equals the fp32 form rounded to nearest even, bit for bit, for
-    aligned (8-byte stores) and odd-stride (2-byte stores) outputs; padding stays untouched."""
+    aligned (whole 16-byte row pieces) and odd-stride or partial-tile (2-byte element
+    stores) outputs; padding stays untouched."""
     torch = torch_dev
     case("packed gemm bf16 m=%d n=%d k=%d ldo=%d" % (m, n, k, n + pad))
     ca, sa, cw, sw = operands(np.random.default_rng(seed), m, n, k)
