@@ -14,7 +14,10 @@
 //  - a stage covers 256 k, i.e. 128 code bytes (one full cache line) per row;
 //  - operands go straight from memory into LDS (buffer loads with the LDS bit),
 //    two stages double-buffered (2 x 68 KB), the next stage's 17 loads per wave
-//    issued among the current stage's first 16 matrix instructions;
+//    issued one after each of the current stage's first 17 matrix instructions
+//    (packed tighter, the texture unit's queue stalls the matrix issue; spread
+//    over three k steps, they arrive late), and waited for 3/4 of the way
+//    through the stage's last k step;
 //  - scales are read in a GEMM-ready layout (kq_pack_mxfp4_scales): the 8 scale
 //    bytes of one 256-k stage of consecutive rows are consecutive, so a stage's
 //    scales for 256 rows are one 2 KB run instead of 256 scattered lines, and
@@ -58,6 +61,8 @@ namespace g256 {
 constexpr int kThreads = 256;
 constexpr int kTile = 256;                      // output rows per tile; columns TN = 256 or 128
 constexpr int kGroupM = 4;                      // row tiles per band of the tile order
+constexpr int kLoadSteps = 2;                   // k steps of a stage that carry the next stage's loads
+constexpr int kNonTemporal = 2;                 // cache-policy operand of a buffer access: nt
 
 // LDS layout of a stage for TN output columns: A codes [256][128], W codes [TN][128],
 // A scales [256][8], W scales [TN][8] (68 KB for TN = 256, 51 KB for TN = 128)
@@ -286,40 +291,62 @@ __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, con
     read_scl(0, S);
     read_frags(0, 0, F0);
 
-    // Stage s (s + 1 < stages): the buffer of stage s + 1 held stage s - 1, whose
-    // last reads came before the previous barrier, so its loads go out during
-    // step 0; the barrier after step 2 makes them visible and ends every wave's
-    // reads of stage s before stage s + 2 reuses the buffer.
-    for (int s = 0; s + 1 < g.stages; ++s) {
-        read_frags(s, 1, F1);
-        __builtin_amdgcn_sched_barrier(0);
-        // the 8 + LW code loads and the scale load of stage s + 1 spread over the
-        // 4 NB matrix instructions of step 0
+    // load l of stage s: 0 .. 8 + LW - 1 the code loads, 8 + LW the scale load
+    constexpr int kLoads = 8 + LW + 1, kPerStep = (kLoads + kLoadSteps - 1) / kLoadSteps;
+    static_assert(kPerStep <= 4 * NB && kLoadSteps <= 3, "every load of a stage needs a slot before the wait");
+    auto issue_load = [&](int s, int l) {
+        if (l < 8 + LW) issue_code(s, l);
+        else issue_scl(s);
+    };
+    // step j of stage s with stage s + 1's loads kPerStep j .. placed one after
+    // each matrix instruction (the loads are spread over the first kLoadSteps
+    // steps, so that the texture unit's queue never stalls the matrix issue)
+    auto step_loading = [&](const Frag<NB> &F, const Scl<NB> &S, auto jc, int s) {
+        constexpr int j = decltype(jc)::value;
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const int slot = NB * a + b;
-                mma(F0, S, J0(), a, b);
-                pin(a, b);
-                issue_code(s + 1, slot);
-                if (slot + 4 * NB < 8 + LW) issue_code(s + 1, slot + 4 * NB);
-                if (slot == 7) issue_scl(s + 1);
+                const int l = kPerStep * j + NB * a + b;
+                mma(F, S, jc, a, b);
+                if (j < kLoadSteps && NB * a + b < kPerStep && l < kLoads) {
+                    pin(a, b);
+                    issue_load(s + 1, l);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
+    };
+
+    // Stage s (s + 1 < stages): the buffer of stage s + 1 held stage s - 1, whose
+    // last reads came before the previous barrier, so its loads go out during
+    // steps 0 .. kLoadSteps - 1; the barrier after step 2 makes them visible and
+    // ends every wave's reads of stage s before stage s + 2 reuses the buffer.
+    for (int s = 0; s + 1 < g.stages; ++s) {
+        read_frags(s, 1, F1);
+        __builtin_amdgcn_sched_barrier(0);
+        step_loading(F0, S, J0(), s);
         read_frags(s, 2, F0);
         __builtin_amdgcn_sched_barrier(0);
-        step(F1, S, J1());
+        step_loading(F1, S, J1(), s);
         __builtin_amdgcn_sched_barrier(0);
         read_frags(s, 3, F1);
         __builtin_amdgcn_sched_barrier(0);
-        step(F0, S, J2());
+        step_loading(F0, S, J2(), s);
+        __builtin_amdgcn_sched_barrier(0);
+        // step 3 split around the wait (3 of its 4 row blocks before): the loads
+        // get most of a step more, and the reads of stage s + 1's first
+        // fragments overlap the last row block
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) mma(F1, S, J3(), a, b);
         __builtin_amdgcn_sched_barrier(0);
         wait_loads_and_lds_then_barrier();
         read_scl(s + 1, Sn);
         read_frags(s + 1, 0, F0);
         __builtin_amdgcn_sched_barrier(0);
-        step(F1, S, J3());
+#pragma unroll
+        for (int b = 0; b < NB; ++b) mma(F1, S, J3(), 3, b);
         __builtin_amdgcn_sched_barrier(0);
         S = Sn;
     }
@@ -459,7 +486,9 @@ __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, con
             const int col = B16 ? wn + 8 * c : wn + 64 * pass + 4 * c;  // from n0
             const int orow = wm + row;                                    // from m0
             if (whole) {
-                __builtin_amdgcn_raw_buffer_store_b128(v, ro, (uint32_t)((orow * g.ldo + col) * esz), 0, 0);
+                // non-temporal: O is not read again here, so it should not push the
+                // operand lines that the other workgroups still read out of L2
+                __builtin_amdgcn_raw_buffer_store_b128(v, ro, (uint32_t)((orow * g.ldo + col) * esz), 0, kNonTemporal);
             } else if (B16) {
                 // plain stores: with 2-byte buffer stores the compiler kept the
                 // descriptor in vector registers and looped over it
