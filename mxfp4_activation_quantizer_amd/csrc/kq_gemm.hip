@@ -170,9 +170,16 @@ __global__ __launch_bounds__(kThreads) void lowrank_project_kernel(const uint16_
 // chunks permuted (chunk q of column c at slot q ^ (c % 16)), so the 16 columns
 // a matrix read touches fall in distinct banks and one direct-to-LDS load (4
 // columns, 1 KB) stays contiguous. Measured on 18432 x 3072, r = 128: 39 us,
-// against 91 us with one producer wave, one step ahead and 64-row tiles; the
-// step time followed how fast R reached LDS, not the X stream or the matrix
-// work.
+// against 91 us with one producer wave, one step ahead and 64-row tiles.
+// Timing variants (outputs wrong, same launch): without the R and X loads 23
+// us, without R 29 us, without X 24 us; with a third R slot and four X steps
+// in flight, or with consumer waves of two 16-row groups (R fragments read once
+// for 32 rows), unchanged or slower. The remaining floor is the in-CU work: the
+// 16 x 16 x 32 instruction issues at half the rate of the 32 x 32 x 16 form on
+// gfx950 (1.3 against 2.45 PFLOP/s measured), and two of the five consumer
+// waves share a SIMD. A 32 x 32 x 16 form with 32-row waves and 128-row tiles
+// ran at 83 us: its X loads cover 32 rows x 32 bytes per instruction, and the
+// X stream alone cost 47 us there.
 constexpr int kProjWaves = 5;                    // consumer waves, 16 rows each
 constexpr int kProjRows = 16 * kProjWaves;       // rows of X per workgroup
 constexpr int kProjProducers = 2;                // waves moving R into LDS
@@ -226,13 +233,16 @@ __global__ __launch_bounds__(64 * (kProjWaves + kProjProducers)) void lowrank_pr
         // wait for the oldest step in flight while the `younger` steps issued after
         // it (kProjLoads loads each) stay in flight, then the step's barrier
         auto wait_then_barrier = [&](int64_t younger) {
-            if (younger >= 1) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kProjLoads) : "memory");
+            if (younger >= 2) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kProjLoads) : "memory");
+            else if (younger == 1) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kProjLoads) : "memory");
             else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         };
-        static_assert(kAhead == 2, "wait_then_barrier covers at most one younger step");
+        static_assert(kAhead >= 1 && kAhead <= 3 && 2 * kProjLoads <= 63,
+                      "wait_then_barrier covers at most two younger steps");
         for (int s = 0; s < kAhead; ++s)
             if (s < steps_up) issue(s);
-        wait_then_barrier(steps_up > 1 ? 1 : 0);
+        // the first step's slice must have landed; the later ones may still be in flight
+        wait_then_barrier((kAhead < steps_up ? kAhead : steps_up) - 1);
         for (int64_t st = 0; st < steps_up; ++st) {
             // the slot of step st + kAhead held step st - 1, read before the last barrier
             if (st + kAhead < steps_up) issue(st + kAhead);
