@@ -281,6 +281,37 @@ __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, con
     using J2 = std::integral_constant<int, 2>;
     using J3 = std::integral_constant<int, 3>;
 
+    // LDS after the product: Z hi [256][64] bf16, Z lo likewise, deq(L) [256][64]
+    // bf16, rows of 128 bytes with the 16-byte chunks permuted as the codes are
+    uint8_t *zh = smem, *zl = smem + 32768, *ll = smem + 65536;
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(Z + m0 * g.r), (short)0, (int)(rows_a * g.r * 4), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rcl = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(cl + n0 * (g.r / 2)), (short)0, (int)(rows_w * (g.r / 2)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsl = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(sl + n0 * (g.r / 32)), (short)0, (int)(rows_w * (g.r / 32)), 0x00020000);
+    // (LR) a chunk (64 of r) is staged by 8 passes of 32 rows: lane t & 7 of row
+    // 32 p + t / 8 takes 8 consecutive columns, so 8 lanes read a row's 256
+    // bytes of Z (32 of L's code bytes) together; the next chunk's loads go
+    // out before this chunk's matrix work (a chunk past r reads zeros)
+    u32x4_t zr[8][2];
+    uint32_t lc[8], ls[8];
+    const int cc = t & 7;
+    auto load_chunk = [&](int r0) {
+        const int kc = r0 + 8 * cc;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int row = 32 * p + (t >> 3);
+            const uint32_t zo = kc < g.r ? (uint32_t)((row * g.r + kc) * 4) : 0x80000000u;
+            zr[p][0] = __builtin_amdgcn_raw_buffer_load_b128(rz, zo, 0, 0);
+            zr[p][1] = __builtin_amdgcn_raw_buffer_load_b128(rz, zo + 16u, 0, 0);
+            const uint32_t co = kc < g.r ? (uint32_t)(row * (g.r / 2) + kc / 2) : 0x80000000u;
+            const uint32_t so = kc < g.r ? (uint32_t)(row * (g.r / 32) + kc / 32) : 0x80000000u;
+            lc[p] = __builtin_amdgcn_raw_buffer_load_b32(rcl, co, 0, 0);
+            ls[p] = __builtin_amdgcn_raw_buffer_load_b8(rsl, so, 0, 0);
+        }
+    };
+
     if (g.stages > 0) {  // k == 0: O = 0
     issue_scl(0);
 #pragma unroll
@@ -352,6 +383,8 @@ __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, con
     }
     {
         const int s = g.stages - 1;
+        // the branch's first chunk is in flight during the last stage
+        if (LR) load_chunk(0);
         read_frags(s, 1, F1);
         step(F0, S, J0());
         read_frags(s, 2, F0);
@@ -360,40 +393,11 @@ __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, con
         step(F0, S, J2());
         step(F1, S, J3());
     }
+    } else if (LR) {
+        load_chunk(0);
     }
 
     if (LR) {
-        // LDS after the product: Z hi [256][64] bf16, Z lo likewise, deq(L) [256][64]
-        // bf16, rows of 128 bytes with the 16-byte chunks permuted as the codes are
-        uint8_t *zh = smem, *zl = smem + 32768, *ll = smem + 65536;
-        const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float *>(Z + m0 * g.r), (short)0, (int)(rows_a * g.r * 4), 0x00020000);
-        const __amdgpu_buffer_rsrc_t rcl = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t *>(cl + n0 * (g.r / 2)), (short)0, (int)(rows_w * (g.r / 2)), 0x00020000);
-        const __amdgpu_buffer_rsrc_t rsl = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t *>(sl + n0 * (g.r / 32)), (short)0, (int)(rows_w * (g.r / 32)), 0x00020000);
-        // a chunk (64 of r) is staged by 8 passes of 32 rows: lane t & 7 of row
-        // 32 p + t / 8 takes 8 consecutive columns, so 8 lanes read a row's 256
-        // bytes of Z (32 of L's code bytes) together; the next chunk's loads go
-        // out before this chunk's matrix work (a chunk past r reads zeros)
-        u32x4_t zr[8][2];
-        uint32_t lc[8], ls[8];
-        const int cc = t & 7;
-        auto load_chunk = [&](int r0) {
-            const int kc = r0 + 8 * cc;
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                const int row = 32 * p + (t >> 3);
-                const uint32_t zo = kc < g.r ? (uint32_t)((row * g.r + kc) * 4) : 0x80000000u;
-                zr[p][0] = __builtin_amdgcn_raw_buffer_load_b128(rz, zo, 0, 0);
-                zr[p][1] = __builtin_amdgcn_raw_buffer_load_b128(rz, zo + 16u, 0, 0);
-                const uint32_t co = kc < g.r ? (uint32_t)(row * (g.r / 2) + kc / 2) : 0x80000000u;
-                const uint32_t so = kc < g.r ? (uint32_t)(row * (g.r / 32) + kc / 32) : 0x80000000u;
-                lc[p] = __builtin_amdgcn_raw_buffer_load_b32(rcl, co, 0, 0);
-                ls[p] = __builtin_amdgcn_raw_buffer_load_b8(rsl, so, 0, 0);
-            }
-        };
-        load_chunk(0);
         for (int r0 = 0; r0 < g.r; r0 += 64) {
             // every wave is done with the previous contents of LDS
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
