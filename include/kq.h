@@ -185,9 +185,11 @@ kq_status kq_mxfp4_gemm(const uint8_t *codes_a, const uint8_t *scales_a, const u
 
 /*
  * The same W4A4 GEMM as kq_mxfp4_gemm (identical arguments, layouts and error
- * rules) on 128 x 512 output tiles of eight waves, k advancing 128 per stage.
- * Both kernels accumulate one 128-k block per matrix instruction in increasing
- * k, so their results are bit-identical.
+ * rules) on 128 x 512 output tiles of eight waves, k advancing 128 per stage,
+ * with the 32 x 32 x 64 scaled instruction (one 64-k block per instruction,
+ * increasing k) as kq_mxfp4_gemm_packed: bit-identical to that one where it
+ * applies (k % 256 == 0); against kq_mxfp4_gemm (128-k blocks), agreement to
+ * fp32 rounding of the partial sums.
  * m rows of codes_a (k/2 bytes each) and 512 rows of codes_w must each span
  * fewer than 2^31 bytes per tile (KQ_ERR_UNSUPPORTED otherwise).
  */
@@ -281,7 +283,7 @@ kq_status kq_mxfp4_gemm_packed_lowrank(const uint8_t *codes_a, const uint8_t *pa
  * codes can differ from the standalone quantizer's at rounding ties (both
  * meet the same tolerance against the exact transform). When every block
  * admits it, O is bit-identical to kq_transform_quantize_mxfp4 followed by
- * kq_mxfp4_gemm.
+ * kq_mxfp4_gemm_wide (the same product kernel).
  *   A         device, bf16 bits [m][lda], lda >= k, lda % 8 == 0, 16-byte aligned
  *   factors   device, fp32 [k/32][5][2][2] (as kq_transform_quantize_mxfp4), 16-byte aligned
  *   codes_w   device, [n][k/2] bytes, 16-byte aligned

@@ -7,15 +7,19 @@
 // product's prologue, so the activation's codes never leave the chip.
 //
 // Tiling. A workgroup (8 waves) computes 128 rows x 512 columns of O; wave w
-// owns rows 64 (w >> 2) .. +63 and columns 128 (w & 3) .. +127 as 4 x 8 tiles of
-// 16 x 16 (v_mfma_scale_f32_16x16x128_f8f6f4, both operands E2M1 with E8M0
-// scales: lane l supplies row l % 16 and the 32 consecutive k of group l / 16,
-// receives rows 4 (l / 16) + t of column l % 16). k advances 128 per stage,
-// one MX group of four E8M0 bytes per row, double-buffered in LDS with one
-// barrier per stage; the next stage's activation loads are in flight while the
-// current stage's matrix instructions run. Staged rows are 80 bytes (64 code
-// bytes + 16 pad) so the 16 rows an operand read touches fall in distinct
-// banks.
+// owns rows 64 (w >> 2) .. +63 and columns 128 (w & 3) .. +127 as 2 x 4 tiles of
+// 32 x 32 (v_mfma_scale_f32_32x32x64_f8f6f4, both operands E2M1 with E8M0
+// scales; on gfx950 it issues FP4 at twice the rate of the 16 x 16 x 128 form).
+// Operands are swapped (the W fragment first), so lane l supplies row l % 32
+// of each fragment and MX block 2 j + l / 32 of k step j, and receives O row
+// l % 32, columns 8 q + 4 (l / 32) + 0..3 of the W fragment in accumulator
+// registers 4 q .. 4 q + 3 -- the instruction, operand order and k order of
+// the packed-scale GEMM, whose results this kernel reproduces bit for bit. k
+// advances 128 per stage (two k steps), one MX group of four E8M0 bytes per
+// row, double-buffered in LDS with one barrier per stage; the next stage's
+// activation loads are in flight while the current stage's matrix instructions
+// run. Staged rows are 80 bytes (64 code bytes + 16 pad), so the 16 rows of one
+// pass of a fragment read fall in distinct banks.
 //
 // Why the wide tile: with the transform in the prologue, every workgroup that
 // shares an activation row block repeats its transform, n / 512 times here
@@ -38,6 +42,7 @@ constexpr int kM = 128, kN = 512;
 constexpr int kRow = 80;  // staged bytes per row: 64 code bytes (128 k) + 16 pad
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 struct Geom {
     int64_t m, n, k, lda, ldo;
@@ -267,13 +272,15 @@ __global__ __launch_bounds__(kThreads) void w4a4_kernel(const void *__restrict__
     const int64_t tm = blockIdx.x / g.tiles_n, tn = blockIdx.x % g.tiles_n;
     const int64_t m0 = tm * kM, n0 = tn * kN;
     const int wm = (wave >> 2) * 64, wn = (wave & 3) * 128;
-    const int r = lane & 15, grp = lane >> 4;
+    const int r = lane & 31, hi = lane >> 5;
 
-    floatx4_t acc[4][8];
+    floatx16_t acc[2][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 8; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
     ARegs ra;
     WRegs rw;
@@ -298,23 +305,41 @@ __global__ __launch_bounds__(kThreads) void w4a4_kernel(const void *__restrict__
         const bool more = s + 1 < g.stages;
         if (more) fetch_a<PRO>(A, sa, g, m0, s + 1, ra);
 
-        i32x8_t av[4];
-        int asc[4];
+        // k step j of the stage (64 k): lane (r, hi) supplies row r of each
+        // fragment and MX block 2 j + hi (16 code bytes); its scale dword is
+        // rearranged so that byte j holds that block's scale (the instruction's
+        // byte select is uniform across lanes)
+        auto lane_scales = [&](uint32_t d) {
+            return hi ? ((d >> 8) & 0xFFu) | ((d >> 16) & 0xFF00u) : (d & 0xFFu) | ((d >> 8) & 0xFF00u);
+        };
+        int asc[2], bsc[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const uint4 q = *reinterpret_cast<const uint4 *>(a_lds[cur] + (wm + a * 16 + r) * kRow + grp * 16);
-            av[a] = i32x8_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-            asc[a] = (int)((as_lds[cur][wm + a * 16 + r] >> (8 * grp)) & 0xFFu);
-        }
+        for (int a = 0; a < 2; ++a) asc[a] = (int)lane_scales(as_lds[cur][wm + 32 * a + r]);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const uint4 q = *reinterpret_cast<const uint4 *>(b_lds[cur] + (wn + b * 16 + r) * kRow + grp * 16);
-            const i32x8_t bv = i32x8_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-            const int bsc = (int)((bs_lds[cur][wn + b * 16 + r] >> (8 * grp)) & 0xFFu);
+        for (int b = 0; b < 4; ++b) bsc[b] = (int)lane_scales(bs_lds[cur][wn + 32 * b + r]);
+        auto frag = [&](const uint8_t *base, int row, int j) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(base + row * kRow + (2 * j + hi) * 16);
+            return i32x8_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+        };
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[a], bv, acc[a][b], 4, 4, 0, asc[a], 0,
-                                                                             bsc);
+        for (int j = 0; j < 2; ++j) {
+            i32x8_t av[2], bv[4];
+#pragma unroll
+            for (int a = 0; a < 2; ++a) av[a] = frag(a_lds[cur], wm + 32 * a + r, j);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) bv[b] = frag(b_lds[cur], wn + 32 * b + r, j);
+            // swapped operands (W fragment first), so a lane receives output row r
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    if (j == 0)
+                        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv[b], av[a], acc[a][b], 4, 4, 0,
+                                                                                    bsc[b], 0, asc[a]);
+                    else
+                        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv[b], av[a], acc[a][b], 4, 4, 1,
+                                                                                    bsc[b], 1, asc[a]);
+                }
         }
         if (more) fetch_w(cw, sw, g, n0, s + 1, rw);
         // coefficients two stages ahead go to the buffer stage s's were in
@@ -326,17 +351,28 @@ __global__ __launch_bounds__(kThreads) void w4a4_kernel(const void *__restrict__
         __syncthreads();
     }
 
+    // lane (r, hi): O row wm + 32 a + r, columns wn + 32 b + 8 q + 4 hi + 0..3
+    const bool vec = (reinterpret_cast<uintptr_t>(O) & 15) == 0 && g.ldo % 4 == 0;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 2; ++a) {
+        const int64_t row = m0 + wm + 32 * a + r;
+        if (row >= g.m) continue;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const int64_t col = n0 + wn + b * 16 + r;
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = m0 + wm + a * 16 + grp * 4 + i;
-                if (row < g.m && col < g.n) O[row * g.ldo + col] = acc[a][b][i];
+            for (int q = 0; q < 4; ++q) {
+                const int64_t col = n0 + wn + 32 * b + 8 * q + 4 * hi;
+                float *o = O + row * g.ldo + col;
+                if (vec && col + 3 < g.n) {
+                    *reinterpret_cast<floatx4_t *>(o) =
+                        floatx4_t{acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (col + e < g.n) o[e] = acc[a][b][4 * q + e];
+                }
             }
-        }
+    }
 }
 
 }  // namespace w4

@@ -52,7 +52,10 @@ def weights_mxfp4(torch, kq, W, fac):
                                         (300, 1100, 416, 4), (129, 513, 96, 5), (64, 600, 4096, 6)])
 def test_wide_gemm_matches_gemm_and_oracle(torch_dev, kq, orc, m, n, k, seed):
     """Seeded random MXFP4 operands (any code byte, scales around 2^0); ragged m and n,
-    k not a multiple of 128 and k/32 not a multiple of 4."""
+    k not a multiple of 128 and k/32 not a multiple of 4. The wide kernel runs the
+    32 x 32 x 64 instruction in ascending k, as the packed-scale GEMM does: bit-identical
+    to it where that one applies (k % 256 == 0); against the 16 x 16 x 128 kernel and
+    the fp64 product, fp32 accumulation accuracy."""
     torch = torch_dev
     case("wide gemm m=%d n=%d k=%d" % (m, n, k))
     rng = np.random.default_rng(seed)
@@ -63,12 +66,17 @@ def test_wide_gemm_matches_gemm_and_oracle(torch_dev, kq, orc, m, n, k, seed):
     ops = [dev(torch, x) for x in (ca, sa, cw, sw)]
     O_wide = kq.mxfp4_gemm_wide(*ops)
     O_ref_kernel = kq.mxfp4_gemm(*ops)
+    if k % 256 == 0:
+        O_packed = kq.mxfp4_gemm_packed(ops[0], kq.pack_mxfp4_scales(ops[1]), ops[2], kq.pack_mxfp4_scales(ops[3]))
     torch.cuda.synchronize()
-    assert torch.equal(O_wide, O_ref_kernel)
+    if k % 256 == 0:
+        assert torch.equal(O_wide, O_packed)
     ref = orc.gemm_dequant(ca, sa, cw, sw, k)
     got = O_wide.cpu().numpy().astype(np.float64)
     absdot = np.abs(orc.dequantize(ca, sa, k)) @ np.abs(orc.dequantize(cw, sw, k)).T
     assert np.all(np.abs(got - ref) <= 64 * 2.0 ** -24 * absdot + 1e-30)
+    other = O_ref_kernel.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - other) <= 128 * 2.0 ** -24 * absdot + 1e-30)
 
 
 def test_wide_gemm_padded_output_and_guard(torch_dev, kq):
@@ -85,7 +93,7 @@ def test_wide_gemm_padded_output_and_guard(torch_dev, kq):
     buf = torch.full((m * ldo + 1024,), 7.5, dtype=torch.float32, device="cuda")
     O = buf[: m * ldo].view(m, ldo)[:, :n]
     kq.mxfp4_gemm_wide(*ops, out=O)
-    ref = kq.mxfp4_gemm(*ops)
+    ref = kq.mxfp4_gemm_packed(ops[0], kq.pack_mxfp4_scales(ops[1]), ops[2], kq.pack_mxfp4_scales(ops[3]))
     torch.cuda.synchronize()
     assert torch.equal(O, ref)
     assert bool((buf[: m * ldo].view(m, ldo)[:, n:] == 7.5).all())
@@ -95,7 +103,7 @@ def test_wide_gemm_padded_output_and_guard(torch_dev, kq):
 @pytest.mark.parametrize("m,k,n,pad", [(37, 160, 70, 0), (300, 3072, 600, 8), (129, 416, 513, 0)])
 def test_fused_layer_matches_pipeline_small(torch_dev, kq, orc, m, k, n, pad):
     """LU-perturbed factors (every block in shear form): the fused layer equals the
-    quantizer followed by the GEMM bit for bit, and the oracle's pipeline within fp32
+    quantizer followed by the wide GEMM bit for bit (the same product kernel), and the oracle's pipeline within fp32
     accumulation accuracy of the same dequantized operands where the codes agree."""
     torch = torch_dev
     case("fused layer m=%d k=%d n=%d pad=%d" % (m, k, n, pad))
@@ -108,7 +116,7 @@ def test_fused_layer_matches_pipeline_small(torch_dev, kq, orc, m, k, n, pad):
     fac_d = dev(torch, fac)
     O_fused = kq.transform_quantize_mxfp4_gemm(A, fac_d, cw, sw)
     ca, sa = kq.transform_quantize_mxfp4(A, fac_d)
-    O_pipe = kq.mxfp4_gemm(ca, sa, cw, sw)
+    O_pipe = kq.mxfp4_gemm_wide(ca, sa, cw, sw)
     torch.cuda.synchronize()
     assert torch.equal(O_fused, O_pipe)
     # against the oracle's pipeline on the same seeded inputs
@@ -138,7 +146,7 @@ def test_fused_layer_nonshear_blocks_against_oracle(torch_dev, kq, orc):
     fac_d = dev(torch, fac)
     O_fused = kq.transform_quantize_mxfp4_gemm(A, fac_d, cw, sw)
     ca, sa = kq.transform_quantize_mxfp4(A, fac_d)
-    O_pipe = kq.mxfp4_gemm(ca, sa, cw, sw)
+    O_pipe = kq.mxfp4_gemm_wide(ca, sa, cw, sw)
     torch.cuda.synchronize()
     ca_r, sa_r, _ = orc.transform_quantize(A_full, fac, want_y=False)
     cw_r, sw_r = orc.quantize_f64(orc.inverse_fold(W, fac))
@@ -163,7 +171,7 @@ def test_fused_layer_exact_factors_reduce_to_plain_quantizer(torch_dev, kq):
     sw = dev(torch, rng.integers(120, 134, (n, k // 32), dtype=np.uint8))
     O_fused = kq.transform_quantize_mxfp4_gemm(A, fac, cw, sw)
     ca, sa = kq.quantize_mxfp4(A)
-    O_q = kq.mxfp4_gemm(ca, sa, cw, sw)
+    O_q = kq.mxfp4_gemm_wide(ca, sa, cw, sw)
     torch.cuda.synchronize()
     # quantize-only writes the sign of exact zeros from the bf16 input; the transform
     # path's y is fp32 and the sign of a zero product does not change the product
@@ -172,7 +180,7 @@ def test_fused_layer_exact_factors_reduce_to_plain_quantizer(torch_dev, kq):
 
 def test_fused_layer_flux_config4(torch_dev, kq, orc):
     """The 18432x3072 FLUX activations and the 3072x3072 folded weights. The fused layer
-    equals the two-launch pipeline bit for bit on the whole output, so its activation
+    equals the two-launch pipeline (quantizer, wide GEMM) bit for bit on the whole output, so its activation
     codes are the standalone quantizer's (checked against the oracle by the quantizer's
     parity rule elsewhere). On sampled rows: the product equals the fp64 product of those
     operands dequantized, to fp32 accumulation accuracy; and rows whose activation codes
@@ -189,7 +197,7 @@ def test_fused_layer_flux_config4(torch_dev, kq, orc):
     A = dev_bf16(torch, w.A)
     O_fused = kq.transform_quantize_mxfp4_gemm(A, fac_d, cw, sw)
     ca, sa = kq.transform_quantize_mxfp4(A, fac_d)
-    O_pipe = kq.mxfp4_gemm(ca, sa, cw, sw)
+    O_pipe = kq.mxfp4_gemm_wide(ca, sa, cw, sw)
     torch.cuda.synchronize()
     assert torch.equal(O_fused, O_pipe)
     rng = np.random.default_rng(8)
