@@ -60,6 +60,10 @@ def parse():
                     help="skip the other configs, the MFMA form, the fold and the W4A4 GEMM timings")
     ap.add_argument("--tensor", type=int, choices=[3072, 12288], default=None,
                     help="time only the tensor with this d (for profiler runs)")
+    ap.add_argument("--gemm-launches", type=int, default=0, metavar="N",
+                    help="launch only the packed-scale W4A4 GEMM N times on seeded random MXFP4 operands "
+                         "of --gemm-shape (for counter runs), print its event median, and exit")
+    ap.add_argument("--gemm-shape", default="18432x3072x3072", help="m x n x k for --gemm-launches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, 10 times (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -551,6 +555,23 @@ def summarize_pmc(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_json):
     print(json.dumps(out, indent=1))
 
 
+def gemm_launches(n, shape):
+    """The packed-scale W4A4 GEMM alone, n launches (fp32 output), for counter runs."""
+    import torch
+
+    import mxfp4_activation_quantizer_amd as kq
+    m, nn, k = (int(x) for x in shape.split("x"))
+    g = torch.Generator(device="cuda").manual_seed(5)
+    ca = torch.randint(0, 256, (m, k // 2), dtype=torch.uint8, device="cuda", generator=g)
+    cw = torch.randint(0, 256, (nn, k // 2), dtype=torch.uint8, device="cuda", generator=g)
+    sa = torch.randint(118, 130, (m, k // 32), dtype=torch.uint8, device="cuda", generator=g)
+    sw = torch.randint(118, 130, (nn, k // 32), dtype=torch.uint8, device="cuda", generator=g)
+    psa, psw = kq.pack_mxfp4_scales(sa), kq.pack_mxfp4_scales(sw)
+    O = torch.empty((m, nn), dtype=torch.float32, device="cuda")
+    d = _events_us(torch, lambda: kq.mxfp4_gemm_packed(ca, psa, cw, psw, out=O), n, 2)
+    log("packed gemm %s: %d launches, median %.1f us" % (shape, n, float(np.median(d))))
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -558,6 +579,9 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.gemm_launches > 0:
+        gemm_launches(args.gemm_launches, args.gemm_shape)
         return
     if args.gpus != 1:
         print("bench.py: measures one GPU only (the quantizer needs no collectives); "
