@@ -35,10 +35,10 @@ ROTATE_BYTES = 512 << 20
 WORKLOAD = ("flux_18432x3072", "flux_18432x12288")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_flux_18432x12288.json")
 # device kernels behind each timed entry point (as rocprofv3 names them)
-KERNEL_NAMES = {"fused": "kq::rowwave_kernel<2, 0, 4, 4> (fused transform + MXFP4)",
-                "smoothquant": "kq::rowwave_kernel<1, 0, 8, 4> (SmoothQuant + MXFP4)",
+KERNEL_NAMES = {"fused": "kq::rowwave_kernel<2, 0, 4, 4, false> (fused transform + MXFP4)",
+                "smoothquant": "kq::rowwave_kernel<1, 0, 8, 4, false> (SmoothQuant + MXFP4)",
                 "quantize": "kq::flat_quantize_kernel (quantize-only)"}
-FUSED_KERNEL = "rowwave_kernel<2, 0, 4, 4>"
+FUSED_KERNEL = "rowwave_kernel<2, 0, 4, 4, false>"
 
 
 def log(msg):
@@ -292,6 +292,15 @@ def extras(torch, kq, synth, flux_sets, reps=100, warmup=20):
         kq.mxfp4_gemm_packed(ca, psa, cw, psw, out=O)
     out["w4a4_layer_fused_18432x3072x3072"]["pipeline_packed_region_us"] = round(
         float(np.median(_events_us(torch, pipeline_packed, 20, 3))), 1)
+    # the quantizer writing the packed scale layout itself: two launches
+    pq = psa
+    def pipeline_packed_quantizer():
+        kq.transform_quantize_mxfp4_packed(A, fac, codes=ca, packed_scales=pq)
+        kq.mxfp4_gemm_packed(ca, pq, cw, psw, out=O)
+    out["w4a4_layer_fused_18432x3072x3072"]["quantizer_packed_scales_us"] = round(float(np.median(
+        _events_us(torch, lambda: kq.transform_quantize_mxfp4_packed(A, fac, codes=ca, packed_scales=pq), 20, 3))), 1)
+    out["w4a4_layer_fused_18432x3072x3072"]["pipeline_packed_quantizer_region_us"] = round(
+        float(np.median(_events_us(torch, pipeline_packed_quantizer, 20, 3))), 1)
     log("fused layer: %s" % out["w4a4_layer_fused_18432x3072x3072"])
     out["w4a4_layer_lowrank_18432x3072x3072_r128"] = lowrank_layer_timing(torch, kq, A, fac, cw, sw, W)
     log("low-rank layer: %s" % out["w4a4_layer_lowrank_18432x3072x3072_r128"])
@@ -342,6 +351,14 @@ def lowrank_layer_timing(torch, kq, A, fac, cw, sw, W, r=128, reps=20):
         kq.pack_mxfp4_scales(sa, out=psa)
         kq.mxfp4_gemm_packed_lowrank(ca, psa, cw, psw, Z, cl, sl, out=O)
     res["layer_with_branch_packed_region_us"] = med(layer_packed)
+
+    # the same with the quantizer writing the packed scales itself (four launches)
+    def layer_packed_quantizer():
+        kq.transform_quantize_mxfp4_packed(A, fac, codes=ca, packed_scales=psa, y16=y16)
+        kq.dequantize_mxfp4_bf16(cr, sr, out=r16)
+        kq.lowrank_project_bf16(y16, r16, out=Z)
+        kq.mxfp4_gemm_packed_lowrank(ca, psa, cw, psw, Z, cl, sl, out=O)
+    res["layer_with_branch_packed_quantizer_region_us"] = med(layer_packed_quantizer)
     return res
 
 

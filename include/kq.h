@@ -329,6 +329,25 @@ kq_status kq_transform_quantize_mxfp4_y16(const uint16_t *A, int64_t m, int64_t 
                                           kq_stream_t stream);
 
 /*
+ * kq_transform_quantize_mxfp4 (or, with y16, kq_transform_quantize_mxfp4_y16)
+ * with the E8M0 scales written straight in the layout kq_pack_mxfp4_scales
+ * makes (the layout kq_mxfp4_gemm_packed* read): the same codes and the same
+ * scale bytes, bit for bit, rearranged as [d/256][m][8] with the even blocks
+ * of each 256-channel stage first -- Sec. 3.1's quantizer of Sec. 3.2 Eq. 5's
+ * transform, its output laid out for Sec. 1 Eq. 2's product, so the layer
+ * needs no separate re-layout launch.
+ *   A, m, d, lda, factors, codes   as kq_transform_quantize_mxfp4
+ *   packed_scales                  device, m d/32 bytes (no alignment needed)
+ *   y16                            device, bf16 bits [m][d], 16-byte aligned, or
+ *                                  NULL (no bf16 output)
+ * d % 256 == 0 (KQ_ERR_SHAPE); m d/32 must stay below 2^31 - 16
+ * (KQ_ERR_UNSUPPORTED). Error rules otherwise as kq_transform_quantize_mxfp4.
+ */
+kq_status kq_transform_quantize_mxfp4_packed(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
+                                             const float *factors, uint8_t *codes, uint8_t *packed_scales,
+                                             uint16_t *y16, kq_stream_t stream);
+
+/*
  * Low-rank branch of Eq. 11, first product: Z = X16 . Q(R)^T, fp32 accumulation
  * (bf16 matrix instructions; the decoded MXFP4 values are exact in bf16).
  *   X16       device, bf16 bits [m][ldx], ldx >= d, ldx % 8 == 0, 16-byte aligned

@@ -39,6 +39,7 @@ EXPORTS = (
     "kq_transform_quantize_mxfp4_gemm",
     "kq_hadamard_quantize_mxfp4",
     "kq_transform_quantize_mxfp4_y16",
+    "kq_transform_quantize_mxfp4_packed",
     "kq_lowrank_project",
     "kq_mxfp4_gemm_lowrank",
     "kq_gemm_f32",
@@ -90,6 +91,7 @@ def lib():
             "kq_transform_quantize_mxfp4_gemm": [p, i64, i64, i64, p, p, p, i64, p, i64, p],
             "kq_hadamard_quantize_mxfp4": [p, i64, i64, i64, i64, p, p, p, p],
             "kq_transform_quantize_mxfp4_y16": [p, i64, i64, i64, p, p, p, p, p],
+            "kq_transform_quantize_mxfp4_packed": [p, i64, i64, i64, p, p, p, p, p],
             "kq_lowrank_project": [p, i64, i64, i64, p, p, i64, p, p],
             "kq_mxfp4_gemm_lowrank": [p, p, p, p, i64, i64, i64, p, p, p, i64, p, i64, p],
             "kq_gemm_f32": [st, st, i64, i64, i64, ctypes.c_float, p, i64, p, i64, ctypes.c_float, p, i64, p,
@@ -243,6 +245,39 @@ def transform_quantize_mxfp4_y16(A, factors, codes=None, scales=None, y16=None, 
            lib().kq_transform_quantize_mxfp4_y16(_p(A), m, d, lda, _p(factors), _p(codes), _p(scales), _p(y16),
                                                  _stream_ptr(stream)))
     return codes, scales, y16
+
+
+def transform_quantize_mxfp4_packed(A, factors, codes=None, packed_scales=None, y16=None, want_y16=False,
+                                     stream=None):
+    """Fused y = A T then MXFP4 with the scales written in the packed-GEMM layout
+    [d/256][m][8] (what pack_mxfp4_scales makes of them; d % 256 == 0), optionally also
+    bf16(y) [m][d] (y16, or want_y16=True to allocate it). Returns codes, packed scales, y16
+    (or None)."""
+    torch = _torch()
+    m, d, lda = _bf16_input(A)
+    _dev(factors, "factors", (torch.float32,))
+    if factors.numel() != (d // 32) * 20 or not factors.is_contiguous():
+        raise ValueError("factors must be contiguous fp32 [d/32][5][2][2]")
+    if codes is None:
+        codes = torch.empty((m, d // 2), dtype=torch.uint8, device=A.device)
+    _dev(codes, "codes", (torch.uint8,))
+    if tuple(codes.shape) != (m, d // 2) or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous [m][d/2] uint8 tensor")
+    if packed_scales is None:
+        packed_scales = torch.empty((d // 256 if d % 256 == 0 else 0, m, 8), dtype=torch.uint8, device=A.device)
+    _dev(packed_scales, "packed_scales", (torch.uint8,))
+    if packed_scales.numel() != m * (d // 32) or not packed_scales.is_contiguous():
+        raise ValueError("packed_scales must be a contiguous uint8 tensor of m * d/32 bytes")
+    if y16 is None and want_y16:
+        y16 = torch.empty((m, d), dtype=torch.bfloat16, device=A.device)
+    if y16 is not None:
+        _dev(y16, "y16", (torch.bfloat16,))
+        if tuple(y16.shape) != (m, d) or not y16.is_contiguous():
+            raise ValueError("y16 must be a contiguous bf16 [m][d] tensor")
+    _check("kq_transform_quantize_mxfp4_packed",
+           lib().kq_transform_quantize_mxfp4_packed(_p(A), m, d, lda, _p(factors), _p(codes), _p(packed_scales),
+                                                    _p(y16) if y16 is not None else None, _stream_ptr(stream)))
+    return codes, packed_scales, y16
 
 
 def lowrank_project(X16, codes_r, scales_r, out=None, stream=None):

@@ -243,7 +243,9 @@ __device__ __forceinline__ void apply_coefs(float y[8], const float c[16]) {
 // Kronecker transform. Each wave's U row loads are issued at once; for the
 // transform they are in flight while wave 0 derives the segment's
 // coefficients (factor loads, reciprocals, LDS writes, barrier).
-template <int MODE, int YOUT, int NW, int U>
+// PK: scales written in the packed-GEMM layout [d/256][m][8] (even blocks of
+// a 256-channel stage first) instead of [m][d/32]; d % 256 == 0.
+template <int MODE, int YOUT, int NW, int U, bool PK = false>
 __global__ __launch_bounds__(NW * 64) void rowwave_kernel(const uint16_t *__restrict__ A, RGeom g,
                                                           const float *__restrict__ params,
                                                           uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
@@ -266,14 +268,31 @@ __global__ __launch_bounds__(NW * 64) void rowwave_kernel(const uint16_t *__rest
     const uint32_t a_bytes = (uint32_t)((g.d - c_seg) * 2);
     const uint32_t a_off = (uint32_t)lane * 16;
     LaneOff lo{(uint32_t)lane * 32, (uint32_t)lane * 16, (uint32_t)lane * 4, (uint32_t)lane >> 2, (lane & 3) == 0};
+    if constexpr (PK) {
+        // packed scale byte of block j: stage j / 8, row, byte 4 (j & 1) + (j & 7) / 2;
+        // a lane past the last block gets an offset past the record count
+        lo.scale = active ? (uint32_t)((j >> 3) * g.m * 8 + 4 * (j & 1) + ((j & 7) >> 1)) : 0xFFFFFFF0u;
+    }
     asm volatile("" : "+v"(lo.y32), "+v"(lo.code), "+v"(lo.scale));  // opaque: not rematerialized per row
     RowOut o;
-    o.codes = reinterpret_cast<char *>(codes + row0 * (g.d / 2) + c_seg / 2);
-    o.scales = reinterpret_cast<char *>(scales + row0 * g.nblk + seg * 16);
-    o.codes_step = (int64_t)NW * (g.d / 2);
-    o.scales_step = (int64_t)NW * g.nblk;
-    o.codes_bytes = (uint32_t)((g.d - c_seg) / 2);
-    o.scales_bytes = (uint32_t)(g.nblk - seg * 16);
+    if constexpr (PK) {
+        // base at the row's 8-byte piece of stage 0; every valid offset of every
+        // row of the wave stays below m d / 32 - 8 row0
+        const int64_t left_bytes = g.m * g.nblk - row0 * 8;
+        o.codes = reinterpret_cast<char *>(codes + row0 * (g.d / 2) + c_seg / 2);
+        o.scales = reinterpret_cast<char *>(scales + row0 * 8);
+        o.codes_step = (int64_t)NW * (g.d / 2);
+        o.scales_step = (int64_t)NW * 8;
+        o.codes_bytes = (uint32_t)((g.d - c_seg) / 2);
+        o.scales_bytes = (uint32_t)(left_bytes > 0 ? left_bytes : 0);
+    } else {
+        o.codes = reinterpret_cast<char *>(codes + row0 * (g.d / 2) + c_seg / 2);
+        o.scales = reinterpret_cast<char *>(scales + row0 * g.nblk + seg * 16);
+        o.codes_step = (int64_t)NW * (g.d / 2);
+        o.scales_step = (int64_t)NW * g.nblk;
+        o.codes_bytes = (uint32_t)((g.d - c_seg) / 2);
+        o.scales_bytes = (uint32_t)(g.nblk - seg * 16);
+    }
     const int ysize = YOUT == kYF32 ? 4 : 2;
     o.y = YOUT == kYNone ? nullptr : static_cast<char *>(yout) + (row0 * g.d + c_seg) * ysize;
     o.y_step = (int64_t)NW * g.d * ysize;
@@ -653,7 +672,7 @@ bool make_rgeom(int64_t m, int64_t d, int64_t lda, int nw, int u, kq::RGeom &g, 
 // each load 4 rows at once and finish (a workgroup covers 16 blocks x 16
 // rows; longer-lived workgroups were slower although they amortize the setup);
 // SmoothQuant, with no setup, takes 8 waves of 4 rows.
-template <int MODE, int YOUT>
+template <int MODE, int YOUT, bool PK = false>
 kq_status launch_rowwave(const uint16_t *A, int64_t m, int64_t d, int64_t lda, const float *params,
                          uint8_t *codes, uint8_t *scales, void *yout, kq_stream_t stream) {
     constexpr int NW = MODE == kq::kKron ? 4 : 8;
@@ -661,8 +680,8 @@ kq_status launch_rowwave(const uint16_t *A, int64_t m, int64_t d, int64_t lda, c
     kq::RGeom g;
     unsigned nwg;
     if (!make_rgeom(m, d, lda, NW, U, g, nwg)) return KQ_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((kq::rowwave_kernel<MODE, YOUT, NW, U>), dim3(nwg), dim3(NW * 64), 0, (hipStream_t)stream, A,
-                       g, params, codes, scales, yout);
+    hipLaunchKernelGGL((kq::rowwave_kernel<MODE, YOUT, NW, U, PK>), dim3(nwg), dim3(NW * 64), 0,
+                       (hipStream_t)stream, A, g, params, codes, scales, yout);
     return launched();
 }
 
@@ -760,6 +779,23 @@ kq_status kq_transform_quantize_mxfp4_y16(const uint16_t *A, int64_t m, int64_t 
     if (!factors || !y16) return KQ_ERR_NULL;
     if (!aligned(factors, 16) || !aligned(y16, 16)) return KQ_ERR_ALIGN;
     return launch_rowwave<kq::kKron, kq::kYBF16>(A, m, d, lda, factors, codes, scales, y16, stream);
+}
+
+kq_status kq_transform_quantize_mxfp4_packed(const uint16_t *A, int64_t m, int64_t d, int64_t lda,
+                                             const float *factors, uint8_t *codes, uint8_t *packed_scales,
+                                             uint16_t *y16, kq_stream_t stream) {
+    kq_status s = check_shape(m, d, lda);
+    if (s != KQ_OK) return s;
+    if (d % 256 != 0) return KQ_ERR_SHAPE;
+    if (m == 0 || d == 0) return KQ_OK;
+    if ((s = check_bf16_io(A, lda, codes, packed_scales)) != KQ_OK) return s;
+    if (!factors) return KQ_ERR_NULL;
+    if (!aligned(factors, 16) || (y16 && !aligned(y16, 16))) return KQ_ERR_ALIGN;
+    // packed offsets span the whole scale array in one 32-bit record count
+    if (m > (((int64_t)1 << 31) - 16) / (d / 32)) return KQ_ERR_UNSUPPORTED;
+    if (y16)
+        return launch_rowwave<kq::kKron, kq::kYBF16, true>(A, m, d, lda, factors, codes, packed_scales, y16, stream);
+    return launch_rowwave<kq::kKron, kq::kYNone, true>(A, m, d, lda, factors, codes, packed_scales, nullptr, stream);
 }
 
 kq_status kq_smoothquant_quantize_mxfp4(const uint16_t *A, int64_t m, int64_t d, int64_t lda,

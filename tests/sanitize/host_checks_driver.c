@@ -89,6 +89,10 @@ int main(void) {
                                                                   NULL), KQ_ERR_UNSUPPORTED);
     expect("calib huge", kq_calib_workspace_bytes((int64_t)1 << 40, (int64_t)1 << 40, (int64_t)1 << 40, &(int64_t){0}),
            KQ_ERR_UNSUPPORTED);
+    expect("packed huge", kq_transform_quantize_mxfp4_packed(GOOD, (int64_t)1 << 30, 256, 256, GOOD, P(0x10000),
+                                                             P(0x10000), NULL, NULL), KQ_ERR_UNSUPPORTED);
+    expect("packed overflow", kq_transform_quantize_mxfp4_packed(GOOD, BIG, 256, 256, GOOD, P(0x10000), P(0x10000),
+                                                                 NULL, NULL), KQ_ERR_SHAPE);
     expect("y16 huge", kq_transform_quantize_mxfp4_y16(GOOD, BIG, 64, 64, GOOD, P(0x10000), P(0x10000), P(0x10000),
                                                        NULL), KQ_ERR_SHAPE);
     expect("smooth huge", kq_smoothquant_quantize_mxfp4(GOOD, 4, BIG / 64 * 32, BIG, GOOD, P(0x10000), P(0x10000),

@@ -149,6 +149,16 @@ GOOD = P(0x10000)  # never dereferenced: every case below fails before a launch
     ("kq_hadamard_quantize_mxfp4", (None, 0, 1024, 1024, 1024, None, None, None, None), kq.KQ_OK),
     ("kq_transform_quantize_mxfp4_y16", (GOOD, 4, 64, 64, GOOD, GOOD, GOOD, None, None), kq.KQ_ERR_NULL),
     ("kq_transform_quantize_mxfp4_y16", (GOOD, 4, 64, 64, GOOD, GOOD, GOOD, P(0x10008), None), kq.KQ_ERR_ALIGN),
+    ("kq_transform_quantize_mxfp4_packed", (GOOD, 4, 128, 128, GOOD, GOOD, GOOD, None, None), kq.KQ_ERR_SHAPE),
+    ("kq_transform_quantize_mxfp4_packed", (GOOD, 4, 256, 256, None, GOOD, GOOD, None, None), kq.KQ_ERR_NULL),
+    ("kq_transform_quantize_mxfp4_packed", (GOOD, 4, 256, 256, GOOD, GOOD, None, None, None), kq.KQ_ERR_NULL),
+    ("kq_transform_quantize_mxfp4_packed", (GOOD, 4, 256, 256, GOOD, GOOD, GOOD, P(0x10008), None),
+     kq.KQ_ERR_ALIGN),
+    ("kq_transform_quantize_mxfp4_packed", (GOOD, 4, 256, 256, P(0x10004), GOOD, GOOD, None, None),
+     kq.KQ_ERR_ALIGN),
+    ("kq_transform_quantize_mxfp4_packed", (GOOD, 1 << 30, 256, 256, GOOD, GOOD, GOOD, None, None),
+     kq.KQ_ERR_UNSUPPORTED),
+    ("kq_transform_quantize_mxfp4_packed", (None, 0, 256, 256, None, None, None, None, None), kq.KQ_OK),
     ("kq_lowrank_project", (GOOD, 4, 64, 64, GOOD, GOOD, 48, GOOD, None), kq.KQ_ERR_SHAPE),
     ("kq_lowrank_project", (GOOD, 4, 64, 60, GOOD, GOOD, 32, GOOD, None), kq.KQ_ERR_SHAPE),
     ("kq_lowrank_project", (GOOD, 4, 64, 72, GOOD, GOOD, 32, P(0x10004), None), kq.KQ_ERR_ALIGN),

@@ -4,7 +4,8 @@ the 32 x 32 x 64 scaled FP4 instruction) and of its scale re-layout
 product against the oracle's dequantized fp64 product (per element, to fp32 rounding
 of the partial sums), against kq_mxfp4_gemm (bit-identical where every fp32 partial
 sum is exact), ragged shapes, padded and unaligned outputs, k = 0, and the FLUX
-18432 x 3072 x 3072 layer.
+18432 x 3072 x 3072 layer; the fused quantizer's packed-scale output against the
+re-layout of its ordinary output.
 """
 import sys
 
@@ -269,3 +270,52 @@ def test_packed_gemm_flux_layer(torch_dev, kq, orc):
     print("[gemm256] flux: max |packed - gemm| %.3g (max allowed %.3g), sampled rows vs oracle max rel %.3g" % (
         diff.max(), (2 * 64 * 2.0 ** -24 * rowbound).max(),
         np.max(np.abs(got[rows] - ref) / (np.abs(ref) + 1e-30))), flush=True)
+
+
+@pytest.mark.parametrize("m,d,seed", [(37, 256, 31), (300, 768, 32), (1000, 3072, 33), (5, 1024, 34)])
+def test_quantizer_packed_scales_equal_pack_of_scales(torch_dev, kq, m, d, seed):
+    """kq_transform_quantize_mxfp4_packed writes the quantizer's codes and, byte for byte,
+    pack_mxfp4_scales of its scales (d = 768 leaves the last 512-channel segment half
+    empty, m = 5 and 37 ragged row groups); with y16, also the y16 entry point's bf16 y.
+    Bytes after the packed array stay untouched."""
+    import synth
+    torch = torch_dev
+    case("quantizer packed scales m=%d d=%d" % (m, d))
+    A = torch.from_numpy(synth.random_bf16_matrix(m, d, seed=seed, scale=3.0).view(np.int16)).cuda().view(
+        torch.bfloat16)
+    fac = dev(torch, synth.lu_perturbed_factors(d // 32, seed=seed + 1))
+    ca, sa = kq.transform_quantize_mxfp4(A, fac)
+    ca16, sa16, y16 = kq.transform_quantize_mxfp4_y16(A, fac)
+    guard = torch.full((m * (d // 32) + 64,), 0xEE, dtype=torch.uint8, device="cuda")
+    pk = guard[:m * (d // 32)]
+    cp, _, none = kq.transform_quantize_mxfp4_packed(A, fac, packed_scales=pk)
+    cq, pq, yq = kq.transform_quantize_mxfp4_packed(A, fac, want_y16=True)
+    ref = kq.pack_mxfp4_scales(sa)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(cp, ca) and torch.equal(pk, ref.reshape(-1))
+    assert torch.equal(cq, ca16) and torch.equal(pq.reshape(-1), kq.pack_mxfp4_scales(sa16).reshape(-1))
+    assert torch.equal(yq, y16)
+    assert bool((guard[m * (d // 32):] == 0xEE).all())
+
+
+def test_quantizer_packed_scales_flux_layer(torch_dev, kq):
+    """The FLUX 18432 x 3072 input: the packed-scale quantizer feeds the packed GEMM with
+    the same result as quantizer + re-layout + GEMM, bit for bit."""
+    import synth
+    torch = torch_dev
+    case("quantizer packed scales flux 18432x3072 + gemm")
+    w = synth.workload("flux_18432x3072")
+    A = torch.from_numpy(w.A.view(np.int16)).cuda().view(torch.bfloat16)
+    fac = dev(torch, w.factors)
+    rng = np.random.default_rng(41)
+    cw = dev(torch, rng.integers(0, 256, (512, 3072 // 2), dtype=np.uint8))
+    sw = dev(torch, rng.integers(118, 130, (512, 3072 // 32), dtype=np.uint8))
+    psw = kq.pack_mxfp4_scales(sw)
+    ca, sa = kq.transform_quantize_mxfp4(A, fac)
+    O_ref = kq.mxfp4_gemm_packed(ca, kq.pack_mxfp4_scales(sa), cw, psw)
+    cp, pp, _ = kq.transform_quantize_mxfp4_packed(A, fac)
+    O = kq.mxfp4_gemm_packed(cp, pp, cw, psw)
+    torch.cuda.synchronize()
+    assert torch.equal(cp, ca)
+    assert torch.equal(O, O_ref)
