@@ -64,6 +64,7 @@ def parse():
                     help="launch only the packed-scale W4A4 GEMM N times on seeded random MXFP4 operands "
                          "of --gemm-shape (for counter runs), print its event median, and exit")
     ap.add_argument("--gemm-shape", default="18432x3072x3072", help="m x n x k for --gemm-launches")
+    ap.add_argument("--gemm-out", choices=("fp32", "bf16"), default="fp32", help="output type for --gemm-launches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, 10 times (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -572,8 +573,9 @@ def summarize_pmc(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_json):
     print(json.dumps(out, indent=1))
 
 
-def gemm_launches(n, shape):
-    """The packed-scale W4A4 GEMM alone, n launches (fp32 output), for counter runs."""
+def gemm_launches(n, shape, out="fp32"):
+    """The packed-scale W4A4 GEMM alone, n launches (fp32 or bf16 output), for counter and
+    kernel-trace runs (k = 0 times the output stores alone)."""
     import torch
 
     import mxfp4_activation_quantizer_amd as kq
@@ -584,9 +586,10 @@ def gemm_launches(n, shape):
     sa = torch.randint(118, 130, (m, k // 32), dtype=torch.uint8, device="cuda", generator=g)
     sw = torch.randint(118, 130, (nn, k // 32), dtype=torch.uint8, device="cuda", generator=g)
     psa, psw = kq.pack_mxfp4_scales(sa), kq.pack_mxfp4_scales(sw)
-    O = torch.empty((m, nn), dtype=torch.float32, device="cuda")
-    d = _events_us(torch, lambda: kq.mxfp4_gemm_packed(ca, psa, cw, psw, out=O), n, 2)
-    log("packed gemm %s: %d launches, median %.1f us" % (shape, n, float(np.median(d))))
+    bf = out == "bf16"
+    O = torch.empty((m, nn), dtype=torch.bfloat16 if bf else torch.float32, device="cuda")
+    d = _events_us(torch, lambda: kq.mxfp4_gemm_packed(ca, psa, cw, psw, out=O, bf16=bf), n, 2)
+    log("packed gemm %s %s: %d launches, median %.1f us" % (shape, out, n, float(np.median(d))))
 
 
 def main():
@@ -598,7 +601,7 @@ def main():
         copy_calibration()
         return
     if args.gemm_launches > 0:
-        gemm_launches(args.gemm_launches, args.gemm_shape)
+        gemm_launches(args.gemm_launches, args.gemm_shape, args.gemm_out)
         return
     if args.gpus != 1:
         print("bench.py: measures one GPU only (the quantizer needs no collectives); "

@@ -85,10 +85,12 @@ def test_pack_scales_is_the_layout(torch_dev, kq, rows, k, seed):
 
 @pytest.mark.parametrize("m,n,k,seed", [(1, 1, 256, 1), (37, 70, 256, 2), (257, 513, 512, 3),
                                         (300, 1100, 768, 4), (256, 256, 2304, 5), (1000, 700, 512, 6),
-                                        (5632, 3000, 512, 9)])
+                                        (5632, 3000, 512, 9), (6400, 2900, 512, 11)])
 def test_packed_gemm_matches_oracle(torch_dev, kq, orc, m, n, k, seed):
     """Seeded random MXFP4 operands (any code byte, scales around 2^0); ragged m and n;
-    5632 x 3000 is 264 tiles, launched in the staggered order on 256 CUs."""
+    5632 x 3000 is 264 tiles, launched in the staggered order on 256 CUs; 6400 x 2900
+    is 300 tiles in the plain order, 88 workgroups taking two items, two of the half
+    tiles right of the last column (nothing to store)."""
     torch = torch_dev
     case("packed gemm m=%d n=%d k=%d" % (m, n, k))
     ca, sa, cw, sw = operands(np.random.default_rng(seed), m, n, k)
@@ -208,7 +210,7 @@ def test_packed_gemm_lowrank_full_tiles_matches_oracle(torch_dev, kq, orc, m, n,
 
 @pytest.mark.parametrize("m,n,k,pad,seed", [(1000, 700, 512, 0, 21), (300, 1100, 768, 3, 22), (257, 513, 256, 1, 23),
                                             (5632, 3072, 256, 0, 24), (5632, 3000, 256, 5, 25),
-                                            (18432, 3072, 3072, 0, 24)])
+                                            (5632, 2900, 512, 0, 26), (18432, 3072, 3072, 0, 24)])
 def test_packed_gemm_bf16_is_rounded_fp32(torch_dev, kq, m, n, k, pad, seed):
     """The bf16-output form equals the fp32 form rounded to nearest even, bit for bit, for
     aligned (whole 16-byte row pieces) and odd-stride or partial-tile (2-byte element
