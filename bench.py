@@ -360,6 +360,32 @@ def lowrank_layer_timing(torch, kq, A, fac, cw, sw, W, r=128, reps=20):
         kq.lowrank_project_bf16(y16, r16, out=Z)
         kq.mxfp4_gemm_packed_lowrank(ca, psa, cw, psw, Z, cl, sl, out=O)
     res["layer_with_branch_packed_quantizer_region_us"] = med(layer_packed_quantizer)
+
+    # the branch's operands prepared outside the product: the projection writes Z's bf16
+    # split, L is decoded to bf16 (both decodes per call, as R's above), and the packed
+    # GEMM moves them straight into LDS (bit-identical to the fp32-Z form)
+    Zh, Zl = kq.lowrank_project_bf16_split(y16, r16)
+    l16 = kq.dequantize_mxfp4_bf16(cl, sl)
+    res["project_bf16_split_us"] = med(lambda: kq.lowrank_project_bf16_split(y16, r16, Zh=Zh, Zl=Zl))
+    res["decode_l_us"] = med(lambda: kq.dequantize_mxfp4_bf16(cl, sl, out=l16))
+    res["gemm_lowrank_split_us"] = med(lambda: kq.mxfp4_gemm_packed_lowrank_split(ca, psa, cw, psw, Zh, Zl, l16,
+                                                                                  out=O))
+
+    def layer_split():
+        kq.transform_quantize_mxfp4_packed(A, fac, codes=ca, packed_scales=psa, y16=y16)
+        kq.dequantize_mxfp4_bf16(cr, sr, out=r16)
+        kq.lowrank_project_bf16_split(y16, r16, Zh=Zh, Zl=Zl)
+        kq.dequantize_mxfp4_bf16(cl, sl, out=l16)
+        kq.mxfp4_gemm_packed_lowrank_split(ca, psa, cw, psw, Zh, Zl, l16, out=O)
+    res["layer_with_branch_split_region_us"] = med(layer_split)
+
+    # the same with R and L decoded once per weight (as W's scales are packed once):
+    # three launches per call
+    def layer_split_prepared():
+        kq.transform_quantize_mxfp4_packed(A, fac, codes=ca, packed_scales=psa, y16=y16)
+        kq.lowrank_project_bf16_split(y16, r16, Zh=Zh, Zl=Zl)
+        kq.mxfp4_gemm_packed_lowrank_split(ca, psa, cw, psw, Zh, Zl, l16, out=O)
+    res["layer_with_branch_split_prepared_region_us"] = med(layer_split_prepared)
     return res
 
 

@@ -270,6 +270,26 @@ kq_status kq_mxfp4_gemm_packed_lowrank(const uint8_t *codes_a, const uint8_t *pa
                                        int64_t r, float *O, int64_t ldo, kq_stream_t stream);
 
 /*
+ * kq_mxfp4_gemm_packed_lowrank with the low-rank operands prepared once outside
+ * the product (Sec. 3.4 Eq. 11's Z deq(L)^T): Z split as Zh = bf16(Z) and
+ * Zl = bf16(Z - Zh) (what kq_lowrank_project_bf16_split writes) and deq(L) in
+ * bf16 (exact; kq_dequantize_mxfp4_bf16 of L's codes and scales). Every output
+ * is the same sum, in the same order, as kq_mxfp4_gemm_packed_lowrank's on the
+ * fp32 Z that Zh + Zl split (bit-identical); the kernel moves the operands
+ * straight into LDS instead of converting them per tile.
+ *   codes_a .. k, O, ldo   as kq_mxfp4_gemm_packed_lowrank
+ *   Zh, Zl                 device, bf16 bits [m][r], 16-byte aligned
+ *   L16                    device, bf16 bits [n][r] (deq(L)), 16-byte aligned
+ *   r                      r > 0, r % 32 == 0 (KQ_ERR_SHAPE)
+ * Size limits as kq_mxfp4_gemm_packed_lowrank (512 r below 2^31).
+ */
+kq_status kq_mxfp4_gemm_packed_lowrank_split(const uint8_t *codes_a, const uint8_t *packed_scales_a,
+                                             const uint8_t *codes_w, const uint8_t *packed_scales_w, int64_t m,
+                                             int64_t n, int64_t k, const uint16_t *Zh, const uint16_t *Zl,
+                                             const uint16_t *L16, int64_t r, float *O, int64_t ldo,
+                                             kq_stream_t stream);
+
+/*
  * The W4A4 layer with the activation transform and quantizer inside the
  * product (Sec. 1 Eq. 1-2; Sec. 3.2 Eq. 5 and Sec. 3.5.1 Eq. 12 for T; Sec. 3.1
  * for Q):
@@ -369,6 +389,18 @@ kq_status kq_lowrank_project(const uint16_t *X16, int64_t m, int64_t d, int64_t 
  */
 kq_status kq_lowrank_project_bf16(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint16_t *R16,
                                   int64_t r, float *Z, kq_stream_t stream);
+
+/*
+ * kq_lowrank_project_bf16 writing Z as its bf16 split instead of fp32: Zh =
+ * bf16(Z) and Zl = bf16(Z - Zh), each rounded to nearest even (Z - Zh is exact
+ * in fp32), from the same fp32 sums (so Zh + Zl is Z to 2^-16 relative; the
+ * operands kq_mxfp4_gemm_packed_lowrank_split reads, Sec. 3.4 Eq. 11).
+ *   X16, m, d, ldx, R16, r   as kq_lowrank_project_bf16
+ *   Zh, Zl                   device, bf16 bits [m][r] each (written), 16-byte aligned
+ * Errors as kq_lowrank_project_bf16.
+ */
+kq_status kq_lowrank_project_bf16_split(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint16_t *R16,
+                                        int64_t r, uint16_t *Zh, uint16_t *Zl, kq_stream_t stream);
 
 /*
  * MXFP4 -> bf16 (Sec. 3.1's dequantization deq(code, scale) = E2M1(code)

@@ -32,10 +32,12 @@ EXPORTS = (
     "kq_mxfp4_gemm_wide",
     "kq_pack_mxfp4_scales",
     "kq_lowrank_project_bf16",
+    "kq_lowrank_project_bf16_split",
     "kq_dequantize_mxfp4_bf16",
     "kq_mxfp4_gemm_packed",
     "kq_mxfp4_gemm_packed_bf16",
     "kq_mxfp4_gemm_packed_lowrank",
+    "kq_mxfp4_gemm_packed_lowrank_split",
     "kq_transform_quantize_mxfp4_gemm",
     "kq_hadamard_quantize_mxfp4",
     "kq_transform_quantize_mxfp4_y16",
@@ -84,10 +86,12 @@ def lib():
             "kq_mxfp4_gemm_wide": [p, p, p, p, i64, i64, i64, p, i64, p],
             "kq_pack_mxfp4_scales": [p, i64, i64, p, p],
             "kq_lowrank_project_bf16": [p, i64, i64, i64, p, i64, p, p],
+            "kq_lowrank_project_bf16_split": [p, i64, i64, i64, p, i64, p, p, p],
             "kq_dequantize_mxfp4_bf16": [p, p, i64, i64, p, p],
             "kq_mxfp4_gemm_packed": [p, p, p, p, i64, i64, i64, p, i64, p],
             "kq_mxfp4_gemm_packed_bf16": [p, p, p, p, i64, i64, i64, p, i64, p],
             "kq_mxfp4_gemm_packed_lowrank": [p, p, p, p, i64, i64, i64, p, p, p, i64, p, i64, p],
+            "kq_mxfp4_gemm_packed_lowrank_split": [p, p, p, p, i64, i64, i64, p, p, p, i64, p, i64, p],
             "kq_transform_quantize_mxfp4_gemm": [p, i64, i64, i64, p, p, p, i64, p, i64, p],
             "kq_hadamard_quantize_mxfp4": [p, i64, i64, i64, i64, p, p, p, p],
             "kq_transform_quantize_mxfp4_y16": [p, i64, i64, i64, p, p, p, p, p],
@@ -342,6 +346,30 @@ def lowrank_project_bf16(X16, R16, out=None, stream=None):
     return out
 
 
+def lowrank_project_bf16_split(X16, R16, Zh=None, Zl=None, stream=None):
+    """As lowrank_project_bf16, Z written as its bf16 split: Zh = bf16(Z), Zl = bf16(Z - Zh)
+    (bf16 [m][r] each). Returns Zh, Zl."""
+    torch = _torch()
+    _dev(X16, "X16", (torch.bfloat16, torch.int16, torch.uint16))
+    _dev(R16, "R16", (torch.bfloat16, torch.int16, torch.uint16))
+    m, d, ldx = _rows(X16, "X16")
+    if R16.dim() != 2 or R16.shape[1] != d or not R16.is_contiguous():
+        raise ValueError("R16 must be a contiguous bf16 [r][d] tensor")
+    r = R16.shape[0]
+    outs = []
+    for t, nm in ((Zh, "Zh"), (Zl, "Zl")):
+        if t is None:
+            t = torch.empty((m, r), dtype=torch.bfloat16, device=X16.device)
+        _dev(t, nm, (torch.bfloat16,))
+        if tuple(t.shape) != (m, r) or not t.is_contiguous():
+            raise ValueError(nm + " must be a contiguous bf16 [m][r] tensor")
+        outs.append(t)
+    Zh, Zl = outs
+    _check("kq_lowrank_project_bf16_split",
+           lib().kq_lowrank_project_bf16_split(_p(X16), m, d, ldx, _p(R16), r, _p(Zh), _p(Zl), _stream_ptr(stream)))
+    return Zh, Zl
+
+
 def mxfp4_gemm_lowrank(codes_a, scales_a, codes_w, scales_w, Z, codes_l, scales_l, out=None, stream=None):
     """O = deq(A) deq(W)^T + Z deq(L)^T (Eq. 11's two terms): Z fp32 [m][r], L in MXFP4
     (codes [n][r/2], scales [n][r/32])."""
@@ -518,6 +546,41 @@ def mxfp4_gemm_packed_lowrank(codes_a, packed_scales_a, codes_w, packed_scales_w
            lib().kq_mxfp4_gemm_packed_lowrank(_p(codes_a), _p(packed_scales_a), _p(codes_w), _p(packed_scales_w), m,
                                               n, k, _p(Z), _p(codes_l), _p(scales_l), r, _p(out), out.stride(0),
                                               _stream_ptr(stream)))
+    return out
+
+
+def mxfp4_gemm_packed_lowrank_split(codes_a, packed_scales_a, codes_w, packed_scales_w, Zh, Zl, L16, out=None,
+                                    stream=None):
+    """mxfp4_gemm_packed_lowrank with the branch's operands prepared once: Z split as Zh, Zl
+    (bf16 [m][r], lowrank_project_bf16_split) and deq(L) in bf16 [n][r]
+    (dequantize_mxfp4_bf16 of L). Bit-identical to the fp32-Z form on the Z they split."""
+    torch = _torch()
+    for t, nm in ((codes_a, "codes_a"), (packed_scales_a, "packed_scales_a"), (codes_w, "codes_w"),
+                  (packed_scales_w, "packed_scales_w")):
+        _dev(t, nm, (torch.uint8,))
+        if not t.is_contiguous():
+            raise ValueError(nm + " must be contiguous")
+    for t, nm in ((Zh, "Zh"), (Zl, "Zl"), (L16, "L16")):
+        _dev(t, nm, (torch.bfloat16, torch.int16, torch.uint16))
+        if t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(nm + " must be a contiguous 2-d bf16 tensor")
+    m, kb = codes_a.shape
+    n = codes_w.shape[0]
+    k = kb * 2
+    r = Zh.shape[1]
+    if tuple(codes_w.shape) != (n, kb) or packed_scales_a.numel() != m * (k // 32) or \
+            packed_scales_w.numel() != n * (k // 32) or tuple(Zh.shape) != (m, r) or tuple(Zl.shape) != (m, r) or \
+            tuple(L16.shape) != (n, r):
+        raise ValueError("operand shapes do not match")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=codes_a.device)
+    _dev(out, "out", (torch.float32,))
+    if out.dim() != 2 or out.shape[0] != m or out.shape[1] != n or out.stride(1) != 1:
+        raise ValueError("out must be fp32 [m][n] with unit column stride")
+    _check("kq_mxfp4_gemm_packed_lowrank_split",
+           lib().kq_mxfp4_gemm_packed_lowrank_split(_p(codes_a), _p(packed_scales_a), _p(codes_w),
+                                                    _p(packed_scales_w), m, n, k, _p(Zh), _p(Zl), _p(L16), r,
+                                                    _p(out), out.stride(0), _stream_ptr(stream)))
     return out
 
 

@@ -199,8 +199,13 @@ __device__ __forceinline__ void proj_dma16(__amdgpu_buffer_rsrc_t d, uint32_t ld
         : "memory");
 }
 
+// SPLIT: Z leaves as its bf16 split, zh = bf16(z) and zl = bf16(z - zh) (both
+// rounded to nearest even by the hardware convert; z - zh is exact in fp32),
+// the operands the packed GEMM's low-rank term multiplies, in place of fp32 z.
+template <bool SPLIT>
 __global__ __launch_bounds__(64 * (kProjWaves + kProjProducers)) void lowrank_project_r16_kernel(
-    const uint16_t *__restrict__ X, ProjGeom g, const uint16_t *__restrict__ r16, float *__restrict__ Z) {
+    const uint16_t *__restrict__ X, ProjGeom g, const uint16_t *__restrict__ r16, float *__restrict__ Z,
+    uint16_t *__restrict__ Zh, uint16_t *__restrict__ Zl) {
     __shared__ __attribute__((aligned(16))) uint8_t rl[kProjSlots][128 * 256];
     const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t tm = blockIdx.x / g.tiles_r, tr = blockIdx.x % g.tiles_r;
@@ -302,7 +307,16 @@ __global__ __launch_bounds__(64 * (kProjWaves + kProjProducers)) void lowrank_pr
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             const int64_t orow = orow0 + tt;
-            if (orow < g.m && col < g.r) Z[orow * g.r + col] = acc[b][tt];
+            if (orow < g.m && col < g.r) {
+                if (SPLIT) {
+                    const __bf16 h = (__bf16)acc[b][tt];
+                    const __bf16 l = (__bf16)(acc[b][tt] - (float)h);
+                    Zh[orow * g.r + col] = __builtin_bit_cast(uint16_t, h);
+                    Zl[orow * g.r + col] = __builtin_bit_cast(uint16_t, l);
+                } else {
+                    Z[orow * g.r + col] = acc[b][tt];
+                }
+            }
         }
     }
 }
@@ -551,6 +565,31 @@ using kqhost::aligned;
 using kqhost::launched;
 }  // namespace
 
+namespace {
+
+template <bool SPLIT>
+kq_status project_r16(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint16_t *R16, int64_t r, float *Z,
+                      uint16_t *Zh, uint16_t *Zl, kq_stream_t stream) {
+    if (m < 0 || d < 0 || d % 32 != 0 || ldx < d || r <= 0 || r % 32 != 0) return KQ_ERR_SHAPE;
+    if (!kqhost::sizes_fit({m, d, ldx, r})) return KQ_ERR_UNSUPPORTED;
+    if (m == 0 || d == 0) return KQ_OK;
+    if (!X16 || !R16 || (SPLIT ? (!Zh || !Zl) : !Z)) return KQ_ERR_NULL;
+    if (!aligned(X16, 16) || ldx % 8 != 0 || !aligned(R16, 16) || (!SPLIT && !aligned(Z, 16)) ||
+        (SPLIT && (!aligned(Zh, 16) || !aligned(Zl, 16))))
+        return KQ_ERR_ALIGN;
+    const int64_t tiles_m = (m + kq::kProjRows - 1) / kq::kProjRows, tiles_r = (r + 127) / 128;
+    if (tiles_m * tiles_r > 0x7FFFFFFF || m > INT64_MAX / 4 / (ldx > r ? ldx : r)) return KQ_ERR_SHAPE;
+    if ((int64_t)kq::kProjRows * ldx * 2 >= ((int64_t)1 << 31) || (int64_t)128 * d * 2 >= ((int64_t)1 << 31))
+        return KQ_ERR_UNSUPPORTED;
+    kq::ProjGeom g{m, d, ldx, r, tiles_r};
+    hipLaunchKernelGGL(kq::lowrank_project_r16_kernel<SPLIT>, dim3((unsigned)(tiles_m * tiles_r)),
+                       dim3(64 * (kq::kProjWaves + kq::kProjProducers)), 0, (hipStream_t)stream, X16, g, R16, Z, Zh,
+                       Zl);
+    return launched();
+}
+
+}  // namespace
+
 extern "C" {
 
 kq_status kq_mxfp4_gemm(const uint8_t *codes_a, const uint8_t *scales_a, const uint8_t *codes_w,
@@ -609,19 +648,12 @@ kq_status kq_lowrank_project(const uint16_t *X16, int64_t m, int64_t d, int64_t 
 
 kq_status kq_lowrank_project_bf16(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint16_t *R16,
                                   int64_t r, float *Z, kq_stream_t stream) {
-    if (m < 0 || d < 0 || d % 32 != 0 || ldx < d || r <= 0 || r % 32 != 0) return KQ_ERR_SHAPE;
-    if (!kqhost::sizes_fit({m, d, ldx, r})) return KQ_ERR_UNSUPPORTED;
-    if (m == 0 || d == 0) return KQ_OK;
-    if (!X16 || !R16 || !Z) return KQ_ERR_NULL;
-    if (!aligned(X16, 16) || ldx % 8 != 0 || !aligned(R16, 16) || !aligned(Z, 16)) return KQ_ERR_ALIGN;
-    const int64_t tiles_m = (m + kq::kProjRows - 1) / kq::kProjRows, tiles_r = (r + 127) / 128;
-    if (tiles_m * tiles_r > 0x7FFFFFFF || m > INT64_MAX / 4 / (ldx > r ? ldx : r)) return KQ_ERR_SHAPE;
-    if ((int64_t)kq::kProjRows * ldx * 2 >= ((int64_t)1 << 31) || (int64_t)128 * d * 2 >= ((int64_t)1 << 31))
-        return KQ_ERR_UNSUPPORTED;
-    kq::ProjGeom g{m, d, ldx, r, tiles_r};
-    hipLaunchKernelGGL(kq::lowrank_project_r16_kernel, dim3((unsigned)(tiles_m * tiles_r)),
-                       dim3(64 * (kq::kProjWaves + kq::kProjProducers)), 0, (hipStream_t)stream, X16, g, R16, Z);
-    return launched();
+    return project_r16<false>(X16, m, d, ldx, R16, r, Z, nullptr, nullptr, stream);
+}
+
+kq_status kq_lowrank_project_bf16_split(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint16_t *R16,
+                                        int64_t r, uint16_t *Zh, uint16_t *Zl, kq_stream_t stream) {
+    return project_r16<true>(X16, m, d, ldx, R16, r, nullptr, Zh, Zl, stream);
 }
 
 kq_status kq_dequantize_mxfp4_bf16(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t k,

@@ -153,11 +153,11 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 //
 // One tile (run-order number u; half h of it when TN = 128) of one workgroup;
 // smem holds 2 stages of the full-width layout plus 1 KB.
-template <bool LR, int TN, bool B16>
+template <bool LR, int TN, bool B16, bool LRS = false>
 __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, const uint8_t *__restrict__ psa,
                                              const uint8_t *__restrict__ cw, const uint8_t *__restrict__ psw,
-                                             const Geom g, const float *__restrict__ Z,
-                                             const uint8_t *__restrict__ cl, const uint8_t *__restrict__ sl,
+                                             const Geom g, const void *__restrict__ lr0,
+                                             const void *__restrict__ lr1, const void *__restrict__ lr2,
                                              void *__restrict__ O, int u, int h, uint8_t *smem) {
     static_assert(TN == 256 || TN == 128, "tile width");
     using L = Lay<TN>;
@@ -285,11 +285,13 @@ __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, con
     // bf16, rows of 128 bytes with the 16-byte chunks permuted as the codes are
     uint8_t *zh = smem, *zl = smem + 32768, *ll = smem + 65536;
     const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(Z + m0 * g.r), (short)0, (int)(rows_a * g.r * 4), 0x00020000);
+        const_cast<float *>(static_cast<const float *>(lr0) + m0 * g.r), (short)0, (int)(rows_a * g.r * 4), 0x00020000);
     const __amdgpu_buffer_rsrc_t rcl = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(cl + n0 * (g.r / 2)), (short)0, (int)(rows_w * (g.r / 2)), 0x00020000);
+        const_cast<uint8_t *>(static_cast<const uint8_t *>(lr1) + n0 * (g.r / 2)), (short)0, (int)(rows_w * (g.r / 2)),
+        0x00020000);
     const __amdgpu_buffer_rsrc_t rsl = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(sl + n0 * (g.r / 32)), (short)0, (int)(rows_w * (g.r / 32)), 0x00020000);
+        const_cast<uint8_t *>(static_cast<const uint8_t *>(lr2) + n0 * (g.r / 32)), (short)0, (int)(rows_w * (g.r / 32)),
+        0x00020000);
     // (LR) a chunk (64 of r) is staged by 8 passes of 32 rows: lane t & 7 of row
     // 32 p + t / 8 takes 8 consecutive columns, so 8 lanes read a row's 256
     // bytes of Z (32 of L's code bytes) together; the next chunk's loads go
@@ -309,6 +311,32 @@ __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, con
             const uint32_t so = kc < g.r ? (uint32_t)(row * (g.r / 32) + kc / 32) : 0x80000000u;
             lc[p] = __builtin_amdgcn_raw_buffer_load_b32(rcl, co, 0, 0);
             ls[p] = __builtin_amdgcn_raw_buffer_load_b8(rsl, so, 0, 0);
+        }
+    };
+
+    // (LRS) the low-rank operands arrive split in bf16 -- Zh = bf16(Z), Zl = bf16(Z - Zh)
+    // [m][r] and deq(L) [n][r] -- and move 32 of r at a time straight into a stage
+    // buffer, like the codes: Zh at 0, Zl at 16 KB, L at 32 KB, rows of 64 bytes with
+    // 16-byte chunk c of row i at slot c ^ ((i / 4) % 4), so a 32-row fragment read
+    // is free of bank conflicts. A chunk takes 4 + 4 + TN / 64 loads per wave of
+    // 16 rows each; the first goes out during the last k stage, each next one during
+    // the current one's matrix work. Same instructions, same order as the fp32-Z
+    // path: bit-identical sums.
+    constexpr int kLrLoads = 8 + TN / 64;
+    const i32x4_t dzh = sdesc(static_cast<const uint16_t *>(lr0) + m0 * g.r, (uint32_t)(rows_a * g.r * 2));
+    const i32x4_t dzl = sdesc(static_cast<const uint16_t *>(lr1) + m0 * g.r, (uint32_t)(rows_a * g.r * 2));
+    const i32x4_t dll = sdesc(static_cast<const uint16_t *>(lr2) + n0 * g.r, (uint32_t)(rows_w * g.r * 2));
+    auto lr_issue = [&](int c, int l) {  // load l of chunk c, into the buffer of stage stages + c
+        const uint32_t st = lds0 + (uint32_t)(((g.stages + c) & 1) * kStage);
+        const int fr = (lane >> 4) & 3;  // (row / 4) % 4 of the lane's row (rows of a load start at multiples of 16)
+        const uint32_t inrow = (uint32_t)(2 * (32 * c + 8 * ((lane & 3) ^ fr)));
+        if (l < 8) {
+            const int j = l & 3, row = 64 * w + 16 * j + (lane >> 2);
+            dma16(l < 4 ? dzh : dzl, st + (l < 4 ? 0u : 16384u) + (uint32_t)((64 * w + 16 * j) * 64),
+                  (uint32_t)(row * g.r * 2) + inrow, 0u);
+        } else {
+            const int j = l - 8, row = (TN / 4) * w + 16 * j + (lane >> 2);
+            dma16(dll, st + 32768u + (uint32_t)(((TN / 4) * w + 16 * j) * 64), (uint32_t)(row * g.r * 2) + inrow, 0u);
         }
     };
 
@@ -384,20 +412,77 @@ __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, con
     {
         const int s = g.stages - 1;
         // the branch's first chunk is in flight during the last stage
-        if (LR) load_chunk(0);
+        if (LR && !LRS) load_chunk(0);
         read_frags(s, 1, F1);
-        step(F0, S, J0());
+        // (LRS) the first chunk's loads, one after each of the first kLrLoads
+        // matrix instructions of steps 0 and 1
+        auto step_lr = [&](const Frag<NB> &F, auto jc, int j0) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    mma(F, S, jc, a, b);
+                    const int l = j0 + NB * a + b;
+                    if (l < kLrLoads) {
+                        pin(a, b);
+                        lr_issue(0, l);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        };
+        static_assert(kLrLoads <= 8 * NB, "the first chunk's loads fit two steps");
+        if constexpr (LRS) step_lr(F0, J0(), 0);
+        else step(F0, S, J0());
         read_frags(s, 2, F0);
-        step(F1, S, J1());
+        if constexpr (LRS) step_lr(F1, J1(), 4 * NB);
+        else step(F1, S, J1());
         read_frags(s, 3, F1);
         step(F0, S, J2());
         step(F1, S, J3());
     }
     } else if (LR) {
-        load_chunk(0);
+        if constexpr (LRS) {
+#pragma unroll
+            for (int l = 0; l < kLrLoads; ++l) lr_issue(0, l);
+        } else {
+            load_chunk(0);
+        }
     }
 
-    if (LR) {
+    if constexpr (LRS) {
+        const int nch = g.r / 32, f = (r >> 2) & 3;
+        for (int c = 0; c < nch; ++c) {
+            // chunk c has landed; every wave is done with the other buffer, which
+            // takes the next chunk's loads at once (a chunk's matrix work hides them)
+            wait_loads_and_lds_then_barrier();
+            if (c + 1 < nch) {
+#pragma unroll
+                for (int l = 0; l < kLrLoads; ++l) lr_issue(c + 1, l);
+            }
+            const uint8_t *st = smem + ((g.stages + c) & 1) * kStage;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int off = 16 * ((2 * kk + hi) ^ f);
+                bf16x8v_t lf[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    lf[b] = *reinterpret_cast<const bf16x8v_t *>(st + 32768 + (wn + 32 * b + r) * 64 + off);
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const bf16x8v_t hf = *reinterpret_cast<const bf16x8v_t *>(st + (wm + 32 * a + r) * 64 + off);
+                    const bf16x8v_t lo =
+                        *reinterpret_cast<const bf16x8v_t *>(st + 16384 + (wm + 32 * a + r) * 64 + off);
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[b], hf, acc[a][b], 0, 0, 0);
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[b], lo, acc[a][b], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+
+    if (LR && !LRS) {
         for (int r0 = 0; r0 < g.r; r0 += 64) {
             // every wave is done with the previous contents of LDS
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -513,19 +598,19 @@ __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, con
 }
 
 // One workgroup per tile (or half tile) in the launch's work order.
-template <bool LR, bool B16>
+template <bool LR, bool B16, bool LRS = false>
 __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__restrict__ ca,
                                                            const uint8_t *__restrict__ psa,
                                                            const uint8_t *__restrict__ cw,
                                                            const uint8_t *__restrict__ psw, Geom g,
-                                                           const float *__restrict__ Z,
-                                                           const uint8_t *__restrict__ cl,
-                                                           const uint8_t *__restrict__ sl,
+                                                           const void *__restrict__ lr0,
+                                                           const void *__restrict__ lr1,
+                                                           const void *__restrict__ lr2,
                                                            void *__restrict__ O) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Lay<256>::kStage + 1024];
     const TileWork wk = tile_work((int)blockIdx.x, g.order);
-    if (wk.half < 0) gemm256_tile<LR, 256, B16>(ca, psa, cw, psw, g, Z, cl, sl, O, wk.tile, 0, smem);
-    else gemm256_tile<LR, 128, B16>(ca, psa, cw, psw, g, Z, cl, sl, O, wk.tile, wk.half, smem);
+    if (wk.half < 0) gemm256_tile<LR, 256, B16, LRS>(ca, psa, cw, psw, g, lr0, lr1, lr2, O, wk.tile, 0, smem);
+    else gemm256_tile<LR, 128, B16, LRS>(ca, psa, cw, psw, g, lr0, lr1, lr2, O, wk.tile, wk.half, smem);
 }
 
 // Compute units of the current device (cached per device; 256 on MI355X).
@@ -675,6 +760,44 @@ kq_status kq_mxfp4_gemm_packed_lowrank(const uint8_t *codes_a, const uint8_t *pa
     hipLaunchKernelGGL((kq::g256::gemm256_kernel<true, false>), dim3((unsigned)kq::g256::tile_order_groups(g.order)),
                        dim3(kq::g256::kThreads), 0, (hipStream_t)stream, codes_a, packed_scales_a, codes_w,
                        packed_scales_w, g, Z, codes_l, scales_l, O);
+    return launched();
+}
+
+
+kq_status kq_mxfp4_gemm_packed_lowrank_split(const uint8_t *codes_a, const uint8_t *packed_scales_a,
+                                             const uint8_t *codes_w, const uint8_t *packed_scales_w, int64_t m,
+                                             int64_t n, int64_t k, const uint16_t *Zh, const uint16_t *Zl,
+                                             const uint16_t *L16, int64_t r, float *O, int64_t ldo,
+                                             kq_stream_t stream) {
+    if (m < 0 || n < 0 || k < 0 || k % 256 != 0 || ldo < n || r <= 0 || r % 32 != 0) return KQ_ERR_SHAPE;
+    if (!kqhost::sizes_fit({m, n, k, ldo, r})) return KQ_ERR_UNSUPPORTED;
+    if (m == 0 || n == 0) return KQ_OK;
+    if (!O || !Zh || !Zl || !L16 || (k > 0 && (!codes_a || !packed_scales_a || !codes_w || !packed_scales_w)))
+        return KQ_ERR_NULL;
+    if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || !aligned(packed_scales_a, 16) ||
+        !aligned(packed_scales_w, 16) || !aligned(O, 4) || !aligned(Zh, 16) || !aligned(Zl, 16) ||
+        !aligned(L16, 16))
+        return KQ_ERR_ALIGN;
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
+    if ((int64_t)256 * (k / 2) >= lim || m * (k / 32) >= lim || n * (k / 32) >= lim ||
+        ((int64_t)255 * ldo + n) * 4 >= lim || tiles_m * tiles_n >= (lim >> 1) || (int64_t)256 * r * 2 >= lim)
+        return KQ_ERR_UNSUPPORTED;
+    kq::g256::Geom g;
+    g.m = m;
+    g.n = n;
+    g.ldo = ldo;
+    g.kbytes = (int)(k / 2);
+    g.stages = (int)(k / 256);
+    g.tiles_m = (int)tiles_m;
+    g.tiles_n = (int)tiles_n;
+    g.nwg = (int)(tiles_m * tiles_n);
+    g.rows16 = aligned(O, 16) && ldo % 4 == 0;
+    g.r = (int)r;
+    g.order = kq::g256::make_tile_order(g.nwg, kq::g256::cu_count());
+    hipLaunchKernelGGL((kq::g256::gemm256_kernel<true, false, true>),
+                       dim3((unsigned)kq::g256::tile_order_groups(g.order)), dim3(kq::g256::kThreads), 0,
+                       (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, Zh, Zl, L16, O);
     return launched();
 }
 

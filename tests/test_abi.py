@@ -105,6 +105,22 @@ GOOD = P(0x10000)  # never dereferenced: every case below fails before a launch
     ("kq_mxfp4_gemm_packed", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, P(0x10002), 4, None), kq.KQ_ERR_ALIGN),
     ("kq_mxfp4_gemm_packed", (GOOD, GOOD, GOOD, GOOD, 4, 4, 1 << 24, GOOD, 4, None), kq.KQ_ERR_UNSUPPORTED),
     ("kq_mxfp4_gemm_packed", (None, None, None, None, 0, 4, 256, None, 4, None), kq.KQ_OK),
+    ("kq_mxfp4_gemm_packed_lowrank_split", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, GOOD, GOOD, GOOD, 48, GOOD, 4, None),
+     kq.KQ_ERR_SHAPE),
+    ("kq_mxfp4_gemm_packed_lowrank_split", (GOOD, GOOD, GOOD, GOOD, 4, 4, 128, GOOD, GOOD, GOOD, 32, GOOD, 4, None),
+     kq.KQ_ERR_SHAPE),
+    ("kq_mxfp4_gemm_packed_lowrank_split", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, GOOD, None, GOOD, 32, GOOD, 4, None),
+     kq.KQ_ERR_NULL),
+    ("kq_mxfp4_gemm_packed_lowrank_split", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, GOOD, GOOD, P(0x10008), 32, GOOD, 4,
+                                            None), kq.KQ_ERR_ALIGN),
+    ("kq_mxfp4_gemm_packed_lowrank_split", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, GOOD, GOOD, GOOD, 1 << 22, GOOD, 4,
+                                            None), kq.KQ_ERR_UNSUPPORTED),
+    ("kq_mxfp4_gemm_packed_lowrank_split", (None, None, None, None, 0, 4, 256, None, None, None, 32, None, 4, None),
+     kq.KQ_OK),
+    ("kq_lowrank_project_bf16_split", (GOOD, 4, 64, 64, GOOD, 48, GOOD, GOOD, None), kq.KQ_ERR_SHAPE),
+    ("kq_lowrank_project_bf16_split", (GOOD, 4, 64, 64, GOOD, 32, GOOD, None, None), kq.KQ_ERR_NULL),
+    ("kq_lowrank_project_bf16_split", (GOOD, 4, 64, 64, GOOD, 32, P(0x10008), GOOD, None), kq.KQ_ERR_ALIGN),
+    ("kq_lowrank_project_bf16_split", (None, 0, 64, 64, None, 32, None, None, None), kq.KQ_OK),
     ("kq_mxfp4_gemm_packed_bf16", (GOOD, GOOD, GOOD, GOOD, 4, 4, 128, GOOD, 4, None), kq.KQ_ERR_SHAPE),
     ("kq_mxfp4_gemm_packed_bf16", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, GOOD, 3, None), kq.KQ_ERR_SHAPE),
     ("kq_mxfp4_gemm_packed_bf16", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, None, 4, None), kq.KQ_ERR_NULL),

@@ -208,6 +208,40 @@ def test_packed_gemm_lowrank_full_tiles_matches_oracle(torch_dev, kq, orc, m, n,
     assert not bad.any(), "%d elements outside the bound, first at %s" % (bad.sum(), np.argwhere(bad)[0])
 
 
+def split_bf16(torch, Z):
+    """Zh = bf16(Z), Zl = bf16(Z - Zh), both rounded to nearest even (torch's fp32 -> bf16)."""
+    Zh = Z.to(torch.bfloat16)
+    return Zh, (Z - Zh.float()).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("m,n,k,r", [(130, 70, 256, 32), (256, 256, 512, 128), (300, 520, 768, 160),
+                                     (6400, 3072, 512, 128), (5632, 3000, 256, 96), (5632, 3072, 512, 128),
+                                     (100, 70, 0, 64), (333, 2900, 256, 224)])
+def test_packed_gemm_lowrank_split_bit_identical(torch_dev, kq, m, n, k, r):
+    """The low-rank term from operands prepared once (Z split as Zh + Zl in bf16, deq(L) in
+    bf16, moved straight into LDS) against the fp32-Z form on the Z they split: the same
+    instructions in the same order, so every output bit agrees. Ragged shapes, several
+    32-wide chunks (r = 224: seven), whole rounds plus half tiles (6400 x 3072), the
+    staggered order (5632 x 3000, 5632 x 3072), k = 0 (the term alone), and half tiles
+    right of the last column (333 x 2900)."""
+    torch = torch_dev
+    case("packed gemm lowrank split %dx%dx%d r=%d" % (m, n, k, r))
+    rng = np.random.default_rng(m + n + k + r + 7)
+    ca, sa, cw, sw = operands(rng, m, n, k) if k > 0 else (np.zeros((m, 0), np.uint8), np.zeros((m, 0), np.uint8),
+                                                           np.zeros((n, 0), np.uint8), np.zeros((n, 0), np.uint8))
+    cl = rng.integers(0, 256, (n, r // 2), dtype=np.uint8)
+    sl = rng.integers(120, 128, (n, r // 32), dtype=np.uint8)
+    Z = (rng.standard_normal((m, r)) * 3.0).astype(np.float32)
+    dca, dsa, dcw, dsw = (dev(torch, x) for x in (ca, sa, cw, sw))
+    psa, psw = kq.pack_mxfp4_scales(dsa), kq.pack_mxfp4_scales(dsw)
+    dZ, dcl, dsl = dev(torch, Z), dev(torch, cl), dev(torch, sl)
+    O = kq.mxfp4_gemm_packed_lowrank(dca, psa, dcw, psw, dZ, dcl, dsl)
+    Zh, Zl = split_bf16(torch, dZ)
+    Os = kq.mxfp4_gemm_packed_lowrank_split(dca, psa, dcw, psw, Zh, Zl, kq.dequantize_mxfp4_bf16(dcl, dsl))
+    torch.cuda.synchronize()
+    assert torch.equal(O, Os)
+
+
 @pytest.mark.parametrize("m,n,k,pad,seed", [(1000, 700, 512, 0, 21), (300, 1100, 768, 3, 22), (257, 513, 256, 1, 23),
                                             (5632, 3072, 256, 0, 24), (5632, 3000, 256, 5, 25),
                                             (5632, 2900, 512, 0, 26), (18432, 3072, 3072, 0, 24)])

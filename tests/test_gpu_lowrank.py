@@ -125,6 +125,26 @@ def test_lowrank_project_bf16_matches(torch_dev, kq, orc, m, d, r):
     assert torch.equal(Z, Z16)
 
 
+@pytest.mark.parametrize("m,d,r", [(100, 96, 32), (300, 3072, 128), (81, 1152, 256), (18432, 3072, 128)])
+def test_lowrank_project_bf16_split_is_split_of_z(torch_dev, kq, orc, m, d, r):
+    """The split-output projection writes bf16(Z) and bf16(Z - bf16(Z)) of the very Z the
+    fp32-output projection computes, bit for bit."""
+    torch = torch_dev
+    case("project bf16 split %dx%d r=%d" % (m, d, r))
+    X = synth.random_bf16_matrix(m, d, seed=d + r + 11)
+    R = np.random.default_rng(r + 11).standard_normal((r, d)) / np.sqrt(d)
+    cr, sr = quantize_host(orc, R)
+    r16 = kq.dequantize_mxfp4_bf16(torch.from_numpy(cr).cuda(), torch.from_numpy(sr).cuda())
+    dX = dev_bf16(torch, X)
+    Z = kq.lowrank_project_bf16(dX, r16)
+    Zh, Zl = kq.lowrank_project_bf16_split(dX, r16)
+    torch.cuda.synchronize()
+    eh = Z.to(torch.bfloat16)
+    el = (Z - eh.float()).to(torch.bfloat16)
+    assert torch.equal(Zh.view(torch.int16), eh.view(torch.int16))
+    assert torch.equal(Zl.view(torch.int16), el.view(torch.int16))
+
+
 def test_lowrank_project_bf16_strided_x(torch_dev, kq, orc):
     """X16 a row-strided view (ldx = d + 64) over several 80-row tiles and a ragged last
     one: the same Z, bit for bit, as the in-workgroup decode path on the same view."""
@@ -250,3 +270,23 @@ def test_lowrank_layer_flux_packed_route(torch_dev, kq, flux_layer):
     worst = float((d / scale).max())
     print("[lowrank] packed vs check route: max |diff| / (row max + 1) %.3g" % worst, flush=True)
     assert worst <= 1e-4
+
+
+def test_lowrank_layer_flux_split_route(torch_dev, kq, flux_layer):
+    """The route with the branch's operands prepared once: the projection writes Z's bf16
+    split, L is decoded to bf16 once, and the packed GEMM moves both straight into LDS.
+    Bit-identical to the packed route (same Z, same instructions and order); sampled rows
+    against the oracle's layer."""
+    torch, F = torch_dev, flux_layer
+    case("lowrank layer 18432x3072x3072 r=128, split-operand route")
+    r16 = kq.dequantize_mxfp4_bf16(F["cr"], F["sr"])
+    Zh, Zl = kq.lowrank_project_bf16_split(F["y16"], r16)
+    psa, psw = kq.pack_mxfp4_scales(F["sa"]), kq.pack_mxfp4_scales(F["sw"])
+    O = kq.mxfp4_gemm_packed_lowrank_split(F["ca"], psa, F["cw"], psw, Zh, Zl,
+                                           kq.dequantize_mxfp4_bf16(F["cl"], F["sl"]))
+    Z = kq.lowrank_project_bf16(F["y16"], r16)
+    Op = kq.mxfp4_gemm_packed_lowrank(F["ca"], psa, F["cw"], psw, Z, F["cl"], F["sl"])
+    torch.cuda.synchronize()
+    assert torch.equal(O, Op)
+    rel = _report(torch, F, O, "split-operand route")
+    assert rel <= 1e-3
