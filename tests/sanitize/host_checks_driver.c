@@ -93,6 +93,14 @@ int main(void) {
                                                              P(0x10000), NULL, NULL), KQ_ERR_UNSUPPORTED);
     expect("packed overflow", kq_transform_quantize_mxfp4_packed(GOOD, BIG, 256, 256, GOOD, P(0x10000), P(0x10000),
                                                                  NULL, NULL), KQ_ERR_SHAPE);
+    expect("lowrank split r", kq_mxfp4_gemm_packed_lowrank_split(GOOD, GOOD, GOOD, GOOD, 4, 4, 256, GOOD, GOOD, GOOD, 48,
+                                                                  P(0x10000), 4, NULL),
+           KQ_ERR_SHAPE);
+    expect("lowrank split huge", kq_mxfp4_gemm_packed_lowrank_split(GOOD, GOOD, GOOD, GOOD, BIG, 4, 256, GOOD, GOOD, GOOD,
+                                                                     32, P(0x10000), 4, NULL),
+           KQ_ERR_UNSUPPORTED);
+    expect("project split huge", kq_lowrank_project_bf16_split(GOOD, BIG, 64, 64, GOOD, 32, P(0x10000), P(0x10000), NULL),
+           KQ_ERR_UNSUPPORTED);
     expect("y16 huge", kq_transform_quantize_mxfp4_y16(GOOD, BIG, 64, 64, GOOD, P(0x10000), P(0x10000), P(0x10000),
                                                        NULL), KQ_ERR_SHAPE);
     expect("smooth huge", kq_smoothquant_quantize_mxfp4(GOOD, 4, BIG / 64 * 32, BIG, GOOD, P(0x10000), P(0x10000),
