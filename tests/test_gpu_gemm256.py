@@ -242,6 +242,33 @@ def test_packed_gemm_lowrank_split_bit_identical(torch_dev, kq, m, n, k, r):
     assert torch.equal(O, Os)
 
 
+@pytest.mark.parametrize("m,n,k,r,pad", [(300, 520, 512, 96, 5), (6400, 2900, 256, 128, 3)])
+def test_packed_gemm_lowrank_split_padded_output(torch_dev, kq, m, n, k, r, pad):
+    """The split low-rank form writing into a row-strided output (ldo = n + pad, the row
+    ends taking element stores): the same bits as into a contiguous one, and the padding
+    columns and the bytes after the last row untouched."""
+    torch = torch_dev
+    case("packed gemm lowrank split padded %dx%dx%d r=%d ldo=%d" % (m, n, k, r, n + pad))
+    rng = np.random.default_rng(m + n + k + r + pad)
+    ca, sa, cw, sw = operands(rng, m, n, k)
+    Zh = torch.from_numpy((rng.standard_normal((m, r)) * 3.0).astype(np.float32)).cuda().to(torch.bfloat16)
+    Zl = torch.from_numpy((rng.standard_normal((m, r)) * 2.0 ** -8).astype(np.float32)).cuda().to(torch.bfloat16)
+    cl = rng.integers(0, 256, (n, r // 2), dtype=np.uint8)
+    sl = rng.integers(120, 128, (n, r // 32), dtype=np.uint8)
+    dca, dsa, dcw, dsw = (dev(torch, x) for x in (ca, sa, cw, sw))
+    psa, psw = kq.pack_mxfp4_scales(dsa), kq.pack_mxfp4_scales(dsw)
+    L16 = kq.dequantize_mxfp4_bf16(dev(torch, cl), dev(torch, sl))
+    ref = kq.mxfp4_gemm_packed_lowrank_split(dca, psa, dcw, psw, Zh, Zl, L16)
+    ldo = n + pad
+    buf = torch.full((m * ldo + 64,), -7.0, dtype=torch.float32, device="cuda")
+    out = buf[:m * ldo].view(m, ldo)[:, :n]
+    kq.mxfp4_gemm_packed_lowrank_split(dca, psa, dcw, psw, Zh, Zl, L16, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert bool((buf[:m * ldo].view(m, ldo)[:, n:] == -7.0).all())
+    assert bool((buf[m * ldo:] == -7.0).all())
+
+
 @pytest.mark.parametrize("m,n,k,pad,seed", [(1000, 700, 512, 0, 21), (300, 1100, 768, 3, 22), (257, 513, 256, 1, 23),
                                             (5632, 3072, 256, 0, 24), (5632, 3000, 256, 5, 25),
                                             (5632, 2900, 512, 0, 26), (18432, 3072, 3072, 0, 24)])

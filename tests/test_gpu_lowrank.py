@@ -147,7 +147,8 @@ def test_lowrank_project_bf16_split_is_split_of_z(torch_dev, kq, orc, m, d, r):
 
 def test_lowrank_project_bf16_strided_x(torch_dev, kq, orc):
     """X16 a row-strided view (ldx = d + 64) over several 80-row tiles and a ragged last
-    one: the same Z, bit for bit, as the in-workgroup decode path on the same view."""
+    one: the same Z, bit for bit, as the in-workgroup decode path on the same view, and the
+    split-output form writes its bf16 split."""
     torch = torch_dev
     m, d, r, pad = 333, 1152, 96, 64
     case("project bf16 strided X %dx%d ldx=%d r=%d" % (m, d, d + pad, r))
@@ -160,8 +161,12 @@ def test_lowrank_project_bf16_strided_x(torch_dev, kq, orc):
     Z = kq.lowrank_project(dX, dcr, dsr)
     Z16 = kq.lowrank_project_bf16(dX, kq.dequantize_mxfp4_bf16(dcr, dsr))
     Zc = kq.lowrank_project_bf16(dX.contiguous(), kq.dequantize_mxfp4_bf16(dcr, dsr))
+    Zh, Zl = kq.lowrank_project_bf16_split(dX, kq.dequantize_mxfp4_bf16(dcr, dsr))
     torch.cuda.synchronize()
     assert torch.equal(Z, Z16) and torch.equal(Z16, Zc)
+    eh = Z16.to(torch.bfloat16)
+    assert torch.equal(Zh.view(torch.int16), eh.view(torch.int16))
+    assert torch.equal(Zl.view(torch.int16), (Z16 - eh.float()).to(torch.bfloat16).view(torch.int16))
 
 
 @pytest.mark.parametrize("m,n,k,r", [(130, 70, 96, 32), (256, 256, 512, 128), (200, 130, 256, 160)])
