@@ -335,18 +335,23 @@ def test_packed_gemm_flux_layer(torch_dev, kq, orc):
         np.max(np.abs(got[rows] - ref) / (np.abs(ref) + 1e-30))), flush=True)
 
 
-@pytest.mark.parametrize("m,d,seed", [(37, 256, 31), (300, 768, 32), (1000, 3072, 33), (5, 1024, 34)])
-def test_quantizer_packed_scales_equal_pack_of_scales(torch_dev, kq, m, d, seed):
+@pytest.mark.parametrize("m,d,seed,swap", [(37, 256, 31, ()), (300, 768, 32, ()), (1000, 3072, 33, ()),
+                                            (5, 1024, 34, ()), (300, 768, 35, (3, 17)), (1000, 3072, 36, (40,))])
+def test_quantizer_packed_scales_equal_pack_of_scales(torch_dev, kq, m, d, seed, swap):
     """kq_transform_quantize_mxfp4_packed writes the quantizer's codes and, byte for byte,
     pack_mxfp4_scales of its scales (d = 768 leaves the last 512-channel segment half
-    empty, m = 5 and 37 ragged row groups); with y16, also the y16 entry point's bf16 y.
-    Bytes after the packed array stay untouched."""
+    empty, m = 5 and 37 ragged row groups; `swap` lists blocks whose G2 is a swap, which has
+    no shear form, so their segments run the general 2x2 stages); with y16, also the y16
+    entry point's bf16 y. Bytes after the packed array stay untouched."""
     import synth
     torch = torch_dev
-    case("quantizer packed scales m=%d d=%d" % (m, d))
+    case("quantizer packed scales m=%d d=%d swap=%s" % (m, d, swap))
     A = torch.from_numpy(synth.random_bf16_matrix(m, d, seed=seed, scale=3.0).view(np.int16)).cuda().view(
         torch.bfloat16)
-    fac = dev(torch, synth.lu_perturbed_factors(d // 32, seed=seed + 1))
+    fac_h = synth.lu_perturbed_factors(d // 32, seed=seed + 1)
+    for blk in swap:
+        fac_h[blk, 1] = np.array([[0.0, 1.0], [1.0, 0.0]], np.float32)
+    fac = dev(torch, fac_h)
     ca, sa = kq.transform_quantize_mxfp4(A, fac)
     ca16, sa16, y16 = kq.transform_quantize_mxfp4_y16(A, fac)
     guard = torch.full((m * (d // 32) + 64,), 0xEE, dtype=torch.uint8, device="cuda")
