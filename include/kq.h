@@ -176,8 +176,12 @@ kq_status kq_inverse_fold_weights(const float *W, int64_t o, int64_t d, const fl
  *   scales_w  device, [n][k/32]
  *   O         device, fp32 [m][ldo], ldo >= n; written, not accumulated into
  * k must be a multiple of 32 (KQ_ERR_SHAPE) and k/2 a multiple of 16 (KQ_ERR_ALIGN).
- * Summation order inside the matrix instruction is the hardware's; results
- * agree with an fp64 sum of the same dequantized products to fp32 rounding.
+ * When k is a positive multiple of 256 and the scales and O are 4-byte aligned,
+ * the product runs on the 256 x 256-tile kernel of kq_mxfp4_gemm_packed, which
+ * then reads these MX-layout scales directly (bit-identical to the packed-scale
+ * call on the same operands); otherwise on a 128 x 128-tile kernel. Summation
+ * order inside the matrix instruction is the hardware's; results agree with an
+ * fp64 sum of the same dequantized products to fp32 rounding.
  */
 kq_status kq_mxfp4_gemm(const uint8_t *codes_a, const uint8_t *scales_a, const uint8_t *codes_w,
                         const uint8_t *scales_w, int64_t m, int64_t n, int64_t k, float *O, int64_t ldo,
@@ -421,7 +425,9 @@ kq_status kq_dequantize_mxfp4_bf16(const uint8_t *codes, const uint8_t *scales, 
  *   codes_a ... ldo   as kq_mxfp4_gemm (W here is the residual W~ - L R)
  *   Z                 device, fp32 [m][r], 16-byte aligned (kq_lowrank_project)
  *   codes_l, scales_l device, L in MXFP4: [n][r/2] (16-byte aligned), [n][r/32]
- * r > 0, r % 32 == 0 (KQ_ERR_SHAPE).
+ * r > 0, r % 32 == 0 (KQ_ERR_SHAPE). Kernel choice as kq_mxfp4_gemm: with k a
+ * positive multiple of 256, that of kq_mxfp4_gemm_packed_lowrank on these
+ * MX-layout scales (bit-identical to it).
  */
 kq_status kq_mxfp4_gemm_lowrank(const uint8_t *codes_a, const uint8_t *scales_a, const uint8_t *codes_w,
                                 const uint8_t *scales_w, int64_t m, int64_t n, int64_t k, const float *Z,

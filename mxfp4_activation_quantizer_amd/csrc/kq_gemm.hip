@@ -565,6 +565,15 @@ using kqhost::aligned;
 using kqhost::launched;
 }  // namespace
 
+namespace kqhost {
+kq_status gemm256_mx(const uint8_t *codes_a, const uint8_t *scales_a, const uint8_t *codes_w, const uint8_t *scales_w,
+                     int64_t m, int64_t n, int64_t k, float *O, int64_t ldo, kq_stream_t stream);
+kq_status gemm256_mx_lowrank(const uint8_t *codes_a, const uint8_t *scales_a, const uint8_t *codes_w,
+                             const uint8_t *scales_w, int64_t m, int64_t n, int64_t k, const float *Z,
+                             const uint8_t *codes_l, const uint8_t *scales_l, int64_t r, float *O, int64_t ldo,
+                             kq_stream_t stream);
+}  // namespace kqhost
+
 namespace {
 
 template <bool SPLIT>
@@ -600,6 +609,13 @@ kq_status kq_mxfp4_gemm(const uint8_t *codes_a, const uint8_t *scales_a, const u
     if (m == 0 || n == 0) return KQ_OK;
     if (!codes_a || !scales_a || !codes_w || !scales_w || !O) return KQ_ERR_NULL;
     if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || (k / 2) % 16 != 0) return KQ_ERR_ALIGN;
+    // k a multiple of 256: the 256 x 256-tile kernel reading the MX-layout scales
+    // (the same instruction and k order as the packed-scale product); when it takes
+    // the shape, it runs
+    if (k > 0 && k % 256 == 0 && aligned(scales_a, 4) && aligned(scales_w, 4) && aligned(O, 4)) {
+        const kq_status st = kqhost::gemm256_mx(codes_a, scales_a, codes_w, scales_w, m, n, k, O, ldo, stream);
+        if (st != KQ_ERR_UNSUPPORTED) return st;
+    }
     const int64_t tiles_m = (m + kq::kGemmTile - 1) / kq::kGemmTile, tiles_n = (n + kq::kGemmTile - 1) / kq::kGemmTile;
     if (tiles_m * tiles_n > 0x7FFFFFFF || m > INT64_MAX / 4 / (ldo > 0 ? ldo : 1)) return KQ_ERR_SHAPE;
     kq::GemmGeom g{m, n, k, ldo, tiles_n, 0};
@@ -619,6 +635,13 @@ kq_status kq_mxfp4_gemm_lowrank(const uint8_t *codes_a, const uint8_t *scales_a,
     if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || (k / 2) % 16 != 0 || !aligned(Z, 16) ||
         !aligned(codes_l, 16))
         return KQ_ERR_ALIGN;
+    // k a multiple of 256: the 256 x 256-tile kernel with the term in its epilogue,
+    // reading the MX-layout scales (as kq_mxfp4_gemm)
+    if (k > 0 && k % 256 == 0 && aligned(scales_a, 4) && aligned(scales_w, 4) && aligned(O, 4)) {
+        const kq_status st = kqhost::gemm256_mx_lowrank(codes_a, scales_a, codes_w, scales_w, m, n, k, Z, codes_l,
+                                                        scales_l, r, O, ldo, stream);
+        if (st != KQ_ERR_UNSUPPORTED) return st;
+    }
     const int64_t tiles_m = (m + kq::kGemmTile - 1) / kq::kGemmTile, tiles_n = (n + kq::kGemmTile - 1) / kq::kGemmTile;
     if (tiles_m * tiles_n > 0x7FFFFFFF || m > INT64_MAX / 4 / (ldo > 0 ? ldo : 1) || m > INT64_MAX / 4 / r)
         return KQ_ERR_SHAPE;

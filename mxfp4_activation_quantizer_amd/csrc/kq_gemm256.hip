@@ -122,6 +122,20 @@ __device__ __forceinline__ void dma16(const i32x4_t &d, uint32_t lds, uint32_t v
         : "memory");
 }
 
+// 4 bytes per lane from the buffer straight into LDS: lane l's bytes land at lds + 4 l.
+__device__ __forceinline__ void dma4(const i32x4_t &d, uint32_t lds, uint32_t voff) {
+    uint32_t keep;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(keep)
+        : "s"(lds), "v"(voff), "s"(d)
+        : "memory");
+}
+
 __device__ __forceinline__ void wait_loads_and_lds_then_barrier() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -153,7 +167,7 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 //
 // One tile (run-order number u; half h of it when TN = 128) of one workgroup;
 // smem holds 2 stages of the full-width layout plus 1 KB.
-template <bool LR, int TN, bool B16, bool LRS = false>
+template <bool LR, int TN, bool B16, bool LRS = false, bool NS = false>
 __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, const uint8_t *__restrict__ psa,
                                              const uint8_t *__restrict__ cw, const uint8_t *__restrict__ psw,
                                              const Geom g, const void *__restrict__ lr0,
@@ -185,6 +199,8 @@ __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, con
     // never stored), or zero on the last stage
     const i32x4_t dsa = sdesc(psa, (uint32_t)(g.stages * 8 * g.m));
     const i32x4_t dsw = sdesc(psw, (uint32_t)(g.stages * 8 * g.n));
+    // (NS) scales in the MX layout [rows][k / 32]: row i's eight bytes of stage s at
+    // (k / 32) i + 8 s, blocks in order; same record counts (k / 32 = 8 stages)
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
     // code load j of wave w: A rows 64 w + 8 j + (lane >> 3) (j < 8), W rows
@@ -217,7 +233,21 @@ __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, con
     const i32x4_t dss = sw_a ? dsa : dsw;
     const uint32_t srow_off = (uint32_t)(8 * ((sw_a ? m0 : n0) + srow)), s_stride = (uint32_t)(8 * (sw_a ? g.m : g.n));
     const uint32_t s_lds = sw_none ? (uint32_t)(2 * kStage) : (uint32_t)((sw_a ? L::kOffSA : L::kOffSW) + 1024 * (w & 1));
+    // (NS) four loads of 256 bytes per wave and stage: load j, lane l: row
+    // 128 (w & 1) + 32 j + l / 2 of the wave's operand, its dword l & 1 of the stage,
+    // into the same [rows][8] bytes of LDS (blocks in order instead of even first)
+    const uint32_t ns_row = (uint32_t)(((sw_a ? m0 : n0) + 128 * (w & 1) + (lane >> 1)) * (int64_t)(8 * g.stages)) +
+                            4u * (uint32_t)(lane & 1);
+    auto issue_scl_ns = [&](int s, int j) {
+        const uint32_t voff = sw_none ? 0x80000000u : ns_row + (uint32_t)(32 * j * 8 * g.stages + 8 * s);
+        dma4(dss, lds0 + (uint32_t)((s & 1) * kStage) * !sw_none + s_lds + 256u * (uint32_t)j, voff);
+    };
     auto issue_scl = [&](int s) {
+        if constexpr (NS) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) issue_scl_ns(s, j);
+            return;
+        }
         const uint32_t voff = sw_none ? 0x80000000u : srow_off + s_stride * (uint32_t)s;
         dma16(dss, lds0 + (uint32_t)((s & 1) * kStage) * !sw_none + s_lds, voff, 0u);
     };
@@ -229,7 +259,24 @@ __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, con
     for (int j = 0; j < 4; ++j) rdo[j] = r * 128 + 16 * ((2 * j + hi) ^ swz8(r & 15));
 
     // stage s: the scale dword of the lane's block parity hi (byte j is block 2 j + hi)
+    // (NS) the dword of parity hi gathered from the row's two dwords: bytes of
+    // blocks hi, 2 + hi (first dword) and 4 + hi, 6 + hi (second)
+    const uint32_t ns_sel = hi ? 0x07050301u : 0x06040200u;
     auto read_scl = [&](int s, Scl<NB> &S) {
+        if constexpr (NS) {
+            const uint8_t *sc = smem + (s & 1) * kStage + 8 * r;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const uint2 d = *reinterpret_cast<const uint2 *>(sc + L::kOffSA + 8 * (wm + 32 * a));
+                S.sa[a] = __builtin_amdgcn_perm(d.y, d.x, ns_sel);
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const uint2 d = *reinterpret_cast<const uint2 *>(sc + L::kOffSW + 8 * (wn + 32 * b));
+                S.sb[b] = __builtin_amdgcn_perm(d.y, d.x, ns_sel);
+            }
+            return;
+        }
         const uint8_t *sc = smem + (s & 1) * kStage + 4 * hi + 8 * r;
 #pragma unroll
         for (int a = 0; a < 4; ++a) S.sa[a] = *reinterpret_cast<const uint32_t *>(sc + L::kOffSA + 8 * (wm + 32 * a));
@@ -351,10 +398,11 @@ __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, con
     read_frags(0, 0, F0);
 
     // load l of stage s: 0 .. 8 + LW - 1 the code loads, 8 + LW the scale load
-    constexpr int kLoads = 8 + LW + 1, kPerStep = (kLoads + kLoadSteps - 1) / kLoadSteps;
+    constexpr int kLoads = 8 + LW + (NS ? 4 : 1), kPerStep = (kLoads + kLoadSteps - 1) / kLoadSteps;
     static_assert(kPerStep <= 4 * NB && kLoadSteps <= 3, "every load of a stage needs a slot before the wait");
     auto issue_load = [&](int s, int l) {
         if (l < 8 + LW) issue_code(s, l);
+        else if (NS) issue_scl_ns(s, l - (8 + LW));
         else issue_scl(s);
     };
     // step j of stage s with stage s + 1's loads kPerStep j .. placed one after
@@ -598,7 +646,7 @@ __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, con
 }
 
 // One workgroup per tile (or half tile) in the launch's work order.
-template <bool LR, bool B16, bool LRS = false>
+template <bool LR, bool B16, bool LRS = false, bool NS = false>
 __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__restrict__ ca,
                                                            const uint8_t *__restrict__ psa,
                                                            const uint8_t *__restrict__ cw,
@@ -609,8 +657,8 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
                                                            void *__restrict__ O) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Lay<256>::kStage + 1024];
     const TileWork wk = tile_work((int)blockIdx.x, g.order);
-    if (wk.half < 0) gemm256_tile<LR, 256, B16, LRS>(ca, psa, cw, psw, g, lr0, lr1, lr2, O, wk.tile, 0, smem);
-    else gemm256_tile<LR, 128, B16, LRS>(ca, psa, cw, psw, g, lr0, lr1, lr2, O, wk.tile, wk.half, smem);
+    if (wk.half < 0) gemm256_tile<LR, 256, B16, LRS, NS>(ca, psa, cw, psw, g, lr0, lr1, lr2, O, wk.tile, 0, smem);
+    else gemm256_tile<LR, 128, B16, LRS, NS>(ca, psa, cw, psw, g, lr0, lr1, lr2, O, wk.tile, wk.half, smem);
 }
 
 // Compute units of the current device (cached per device; 256 on MI355X).
@@ -676,17 +724,19 @@ namespace {
 // tiles and the last partial round as half-width tiles when twice its tile count
 // still fits one round of CUs (e.g. 864 tiles on 256 CUs: 768 full, then 96 tiles as
 // 192 halves, about half a round instead of a whole one).
-template <bool B16>
+// NS: the scales in the MX layout [rows][k / 32] (4-byte aligned) instead of packed.
+template <bool B16, bool NS = false>
 kq_status gemm_packed(const uint8_t *codes_a, const uint8_t *packed_scales_a, const uint8_t *codes_w,
                       const uint8_t *packed_scales_w, int64_t m, int64_t n, int64_t k, void *O, int64_t ldo,
                       kq_stream_t stream) {
     constexpr int esz = B16 ? 2 : 4;
+    constexpr int sal = NS ? 4 : 16;
     if (m < 0 || n < 0 || k < 0 || k % 256 != 0 || ldo < n) return KQ_ERR_SHAPE;
     if (!kqhost::sizes_fit({m, n, k, ldo})) return KQ_ERR_UNSUPPORTED;
     if (m == 0 || n == 0) return KQ_OK;
     if (!O || (k > 0 && (!codes_a || !packed_scales_a || !codes_w || !packed_scales_w))) return KQ_ERR_NULL;
-    if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || !aligned(packed_scales_a, 16) ||
-        !aligned(packed_scales_w, 16) || !aligned(O, esz))
+    if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || !aligned(packed_scales_a, sal) ||
+        !aligned(packed_scales_w, sal) || !aligned(O, esz))
         return KQ_ERR_ALIGN;
     // buffer record counts and offsets are 32-bit
     const int64_t lim = (int64_t)1 << 31;
@@ -706,13 +756,68 @@ kq_status gemm_packed(const uint8_t *codes_a, const uint8_t *packed_scales_a, co
     g.rows16 = aligned(O, 16) && (ldo * esz) % 16 == 0;
     g.r = 0;
     g.order = kq::g256::make_tile_order(g.nwg, kq::g256::cu_count());
-    hipLaunchKernelGGL((kq::g256::gemm256_kernel<false, B16>), dim3((unsigned)kq::g256::tile_order_groups(g.order)),
-                       dim3(kq::g256::kThreads), 0, (hipStream_t)stream, codes_a, packed_scales_a, codes_w,
-                       packed_scales_w, g, nullptr, nullptr, nullptr, O);
+    hipLaunchKernelGGL((kq::g256::gemm256_kernel<false, B16, false, NS>),
+                       dim3((unsigned)kq::g256::tile_order_groups(g.order)), dim3(kq::g256::kThreads), 0,
+                       (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, nullptr, nullptr,
+                       nullptr, O);
+    return launched();
+}
+
+// NS: the scales in the MX layout [rows][k / 32] (4-byte aligned) instead of packed.
+template <bool NS>
+kq_status gemm_lowrank(const uint8_t *codes_a, const uint8_t *packed_scales_a, const uint8_t *codes_w,
+                       const uint8_t *packed_scales_w, int64_t m, int64_t n, int64_t k, const float *Z,
+                       const uint8_t *codes_l, const uint8_t *scales_l, int64_t r, float *O, int64_t ldo,
+                       kq_stream_t stream) {
+    constexpr int sal = NS ? 4 : 16;
+    if (m < 0 || n < 0 || k < 0 || k % 256 != 0 || ldo < n || r <= 0 || r % 32 != 0) return KQ_ERR_SHAPE;
+    if (!kqhost::sizes_fit({m, n, k, ldo, r})) return KQ_ERR_UNSUPPORTED;
+    if (m == 0 || n == 0) return KQ_OK;
+    if (!O || !Z || !codes_l || !scales_l || (k > 0 && (!codes_a || !packed_scales_a || !codes_w || !packed_scales_w)))
+        return KQ_ERR_NULL;
+    if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || !aligned(packed_scales_a, sal) ||
+        !aligned(packed_scales_w, sal) || !aligned(O, 4) || !aligned(Z, 16) || !aligned(codes_l, 4))
+        return KQ_ERR_ALIGN;
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
+    if ((int64_t)256 * (k / 2) >= lim || m * (k / 32) >= lim || n * (k / 32) >= lim ||
+        ((int64_t)255 * ldo + n) * 4 >= lim || tiles_m * tiles_n >= (lim >> 1) || (int64_t)256 * r * 4 + 32 >= lim)
+        return KQ_ERR_UNSUPPORTED;
+    kq::g256::Geom g;
+    g.m = m;
+    g.n = n;
+    g.ldo = ldo;
+    g.kbytes = (int)(k / 2);
+    g.stages = (int)(k / 256);
+    g.tiles_m = (int)tiles_m;
+    g.tiles_n = (int)tiles_n;
+    g.nwg = (int)(tiles_m * tiles_n);
+    g.rows16 = aligned(O, 16) && ldo % 4 == 0;
+    g.r = (int)r;
+    g.order = kq::g256::make_tile_order(g.nwg, kq::g256::cu_count());
+    hipLaunchKernelGGL((kq::g256::gemm256_kernel<true, false, false, NS>),
+                       dim3((unsigned)kq::g256::tile_order_groups(g.order)), dim3(kq::g256::kThreads), 0,
+                       (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, Z, codes_l,
+                       scales_l, O);
     return launched();
 }
 
 }  // namespace
+
+namespace kqhost {
+// The MX-layout product on the 256 x 256-tile kernel (k % 256 == 0), for kq_mxfp4_gemm.
+kq_status gemm256_mx(const uint8_t *codes_a, const uint8_t *scales_a, const uint8_t *codes_w, const uint8_t *scales_w,
+                     int64_t m, int64_t n, int64_t k, float *O, int64_t ldo, kq_stream_t stream) {
+    return gemm_packed<false, true>(codes_a, scales_a, codes_w, scales_w, m, n, k, O, ldo, stream);
+}
+// The same with the low-rank term (fp32 Z, MXFP4 L), for kq_mxfp4_gemm_lowrank.
+kq_status gemm256_mx_lowrank(const uint8_t *codes_a, const uint8_t *scales_a, const uint8_t *codes_w,
+                             const uint8_t *scales_w, int64_t m, int64_t n, int64_t k, const float *Z,
+                             const uint8_t *codes_l, const uint8_t *scales_l, int64_t r, float *O, int64_t ldo,
+                             kq_stream_t stream) {
+    return gemm_lowrank<true>(codes_a, scales_a, codes_w, scales_w, m, n, k, Z, codes_l, scales_l, r, O, ldo, stream);
+}
+}  // namespace kqhost
 
 extern "C" {
 
@@ -732,35 +837,8 @@ kq_status kq_mxfp4_gemm_packed_lowrank(const uint8_t *codes_a, const uint8_t *pa
                                        const uint8_t *codes_w, const uint8_t *packed_scales_w, int64_t m, int64_t n,
                                        int64_t k, const float *Z, const uint8_t *codes_l, const uint8_t *scales_l,
                                        int64_t r, float *O, int64_t ldo, kq_stream_t stream) {
-    if (m < 0 || n < 0 || k < 0 || k % 256 != 0 || ldo < n || r <= 0 || r % 32 != 0) return KQ_ERR_SHAPE;
-    if (!kqhost::sizes_fit({m, n, k, ldo, r})) return KQ_ERR_UNSUPPORTED;
-    if (m == 0 || n == 0) return KQ_OK;
-    if (!O || !Z || !codes_l || !scales_l || (k > 0 && (!codes_a || !packed_scales_a || !codes_w || !packed_scales_w)))
-        return KQ_ERR_NULL;
-    if (!aligned(codes_a, 16) || !aligned(codes_w, 16) || !aligned(packed_scales_a, 16) ||
-        !aligned(packed_scales_w, 16) || !aligned(O, 4) || !aligned(Z, 16) || !aligned(codes_l, 4))
-        return KQ_ERR_ALIGN;
-    const int64_t lim = (int64_t)1 << 31;
-    const int64_t tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
-    if ((int64_t)256 * (k / 2) >= lim || m * (k / 32) >= lim || n * (k / 32) >= lim ||
-        ((int64_t)255 * ldo + n) * 4 >= lim || tiles_m * tiles_n >= (lim >> 1) || (int64_t)256 * r * 4 + 32 >= lim)
-        return KQ_ERR_UNSUPPORTED;
-    kq::g256::Geom g;
-    g.m = m;
-    g.n = n;
-    g.ldo = ldo;
-    g.kbytes = (int)(k / 2);
-    g.stages = (int)(k / 256);
-    g.tiles_m = (int)tiles_m;
-    g.tiles_n = (int)tiles_n;
-    g.nwg = (int)(tiles_m * tiles_n);
-    g.rows16 = aligned(O, 16) && ldo % 4 == 0;
-    g.r = (int)r;
-    g.order = kq::g256::make_tile_order(g.nwg, kq::g256::cu_count());
-    hipLaunchKernelGGL((kq::g256::gemm256_kernel<true, false>), dim3((unsigned)kq::g256::tile_order_groups(g.order)),
-                       dim3(kq::g256::kThreads), 0, (hipStream_t)stream, codes_a, packed_scales_a, codes_w,
-                       packed_scales_w, g, Z, codes_l, scales_l, O);
-    return launched();
+    return gemm_lowrank<false>(codes_a, packed_scales_a, codes_w, packed_scales_w, m, n, k, Z, codes_l, scales_l, r, O,
+                               ldo, stream);
 }
 
 

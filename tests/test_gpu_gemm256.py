@@ -208,6 +208,51 @@ def test_packed_gemm_lowrank_full_tiles_matches_oracle(torch_dev, kq, orc, m, n,
     assert not bad.any(), "%d elements outside the bound, first at %s" % (bad.sum(), np.argwhere(bad)[0])
 
 
+@pytest.mark.parametrize("m,n,k,pad", [(130, 70, 256, 0), (300, 520, 768, 3), (6400, 3072, 512, 0),
+                                        (5632, 3000, 256, 1), (333, 2900, 512, 0), (5, 257, 1024, 2)])
+def test_mx_layout_gemm_is_packed_gemm(torch_dev, kq, orc, m, n, k, pad):
+    """kq_mxfp4_gemm with k a multiple of 256 runs the 256 x 256-tile kernel on the
+    MX-layout scales (each stage's eight bytes per row gathered from [rows][k / 32]):
+    bit for bit the packed-scale product on the same operands, whole tiles, half tiles
+    and the staggered order (6400 x 3072, 5632 x 3000), ragged rows and columns, a
+    row-strided output with its padding untouched; checked against the oracle's sums too."""
+    torch = torch_dev
+    case("mx-layout gemm %dx%dx%d ldo=%d" % (m, n, k, n + pad))
+    rng = np.random.default_rng(m + n + k + pad + 5)
+    ca, sa, cw, sw = operands(rng, m, n, k)
+    dca, dsa, dcw, dsw = (dev(torch, x) for x in (ca, sa, cw, sw))
+    ref = kq.mxfp4_gemm_packed(dca, kq.pack_mxfp4_scales(dsa), dcw, kq.pack_mxfp4_scales(dsw))
+    ldo = n + pad
+    buf = torch.full((m * ldo + 32,), -3.0, dtype=torch.float32, device="cuda")
+    out = buf[:m * ldo].view(m, ldo)[:, :n]
+    kq.mxfp4_gemm(dca, dsa, dcw, dsw, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert bool((buf[:m * ldo].view(m, ldo)[:, n:] == -3.0).all()) and bool((buf[m * ldo:] == -3.0).all())
+    if m * n <= 400000:
+        got = out.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - orc.gemm_dequant(ca, sa, cw, sw, k)) <= bound(orc, ca, sa, cw, sw, k))
+
+
+@pytest.mark.parametrize("m,n,k,r", [(130, 70, 256, 32), (6400, 3072, 512, 128), (5632, 3000, 256, 96)])
+def test_mx_layout_gemm_lowrank_is_packed(torch_dev, kq, m, n, k, r):
+    """kq_mxfp4_gemm_lowrank with k a multiple of 256 runs the 256 x 256-tile kernel with
+    the low-rank term, on the MX-layout scales: bit for bit the packed-scale form."""
+    torch = torch_dev
+    case("mx-layout gemm lowrank %dx%dx%d r=%d" % (m, n, k, r))
+    rng = np.random.default_rng(m + n + k + r + 9)
+    ca, sa, cw, sw = operands(rng, m, n, k)
+    cl = rng.integers(0, 256, (n, r // 2), dtype=np.uint8)
+    sl = rng.integers(120, 128, (n, r // 32), dtype=np.uint8)
+    Z = (rng.standard_normal((m, r)) * 3.0).astype(np.float32)
+    dca, dsa, dcw, dsw = (dev(torch, x) for x in (ca, sa, cw, sw))
+    dZ, dcl, dsl = dev(torch, Z), dev(torch, cl), dev(torch, sl)
+    ref = kq.mxfp4_gemm_packed_lowrank(dca, kq.pack_mxfp4_scales(dsa), dcw, kq.pack_mxfp4_scales(dsw), dZ, dcl, dsl)
+    O = kq.mxfp4_gemm_lowrank(dca, dsa, dcw, dsw, dZ, dcl, dsl)
+    torch.cuda.synchronize()
+    assert torch.equal(O, ref)
+
+
 def split_bf16(torch, Z):
     """Zh = bf16(Z), Zl = bf16(Z - Zh), both rounded to nearest even (torch's fp32 -> bf16)."""
     Zh = Z.to(torch.bfloat16)
