@@ -386,6 +386,15 @@ def lowrank_layer_timing(torch, kq, A, fac, cw, sw, W, r=128, reps=20):
         kq.lowrank_project_bf16_split(y16, r16, Zh=Zh, Zl=Zl)
         kq.mxfp4_gemm_packed_lowrank_split(ca, psa, cw, psw, Zh, Zl, l16, out=O)
     res["layer_with_branch_split_prepared_region_us"] = med(layer_split_prepared)
+
+    # R kept in MXFP4 (the projection's producers decode it) and L decoded once per weight
+    res["project_split_mx_r_us"] = med(lambda: kq.lowrank_project_split(y16, cr, sr, Zh=Zh, Zl=Zl))
+
+    def layer_mx_r():
+        kq.transform_quantize_mxfp4_packed(A, fac, codes=ca, packed_scales=psa, y16=y16)
+        kq.lowrank_project_split(y16, cr, sr, Zh=Zh, Zl=Zl)
+        kq.mxfp4_gemm_packed_lowrank_split(ca, psa, cw, psw, Zh, Zl, l16, out=O)
+    res["layer_with_branch_mx_r_region_us"] = med(layer_mx_r)
     return res
 
 

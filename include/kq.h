@@ -378,7 +378,9 @@ kq_status kq_transform_quantize_mxfp4_packed(const uint16_t *A, int64_t m, int64
  *   codes_r   device, [r][d/2] (R in MXFP4, blocks along d), 16-byte aligned
  *   scales_r  device, [r][d/32]
  *   Z         device, fp32 [m][r], 16-byte aligned, written
- * d % 32 == 0, r > 0, r % 32 == 0 (KQ_ERR_SHAPE).
+ * d % 32 == 0, r > 0, r % 32 == 0 (KQ_ERR_SHAPE); 80 rows of X16 and 128 rows of
+ * R's codes must each span fewer than 2^31 bytes (KQ_ERR_UNSUPPORTED). The same
+ * Z, bit for bit, as kq_lowrank_project_bf16 on kq_dequantize_mxfp4_bf16 of R.
  */
 kq_status kq_lowrank_project(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint8_t *codes_r,
                              const uint8_t *scales_r, int64_t r, float *Z, kq_stream_t stream);
@@ -405,6 +407,19 @@ kq_status kq_lowrank_project_bf16(const uint16_t *X16, int64_t m, int64_t d, int
  */
 kq_status kq_lowrank_project_bf16_split(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint16_t *R16,
                                         int64_t r, uint16_t *Zh, uint16_t *Zl, kq_stream_t stream);
+
+/*
+ * kq_lowrank_project writing Z as its bf16 split (Zh = bf16(Z), Zl = bf16(Z - Zh),
+ * as kq_lowrank_project_bf16_split) from R in MXFP4: the operands of
+ * kq_mxfp4_gemm_packed_lowrank_split without a decoded copy of R (Sec. 3.4 Eq. 11).
+ *   X16, m, d, ldx, codes_r, scales_r, r   as kq_lowrank_project
+ *   Zh, Zl                                 device, bf16 bits [m][r] each (written), 16-byte aligned
+ * Errors as kq_lowrank_project; bit-identical to kq_lowrank_project_bf16_split on
+ * kq_dequantize_mxfp4_bf16 of R.
+ */
+kq_status kq_lowrank_project_split(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint8_t *codes_r,
+                                   const uint8_t *scales_r, int64_t r, uint16_t *Zh, uint16_t *Zl,
+                                   kq_stream_t stream);
 
 /*
  * MXFP4 -> bf16 (Sec. 3.1's dequantization deq(code, scale) = E2M1(code)

@@ -33,6 +33,7 @@ EXPORTS = (
     "kq_pack_mxfp4_scales",
     "kq_lowrank_project_bf16",
     "kq_lowrank_project_bf16_split",
+    "kq_lowrank_project_split",
     "kq_dequantize_mxfp4_bf16",
     "kq_mxfp4_gemm_packed",
     "kq_mxfp4_gemm_packed_bf16",
@@ -87,6 +88,7 @@ def lib():
             "kq_pack_mxfp4_scales": [p, i64, i64, p, p],
             "kq_lowrank_project_bf16": [p, i64, i64, i64, p, i64, p, p],
             "kq_lowrank_project_bf16_split": [p, i64, i64, i64, p, i64, p, p, p],
+            "kq_lowrank_project_split": [p, i64, i64, i64, p, p, i64, p, p, p],
             "kq_dequantize_mxfp4_bf16": [p, p, i64, i64, p, p],
             "kq_mxfp4_gemm_packed": [p, p, p, p, i64, i64, i64, p, i64, p],
             "kq_mxfp4_gemm_packed_bf16": [p, p, p, p, i64, i64, i64, p, i64, p],
@@ -304,6 +306,34 @@ def lowrank_project(X16, codes_r, scales_r, out=None, stream=None):
     _check("kq_lowrank_project",
            lib().kq_lowrank_project(_p(X16), m, d, ldx, _p(codes_r), _p(scales_r), r, _p(out), _stream_ptr(stream)))
     return out
+
+
+def lowrank_project_split(X16, codes_r, scales_r, Zh=None, Zl=None, stream=None):
+    """As lowrank_project (R in MXFP4), Z written as its bf16 split: Zh = bf16(Z),
+    Zl = bf16(Z - Zh) (bf16 [m][r] each). Returns Zh, Zl."""
+    torch = _torch()
+    _dev(X16, "X16", (torch.bfloat16, torch.int16, torch.uint16))
+    m, d, ldx = _rows(X16, "X16")
+    for t, nm in ((codes_r, "codes_r"), (scales_r, "scales_r")):
+        _dev(t, nm, (torch.uint8,))
+        if not t.is_contiguous():
+            raise ValueError(nm + " must be contiguous")
+    r = codes_r.shape[0]
+    if tuple(codes_r.shape) != (r, d // 2) or tuple(scales_r.shape) != (r, d // 32):
+        raise ValueError("R operand shapes do not match X16")
+    outs = []
+    for t, nm in ((Zh, "Zh"), (Zl, "Zl")):
+        if t is None:
+            t = torch.empty((m, r), dtype=torch.bfloat16, device=X16.device)
+        _dev(t, nm, (torch.bfloat16,))
+        if tuple(t.shape) != (m, r) or not t.is_contiguous():
+            raise ValueError(nm + " must be a contiguous bf16 [m][r] tensor")
+        outs.append(t)
+    Zh, Zl = outs
+    _check("kq_lowrank_project_split",
+           lib().kq_lowrank_project_split(_p(X16), m, d, ldx, _p(codes_r), _p(scales_r), r, _p(Zh), _p(Zl),
+                                          _stream_ptr(stream)))
+    return Zh, Zl
 
 
 def dequantize_mxfp4_bf16(codes, scales, out=None, stream=None):

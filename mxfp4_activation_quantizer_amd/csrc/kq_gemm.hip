@@ -41,126 +41,11 @@ struct ProjGeom {
     int64_t m, d, ldx, r, tiles_r;
 };
 
-constexpr int kProjRow = 128 * 2 + 16;  // bytes per staged R column: 128 bf16 + 16 of padding
-constexpr int kProjAhead = 3;            // steps of X in flight per wave
+constexpr int kProjAhead = 3;  // steps of X in flight per wave
 
-// The workgroup decodes each step's slice of MXFP4 R into LDS itself.
-__global__ __launch_bounds__(kThreads) void lowrank_project_kernel(const uint16_t *__restrict__ X, ProjGeom g,
-                                                                   const uint8_t *__restrict__ cr,
-                                                                   const uint8_t *__restrict__ sr,
-                                                                   float *__restrict__ Z) {
-    __shared__ __attribute__((aligned(16))) uint8_t rl[2][128 * kProjRow];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int64_t tm = blockIdx.x / g.tiles_r, tr = blockIdx.x % g.tiles_r;
-    const int64_t col0 = tr * 128;
-    const int grp = lane >> 4;
-    // this thread's share of an R slice: column dc, k half dh (64 k = 32 code bytes, 2 scales)
-    const int dc = t >> 1, dh = t & 1;
-    struct RRegs {
-        uint4 c[2];
-        uint32_t s[2];
-    };
-    // Loads go through per-tile buffer descriptors whose record counts end at the
-    // last valid row (rows past m or r read zero), with no branches around them,
-    // so the compiler's wait counts stay exact; a load past d gets an offset
-    // beyond the record count and reads zero too.
-    const int64_t rows_r = g.r - col0 < 128 ? g.r - col0 : 128;
-    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(cr + col0 * (g.d / 2)), (short)0, (int)(rows_r * (g.d / 2)), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(sr + col0 * (g.d / 32)), (short)0, (int)(rows_r * (g.d / 32)), 0x00020000);
-    auto fetch_r = [&](int64_t k0, RRegs &R) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int64_t k = k0 + 64 * dh + 32 * h;  // a 32-k group
-            // past d the offset is moved beyond every record count, so the load
-            // returns zero codes (and a zero scale byte, which only scales zeros)
-            const bool in = k < g.d;
-            const uint32_t co = in ? (uint32_t)(dc * (g.d / 2) + k / 2) : 0x80000000u;
-            const uint32_t so = in ? (uint32_t)(dc * (g.d / 32) + k / 32) : 0x80000000u;
-            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc, co, 0, 0);
-            R.c[h] = make_uint4(v[0], v[1], v[2], v[3]);
-            R.s[h] = __builtin_amdgcn_raw_buffer_load_b8(rs, so, 0, 0);
-        }
-    };
-    auto stash_r = [&](uint8_t *buf, const RRegs &R) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint8_t *dst = buf + dc * kProjRow + 128 * dh + 64 * h;
-            *reinterpret_cast<bf16x8_t *>(dst) = decode_fp4x8_bf16_cvt(R.c[h].x, R.s[h]);
-            *reinterpret_cast<bf16x8_t *>(dst + 16) = decode_fp4x8_bf16_cvt(R.c[h].y, R.s[h]);
-            *reinterpret_cast<bf16x8_t *>(dst + 32) = decode_fp4x8_bf16_cvt(R.c[h].z, R.s[h]);
-            *reinterpret_cast<bf16x8_t *>(dst + 48) = decode_fp4x8_bf16_cvt(R.c[h].w, R.s[h]);
-        }
-    };
-    const int64_t rows_x = g.m - tm * 64 < 64 ? g.m - tm * 64 : 64;
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(X + tm * 64 * g.ldx), (short)0, (int)(rows_x * g.ldx * 2), 0x00020000);
-    const uint32_t xoff = (uint32_t)(((wave * 16 + (lane & 15)) * g.ldx + 8 * grp) * 2);
-    auto fetch_x = [&](int64_t k0, uint4 q[4]) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t k = k0 + 32 * u + 8 * grp;
-            const uint32_t xo = k < g.d ? xoff + (uint32_t)((k0 + 32 * u) * 2) : 0x80000000u;
-            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 2);
-            q[u] = make_uint4(v[0], v[1], v[2], v[3]);
-        }
-    };
-    floatx4_t acc[8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) acc[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    // X is the only HBM stream and there is about one wave per SIMD, so each
-    // wave keeps kProjAhead steps of its X rows in flight (a register ring);
-    // the R slice (L2-resident) is fetched one step ahead into the other LDS buffer.
-    RRegs R;
-    uint4 xq[kProjAhead][4];
-    const int64_t steps = (g.d + 127) / 128;
-    fetch_r(0, R);
-#pragma unroll
-    for (int p = 0; p < kProjAhead; ++p) fetch_x((int64_t)p * 128, xq[p]);
-    stash_r(rl[0], R);
-    __syncthreads();
-    // the step count is rounded up to a multiple of kProjAhead: a step past d loads
-    // zeros (X and R), so its products add exact zeros, and the loop body has no
-    // branch for the compiler's wait counts to lose track across
-    const int64_t steps_up = (steps + kProjAhead - 1) / kProjAhead * kProjAhead;
-    for (int64_t st0 = 0; st0 < steps_up; st0 += kProjAhead) {
-#pragma unroll
-        for (int p = 0; p < kProjAhead; ++p) {
-            const int64_t st = st0 + p;
-            const int cur = (int)(st & 1);
-            fetch_r((st + 1) * 128, R);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const bf16x8_t xa = as_bf16x8(xq[p][u]);
-#pragma unroll
-                for (int b = 0; b < 8; ++b) {
-                    const bf16x8_t rb = *reinterpret_cast<const bf16x8_t *>(
-                        rl[cur] + (b * 16 + (lane & 15)) * kProjRow + 64 * u + 16 * grp);
-                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, rb, acc[b], 0, 0, 0);
-                }
-            }
-            // refill this slot with the step kProjAhead ahead (zeros past d)
-            fetch_x((st + kProjAhead) * 128, xq[p]);
-            stash_r(rl[cur ^ 1], R);
-            __syncthreads();
-        }
-    }
-    const int64_t orow0 = tm * 64 + wave * 16 + grp * 4;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const int64_t col = col0 + b * 16 + (lane & 15);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int64_t orow = orow0 + tt;
-            if (orow < g.m && col < g.r) Z[orow * g.r + col] = acc[b][tt];
-        }
-    }
-}
-
-// Z = X R16^T with R already in bf16 [r][d]: per output element the same
-// matrix instructions in the same k order as lowrank_project_kernel
-// (bit-identical Z), with the work split by wave. A workgroup covers 80 rows of
+// Z = X R16^T with R in bf16 [r][d] (or MXFP4, decoded by the producers; RMX
+// below): per output element the 16 x 16 x 32 bf16 matrix instruction over 32 k
+// at a time in ascending k, with the work split by wave. A workgroup covers 80 rows of
 // X (18432 rows make 231 workgroups, one round on 256 CUs; 64-row tiles left a
 // second round of 32): waves 0-4 own 16 rows each and stream them, kProjAhead
 // steps ahead in registers, so their memory waits are for their own X loads
@@ -202,10 +87,18 @@ __device__ __forceinline__ void proj_dma16(__amdgpu_buffer_rsrc_t d, uint32_t ld
 // SPLIT: Z leaves as its bf16 split, zh = bf16(z) and zl = bf16(z - zh) (both
 // rounded to nearest even by the hardware convert; z - zh is exact in fp32),
 // the operands the packed GEMM's low-rank term multiplies, in place of fp32 z.
-template <bool SPLIT>
+//
+// RMX: R arrives in MXFP4 (codes [r][d/2] at r16's place, scales [r][d/32] at
+// sr) and the producers decode it: producer lane c (0 .. 127, one column of the
+// tile) loads its column's 64 code bytes and 4 scale bytes of a step two steps
+// ahead into registers, and writes the step after the current one into its LDS
+// slot as bf16 (the same values as kq_dequantize_mxfp4_bf16, the same layout as
+// the bf16 loads), a quarter of the bf16 form's bytes from L2. Consumers as above:
+// bit-identical Z.
+template <bool SPLIT, bool RMX = false>
 __global__ __launch_bounds__(64 * (kProjWaves + kProjProducers)) void lowrank_project_r16_kernel(
     const uint16_t *__restrict__ X, ProjGeom g, const uint16_t *__restrict__ r16, float *__restrict__ Z,
-    uint16_t *__restrict__ Zh, uint16_t *__restrict__ Zl) {
+    uint16_t *__restrict__ Zh, uint16_t *__restrict__ Zl, const uint8_t *__restrict__ sr = nullptr) {
     __shared__ __attribute__((aligned(16))) uint8_t rl[kProjSlots][128 * 256];
     const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t tm = blockIdx.x / g.tiles_r, tr = blockIdx.x % g.tiles_r;
@@ -216,6 +109,67 @@ __global__ __launch_bounds__(64 * (kProjWaves + kProjProducers)) void lowrank_pr
     const uint32_t lds0 = (uint32_t)(uintptr_t)&rl[0][0];
     constexpr int kAhead = kProjSlots - 1;  // R steps in flight beyond the one being read
 
+    if (RMX && wave >= kProjWaves) {
+        const int c = 64 * (wave - kProjWaves) + lane;  // the lane's column of the tile
+        const int64_t rows_r = g.r - col0 < 128 ? g.r - col0 : 128;
+        const uint8_t *cr = reinterpret_cast<const uint8_t *>(r16);
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(cr + col0 * (g.d / 2)), (short)0, (int)(rows_r * (g.d / 2)), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(sr + col0 * (g.d / 32)), (short)0, (int)(rows_r * (g.d / 32)), 0x00020000);
+        struct RStep {
+            uint4 q[4];
+            uint32_t sc[4];
+        };
+        // step st's four 32-k groups of column c; a group past d reads zeros (offset
+        // beyond every record count), so it decodes to exact zeros
+        auto fetch = [&](int64_t st, RStep &R) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const int64_t k = st * 128 + 32 * h;
+                const bool in = k < g.d;
+                const uint32_t co = in ? (uint32_t)(c * (g.d / 2) + k / 2) : 0x80000000u;
+                const uint32_t so = in ? (uint32_t)(c * (g.d / 32) + k / 32) : 0x80000000u;
+                const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc, co, 0, 0);
+                R.q[h] = make_uint4(v[0], v[1], v[2], v[3]);
+                R.sc[h] = __builtin_amdgcn_raw_buffer_load_b8(rs, so, 0, 0);
+            }
+        };
+        // chunk q (8 values of k, 16 bytes) of column c at slot q ^ (c % 16)
+        auto stash = [&](int64_t st, const RStep &R) {
+            uint8_t *col = &rl[st % kProjSlots][0] + c * 256;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint32_t w4[4] = {R.q[h].x, R.q[h].y, R.q[h].z, R.q[h].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<bf16x8_t *>(col + 16 * ((4 * h + i) ^ (c & 15))) =
+                        decode_fp4x8_bf16_cvt(w4[i], R.sc[h]);
+            }
+        };
+        // step st + 1 is written during step st (its slot held step st - 2, read before
+        // the barrier that opened step st - 1), with its loads issued two steps earlier
+        RStep ring[2];
+        fetch(0, ring[0]);
+        if (1 < steps_up) fetch(1, ring[1]);
+        stash(0, ring[0]);
+        if (2 < steps_up) fetch(2, ring[0]);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        for (int64_t st0 = 0; st0 < steps_up; st0 += 2) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int64_t st = st0 + p;
+                if (st < steps_up) {
+                    if (st + 1 < steps_up) {
+                        stash(st + 1, ring[(p + 1) & 1]);
+                        if (st + 3 < steps_up) fetch(st + 3, ring[(p + 1) & 1]);
+                    }
+                    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                }
+            }
+        }
+        return;
+    }
     if (wave >= kProjWaves) {
         // producer pi: loads j = kProjLoads pi .. of each step; load j covers columns 4 j .. 4 j + 3
         const int pi = wave - kProjWaves;
@@ -576,13 +530,14 @@ kq_status gemm256_mx_lowrank(const uint8_t *codes_a, const uint8_t *scales_a, co
 
 namespace {
 
-template <bool SPLIT>
+// RMX: R16 holds R's MXFP4 codes [r][d/2] (16-byte aligned) and SR its scales [r][d/32].
+template <bool SPLIT, bool RMX = false>
 kq_status project_r16(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint16_t *R16, int64_t r, float *Z,
-                      uint16_t *Zh, uint16_t *Zl, kq_stream_t stream) {
+                      uint16_t *Zh, uint16_t *Zl, kq_stream_t stream, const uint8_t *SR = nullptr) {
     if (m < 0 || d < 0 || d % 32 != 0 || ldx < d || r <= 0 || r % 32 != 0) return KQ_ERR_SHAPE;
     if (!kqhost::sizes_fit({m, d, ldx, r})) return KQ_ERR_UNSUPPORTED;
     if (m == 0 || d == 0) return KQ_OK;
-    if (!X16 || !R16 || (SPLIT ? (!Zh || !Zl) : !Z)) return KQ_ERR_NULL;
+    if (!X16 || !R16 || (RMX && !SR) || (SPLIT ? (!Zh || !Zl) : !Z)) return KQ_ERR_NULL;
     if (!aligned(X16, 16) || ldx % 8 != 0 || !aligned(R16, 16) || (!SPLIT && !aligned(Z, 16)) ||
         (SPLIT && (!aligned(Zh, 16) || !aligned(Zl, 16))))
         return KQ_ERR_ALIGN;
@@ -591,9 +546,9 @@ kq_status project_r16(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, co
     if ((int64_t)kq::kProjRows * ldx * 2 >= ((int64_t)1 << 31) || (int64_t)128 * d * 2 >= ((int64_t)1 << 31))
         return KQ_ERR_UNSUPPORTED;
     kq::ProjGeom g{m, d, ldx, r, tiles_r};
-    hipLaunchKernelGGL(kq::lowrank_project_r16_kernel<SPLIT>, dim3((unsigned)(tiles_m * tiles_r)),
+    hipLaunchKernelGGL((kq::lowrank_project_r16_kernel<SPLIT, RMX>), dim3((unsigned)(tiles_m * tiles_r)),
                        dim3(64 * (kq::kProjWaves + kq::kProjProducers)), 0, (hipStream_t)stream, X16, g, R16, Z, Zh,
-                       Zl);
+                       Zl, SR);
     return launched();
 }
 
@@ -658,15 +613,8 @@ kq_status kq_lowrank_project(const uint16_t *X16, int64_t m, int64_t d, int64_t 
     if (m == 0 || d == 0) return KQ_OK;
     if (!X16 || !codes_r || !scales_r || !Z) return KQ_ERR_NULL;
     if (!aligned(X16, 16) || ldx % 8 != 0 || !aligned(codes_r, 16) || !aligned(Z, 16)) return KQ_ERR_ALIGN;
-    const int64_t tiles_m = (m + 63) / 64, tiles_r = (r + 127) / 128;
-    if (tiles_m * tiles_r > 0x7FFFFFFF || m > INT64_MAX / 4 / (ldx > r ? ldx : r)) return KQ_ERR_SHAPE;
-    // per-tile buffer records are 32-bit: 64 rows of X, 128 rows of R's codes
-    if ((int64_t)64 * ldx * 2 >= ((int64_t)1 << 31) || (int64_t)128 * (d / 2) + 128 >= ((int64_t)1 << 31))
-        return KQ_ERR_UNSUPPORTED;
-    kq::ProjGeom g{m, d, ldx, r, tiles_r};
-    hipLaunchKernelGGL(kq::lowrank_project_kernel, dim3((unsigned)(tiles_m * tiles_r)), dim3(kq::kThreads),
-                       0, (hipStream_t)stream, X16, g, codes_r, scales_r, Z);
-    return launched();
+    return project_r16<false, true>(X16, m, d, ldx, reinterpret_cast<const uint16_t *>(codes_r), r, Z, nullptr,
+                                    nullptr, stream, scales_r);
 }
 
 kq_status kq_lowrank_project_bf16(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint16_t *R16,
@@ -677,6 +625,13 @@ kq_status kq_lowrank_project_bf16(const uint16_t *X16, int64_t m, int64_t d, int
 kq_status kq_lowrank_project_bf16_split(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint16_t *R16,
                                         int64_t r, uint16_t *Zh, uint16_t *Zl, kq_stream_t stream) {
     return project_r16<true>(X16, m, d, ldx, R16, r, nullptr, Zh, Zl, stream);
+}
+
+kq_status kq_lowrank_project_split(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, const uint8_t *codes_r,
+                                   const uint8_t *scales_r, int64_t r, uint16_t *Zh, uint16_t *Zl,
+                                   kq_stream_t stream) {
+    return project_r16<true, true>(X16, m, d, ldx, reinterpret_cast<const uint16_t *>(codes_r), r, nullptr, Zh, Zl,
+                                   stream, scales_r);
 }
 
 kq_status kq_dequantize_mxfp4_bf16(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t k,

@@ -121,6 +121,10 @@ GOOD = P(0x10000)  # never dereferenced: every case below fails before a launch
     ("kq_lowrank_project_bf16_split", (GOOD, 4, 64, 64, GOOD, 32, GOOD, None, None), kq.KQ_ERR_NULL),
     ("kq_lowrank_project_bf16_split", (GOOD, 4, 64, 64, GOOD, 32, P(0x10008), GOOD, None), kq.KQ_ERR_ALIGN),
     ("kq_lowrank_project_bf16_split", (None, 0, 64, 64, None, 32, None, None, None), kq.KQ_OK),
+    ("kq_lowrank_project_split", (GOOD, 4, 64, 64, GOOD, GOOD, 48, GOOD, GOOD, None), kq.KQ_ERR_SHAPE),
+    ("kq_lowrank_project_split", (GOOD, 4, 64, 64, GOOD, None, 32, GOOD, GOOD, None), kq.KQ_ERR_NULL),
+    ("kq_lowrank_project_split", (GOOD, 4, 64, 64, P(0x10008), GOOD, 32, GOOD, GOOD, None), kq.KQ_ERR_ALIGN),
+    ("kq_lowrank_project_split", (None, 0, 64, 64, None, None, 32, None, None, None), kq.KQ_OK),
     ("kq_mxfp4_gemm_packed_bf16", (GOOD, GOOD, GOOD, GOOD, 4, 4, 128, GOOD, 4, None), kq.KQ_ERR_SHAPE),
     ("kq_mxfp4_gemm_packed_bf16", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, GOOD, 3, None), kq.KQ_ERR_SHAPE),
     ("kq_mxfp4_gemm_packed_bf16", (GOOD, GOOD, GOOD, GOOD, 4, 4, 256, None, 4, None), kq.KQ_ERR_NULL),

@@ -145,6 +145,34 @@ def test_lowrank_project_bf16_split_is_split_of_z(torch_dev, kq, orc, m, d, r):
     assert torch.equal(Zl.view(torch.int16), el.view(torch.int16))
 
 
+@pytest.mark.parametrize("m,d,r,edge", [(100, 96, 32, False), (300, 3072, 128, False), (81, 1152, 256, False),
+                                        (333, 160, 64, True), (18432, 3072, 128, False)])
+def test_lowrank_project_mx_r_is_decoded_r(torch_dev, kq, orc, m, d, r, edge):
+    """R in MXFP4, decoded by the projection's producer waves (hardware convert, the
+    arithmetic decode for scale bytes outside 2..252): Z and its bf16 split bit for bit
+    those of the bf16-R projection on kq_dequantize_mxfp4_bf16 of R. d = 96 and 160
+    end inside a 128-k step; `edge` puts scale bytes 0, 1, 253 and 254 in R."""
+    torch = torch_dev
+    case("project mx R %dx%d r=%d edge=%s" % (m, d, r, edge))
+    X = synth.random_bf16_matrix(m, d, seed=d + r + 31, scale=0.25 if edge else 1.0)
+    R = np.random.default_rng(r + d + 31).standard_normal((r, d)) / np.sqrt(d)
+    cr, sr = quantize_host(orc, R)
+    if edge:
+        sr = sr.copy()
+        sr[0, 0], sr[1, -1], sr[r - 1, 1], sr[r // 2, 2] = 0, 1, 253, 254
+    dX = dev_bf16(torch, X)
+    dcr, dsr = torch.from_numpy(cr).cuda(), torch.from_numpy(sr).cuda()
+    r16 = kq.dequantize_mxfp4_bf16(dcr, dsr)
+    Z = kq.lowrank_project(dX, dcr, dsr)
+    Zr = kq.lowrank_project_bf16(dX, r16)
+    Zh, Zl = kq.lowrank_project_split(dX, dcr, dsr)
+    Zhr, Zlr = kq.lowrank_project_bf16_split(dX, r16)
+    torch.cuda.synchronize()
+    assert torch.equal(Z.view(torch.int32), Zr.view(torch.int32))
+    assert torch.equal(Zh.view(torch.int16), Zhr.view(torch.int16))
+    assert torch.equal(Zl.view(torch.int16), Zlr.view(torch.int16))
+
+
 def test_lowrank_project_bf16_strided_x(torch_dev, kq, orc):
     """X16 a row-strided view (ldx = d + 64) over several 80-row tiles and a ragged last
     one: the same Z, bit for bit, as the in-workgroup decode path on the same view, and the
