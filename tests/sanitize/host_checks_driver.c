@@ -101,6 +101,11 @@ int main(void) {
            KQ_ERR_UNSUPPORTED);
     expect("project split huge", kq_lowrank_project_bf16_split(GOOD, BIG, 64, 64, GOOD, 32, P(0x10000), P(0x10000), NULL),
            KQ_ERR_UNSUPPORTED);
+    expect("project mx split huge", kq_lowrank_project_split(GOOD, BIG, 64, 64, GOOD, GOOD, 32, P(0x10000), P(0x10000),
+                                                             NULL),
+           KQ_ERR_UNSUPPORTED);
+    expect("project mx split r", kq_lowrank_project_split(GOOD, 4, 64, 64, GOOD, GOOD, 40, P(0x10000), P(0x10000), NULL),
+           KQ_ERR_SHAPE);
     expect("y16 huge", kq_transform_quantize_mxfp4_y16(GOOD, BIG, 64, 64, GOOD, P(0x10000), P(0x10000), P(0x10000),
                                                        NULL), KQ_ERR_SHAPE);
     expect("smooth huge", kq_smoothquant_quantize_mxfp4(GOOD, 4, BIG / 64 * 32, BIG, GOOD, P(0x10000), P(0x10000),
