@@ -227,6 +227,47 @@ def test_fused_layer_flux_config4(torch_dev, kq, orc):
     assert w_diff <= 1e-5 * cw_h.size
 
 
+@pytest.mark.parametrize("m,k,n,pad,kind", [(6000, 512, 3000, 0, "lu"), (300, 768, 520, 16, "swap"),
+                                             (5, 256, 257, 0, "identity"), (1000, 1024, 700, 8, "lu")])
+def test_fused_layer_against_mx_gemm(torch_dev, kq, orc, m, k, n, pad, kind):
+    """The fused layer against the quantizer followed by kq_mxfp4_gemm (the 256 x 256-tile
+    kernel on these k): with every block in shear form ("lu") or exact factors
+    ("identity") bit for bit (the same codes, the same instructions in the same k order);
+    with swap blocks (no shear form) within 1e-3 of the oracle's pipeline. Row-strided A
+    (lda = k + pad), ragged m and n, several workgroup rounds (6000 x 3000)."""
+    torch = torch_dev
+    case("fused layer vs mx gemm m=%d k=%d n=%d pad=%d %s" % (m, k, n, pad, kind))
+    A_full = synth.random_bf16_matrix(m, k + pad, seed=m + k + n, scale=2.0)
+    if kind == "identity":
+        fac = synth.special_factors(k // 32, "identity")
+    else:
+        fac = synth.lu_perturbed_factors(k // 32, seed=k + 11)
+        if kind == "swap":
+            for blk in (1, 9, 19):
+                fac[blk, 1] = np.array([[0.0, 1.0], [1.0, 0.0]], np.float32)
+    W = synth.weights(n, k, 2004 + n)
+    cw, sw = weights_mxfp4(torch, kq, W, fac if kind != "identity" else synth.special_factors(k // 32, "identity"))
+    A = dev_bf16(torch, A_full)[:, :k]
+    fac_d = dev(torch, fac)
+    O_fused = kq.transform_quantize_mxfp4_gemm(A, fac_d, cw, sw)
+    if kind == "identity":
+        ca, sa = kq.quantize_mxfp4(A)
+    else:
+        ca, sa = kq.transform_quantize_mxfp4(A, fac_d)
+    O_pipe = kq.mxfp4_gemm(ca, sa, cw, sw)
+    torch.cuda.synchronize()
+    if kind != "swap":
+        assert torch.equal(O_fused, O_pipe)
+    else:
+        ca_r, sa_r, _ = orc.transform_quantize(np.ascontiguousarray(A_full[:, :k]), fac, want_y=False)
+        cw_r, sw_r = orc.quantize_f64(orc.inverse_fold(W, fac))
+        O_r = orc.gemm_dequant(ca_r, sa_r, cw_r, sw_r, k)
+        got = O_fused.cpu().numpy().astype(np.float64)
+        rel = np.linalg.norm(got - O_r) / np.linalg.norm(O_r)
+        print("[w4a4-fused] swap blocks: rel vs oracle pipeline %.3g" % rel, flush=True)
+        assert rel <= 1e-3, rel
+
+
 def test_fused_layer_empty_and_k0(torch_dev, kq):
     torch = torch_dev
     case("fused layer empty")
