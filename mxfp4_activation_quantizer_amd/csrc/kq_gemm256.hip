@@ -23,7 +23,11 @@
 //    scales for 256 rows are one 2 KB run instead of 256 scattered lines, and
 //    they are ordered even blocks first, so the scale a lane needs at step j
 //    is byte j of the dword of its block parity: the instruction's byte select
-//    picks it, with no per-lane shift;
+//    picks it, with no per-lane shift. The same kernel also reads the MX layout
+//    [rows][k/32] as the quantizer writes it (NS): four 4-byte-per-lane loads per
+//    wave and stage gather the rows' eight bytes, and one byte permute builds
+//    the parity dword (about 15% slower at 18432 x 3072 x 3072: the scattered
+//    scale lines);
 //  - tiles are numbered so that each XCD (workgroups are dealt to the eight XCDs
 //    round robin) gets a contiguous run, walked in bands of 4 row tiles, which
 //    keeps the operand rows a run shares in that XCD's L2; one launch covers
