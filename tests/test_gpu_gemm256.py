@@ -253,6 +253,36 @@ def test_mx_layout_gemm_lowrank_is_packed(torch_dev, kq, m, n, k, r):
     assert torch.equal(O, ref)
 
 
+def test_mx_layout_gemm_scales_4_byte_aligned(torch_dev, kq, orc):
+    """MX-layout scales whose base is 4-byte but not 16-byte aligned (a view 4 bytes into
+    a buffer): the 256 x 256-tile kernel still takes them (its scale loads are 4 bytes
+    per lane) and matches the packed-scale product bit for bit; 2-byte-aligned scales
+    go to the 128 x 128 kernel, which agrees with the oracle-checked product to fp32
+    accumulation accuracy."""
+    torch = torch_dev
+    m, n, k = 700, 600, 512
+    case("mx-layout gemm misaligned scales %dx%dx%d" % (m, n, k))
+    rng = np.random.default_rng(77)
+    ca, sa, cw, sw = operands(rng, m, n, k)
+    dca, dcw = dev(torch, ca), dev(torch, cw)
+    ref = kq.mxfp4_gemm_packed(dca, kq.pack_mxfp4_scales(dev(torch, sa)), dcw, kq.pack_mxfp4_scales(dev(torch, sw)))
+    for off in (4, 2):
+        ba = torch.zeros(sa.size + 16, dtype=torch.uint8, device="cuda")
+        bw = torch.zeros(sw.size + 16, dtype=torch.uint8, device="cuda")
+        va = ba[off:off + sa.size].view(sa.shape)
+        vw = bw[off:off + sw.size].view(sw.shape)
+        va.copy_(torch.from_numpy(sa).cuda())
+        vw.copy_(torch.from_numpy(sw).cuda())
+        assert va.data_ptr() % 16 == off and vw.data_ptr() % 16 == off
+        O = kq.mxfp4_gemm(dca, va, dcw, vw)
+        torch.cuda.synchronize()
+        if off == 4:
+            assert torch.equal(O, ref)
+        else:
+            got, want = O.cpu().numpy().astype(np.float64), ref.cpu().numpy().astype(np.float64)
+            assert np.all(np.abs(got - want) <= 2 * bound(orc, ca, sa, cw, sw, k))
+
+
 def split_bf16(torch, Z):
     """Zh = bf16(Z), Zl = bf16(Z - Zh), both rounded to nearest even (torch's fp32 -> bf16)."""
     Zh = Z.to(torch.bfloat16)
