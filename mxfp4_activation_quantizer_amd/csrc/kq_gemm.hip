@@ -543,7 +543,9 @@ kq_status project_r16(const uint16_t *X16, int64_t m, int64_t d, int64_t ldx, co
         return KQ_ERR_ALIGN;
     const int64_t tiles_m = (m + kq::kProjRows - 1) / kq::kProjRows, tiles_r = (r + 127) / 128;
     if (tiles_m * tiles_r > 0x7FFFFFFF || m > INT64_MAX / 4 / (ldx > r ? ldx : r)) return KQ_ERR_SHAPE;
-    if ((int64_t)kq::kProjRows * ldx * 2 >= ((int64_t)1 << 31) || (int64_t)128 * d * 2 >= ((int64_t)1 << 31))
+    // 32-bit buffer records: 80 rows of X, 128 rows of R (bf16, or MXFP4 codes)
+    if ((int64_t)kq::kProjRows * ldx * 2 >= ((int64_t)1 << 31) ||
+        (int64_t)128 * (RMX ? d / 2 : d * 2) >= ((int64_t)1 << 31))
         return KQ_ERR_UNSUPPORTED;
     kq::ProjGeom g{m, d, ldx, r, tiles_r};
     hipLaunchKernelGGL((kq::lowrank_project_r16_kernel<SPLIT, RMX>), dim3((unsigned)(tiles_m * tiles_r)),
