@@ -283,6 +283,63 @@ def test_mx_layout_gemm_scales_4_byte_aligned(torch_dev, kq, orc):
             assert np.all(np.abs(got - want) <= 2 * bound(orc, ca, sa, cw, sw, k))
 
 
+def test_w4a4_layers_graph_replays_match_eager(torch_dev, kq):
+    """The W4A4 layer's launch sequences inside a captured HIP graph: the plain layer
+    (quantizer writing the packed scales, packed GEMM) and the Eq. 11 layer (quantizer
+    with the bf16 activation, projection from MXFP4 R writing Z's split, GEMM with the
+    low-rank term). Every replay, with eager work and synchronizations in between,
+    writes the eager output bit for bit."""
+    import synth
+    torch = torch_dev
+    m, k, n, r = 600, 512, 520, 64
+    case("w4a4 layer graph replay %dx%dx%d r=%d" % (m, k, n, r))
+    rng = np.random.default_rng(41)
+    A = torch.from_numpy(synth.random_bf16_matrix(m, k, seed=42, scale=2.0).view(np.int16)).cuda().view(
+        torch.bfloat16)
+    fac = dev(torch, synth.lu_perturbed_factors(k // 32, seed=43))
+    _, _, cw, sw = operands(rng, 1, n, k)
+    dcw, psw = dev(torch, cw), kq.pack_mxfp4_scales(dev(torch, sw))
+    cr = dev(torch, rng.integers(0, 256, (r, k // 2), dtype=np.uint8))
+    sr = dev(torch, rng.integers(118, 128, (r, k // 32), dtype=np.uint8))
+    L16 = kq.dequantize_mxfp4_bf16(dev(torch, rng.integers(0, 256, (n, r // 2), dtype=np.uint8)),
+                                   dev(torch, rng.integers(118, 128, (n, r // 32), dtype=np.uint8)))
+    ca = torch.empty((m, k // 2), dtype=torch.uint8, device="cuda")
+    psa = torch.empty((m * (k // 32),), dtype=torch.uint8, device="cuda")
+    y16 = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+    Zh = torch.empty((m, r), dtype=torch.bfloat16, device="cuda")
+    Zl = torch.empty_like(Zh)
+    O1 = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    O2 = torch.empty_like(O1)
+
+    def layers():
+        kq.transform_quantize_mxfp4_packed(A, fac, codes=ca, packed_scales=psa)
+        kq.mxfp4_gemm_packed(ca, psa, dcw, psw, out=O1)
+        kq.transform_quantize_mxfp4_packed(A, fac, codes=ca, packed_scales=psa, y16=y16)
+        kq.lowrank_project_split(y16, cr, sr, Zh=Zh, Zl=Zl)
+        kq.mxfp4_gemm_packed_lowrank_split(ca, psa, dcw, psw, Zh, Zl, L16, out=O2)
+
+    layers()
+    torch.cuda.synchronize()
+    ref1, ref2 = O1.clone(), O2.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layers()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layers()
+    for rep in range(3):
+        for t in (O1, O2, Zh, Zl, ca, psa):
+            t.zero_()
+        other = kq.mxfp4_gemm_packed(ca, psa, dcw, psw)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(O1, ref1) and torch.equal(O2, ref2), "replay %d" % rep
+        assert other.shape == ref1.shape
+
+
 def split_bf16(torch, Z):
     """Zh = bf16(Z), Zl = bf16(Z - Zh), both rounded to nearest even (torch's fp32 -> bf16)."""
     Zh = Z.to(torch.bfloat16)
