@@ -340,6 +340,35 @@ def test_w4a4_layers_graph_replays_match_eager(torch_dev, kq):
         assert other.shape == ref1.shape
 
 
+def test_packed_gemm_extreme_scale_bytes(torch_dev, kq, orc):
+    """E8M0 scale bytes at the ends of the range the quantizer writes: on even k blocks
+    A's bytes 0, 1, 2 (block scales 2^-127 .. 2^-125) against W's 180, 220, 254 (2^53 ..
+    2^127), so the scale products span 2^-74 .. 2^2; on odd blocks both near 2^0. The
+    packed-scale kernel and the MX-layout path agree bit for bit, and both match the fp64
+    product of the dequantized operands to fp32 accumulation accuracy."""
+    torch = torch_dev
+    m, n, k = 300, 260, 512
+    case("packed gemm extreme scale bytes %dx%dx%d" % (m, n, k))
+    rng = np.random.default_rng(99)
+    ca = rng.integers(0, 256, (m, k // 2), dtype=np.uint8)
+    cw = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    sa = np.empty((m, k // 32), np.uint8)
+    sw = np.empty((n, k // 32), np.uint8)
+    sa[:, 0::2] = rng.choice(np.array([0, 1, 2], np.uint8), size=(m, k // 64))
+    sw[:, 0::2] = rng.choice(np.array([180, 220, 254], np.uint8), size=(n, k // 64))
+    sa[:, 1::2] = rng.choice(np.array([126, 127, 128], np.uint8), size=(m, k // 64))
+    sw[:, 1::2] = rng.choice(np.array([127, 130], np.uint8), size=(n, k // 64))
+    dca, dsa, dcw, dsw = (dev(torch, x) for x in (ca, sa, cw, sw))
+    O = kq.mxfp4_gemm_packed(dca, kq.pack_mxfp4_scales(dsa), dcw, kq.pack_mxfp4_scales(dsw))
+    O_mx = kq.mxfp4_gemm(dca, dsa, dcw, dsw)
+    torch.cuda.synchronize()
+    assert torch.equal(O.view(torch.int32), O_mx.view(torch.int32))
+    got = O.cpu().numpy().astype(np.float64)
+    ref = orc.gemm_dequant(ca, sa, cw, sw, k)
+    assert np.isfinite(got).all()
+    assert np.all(np.abs(got - ref) <= bound(orc, ca, sa, cw, sw, k))
+
+
 def split_bf16(torch, Z):
     """Zh = bf16(Z), Zl = bf16(Z - Zh), both rounded to nearest even (torch's fp32 -> bf16)."""
     Zh = Z.to(torch.bfloat16)
