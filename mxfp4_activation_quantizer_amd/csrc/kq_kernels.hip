@@ -465,10 +465,15 @@ struct LGeom {
 };
 
 template <bool DEBUG>
-__global__ __launch_bounds__(kThreads) void kron_mfma_lds_kernel(
+__global__ __launch_bounds__(kThreads, 3) void kron_mfma_lds_kernel(
     const uint16_t *__restrict__ A, LGeom g, const float *__restrict__ factors,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ ydbg) {
     __shared__ uint4 xs[2][16][65];
+    // codes and scale bytes of a tile, row-major (16 tokens x 16 blocks; a code row is padded to
+    // 68 dwords, so the 64 lanes of one write land in 64 different banks), written to HBM after
+    // the next barrier as whole 256-byte code rows and 16-byte scale rows
+    __shared__ __attribute__((aligned(16))) uint32_t cs[2][16][68];
+    __shared__ uint8_t ss[2][16][16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
     const int strip = (int)(blockIdx.x % (unsigned)g.nstrip);
     const int64_t tile0 = (int64_t)(blockIdx.x / (unsigned)g.nstrip) * g.iters;
@@ -493,17 +498,33 @@ __global__ __launch_bounds__(kThreads) void kron_mfma_lds_kernel(
         for (int r = 0; r < 4; ++r) xs[buf][4 * r + (tid >> 6)][tid & 63] = v[r];
     };
 
+    // tile t from buffer b to HBM: thread tid moves 16 code bytes of token 16 t + tid / 16
+    // (columns 16 (tid % 16) ..) and that token's scale byte of block tid % 16 of the strip
+    auto flush = [&](int64_t t, int b) {
+        const int r = tid >> 4, c = tid & 15;
+        const int64_t tok = t * 16 + r;
+        if (tok < g.m) {
+            *reinterpret_cast<uint4 *>(codes + tok * (g.d / 2) + (int64_t)strip * 256 + 16 * c) =
+                *reinterpret_cast<const uint4 *>(&cs[b][r][4 * c]);
+            scales[tok * g.nblk + strip * 16 + c] = ss[b][r][c];
+        }
+    };
+
     uint4 v[4];
     if (tile0 * 16 >= g.m) return;  // uniform within the workgroup
     load_tile(tile0, v);
     store_tile(0, v);
     __syncthreads();
-    for (int it = 0; it < g.iters; ++it) {
+    int it = 0;
+    for (; it < g.iters; ++it) {
         const int64_t t = tile0 + it;
         if (t * 16 >= g.m) break;  // uniform within the workgroup
         const bool more = it + 1 < g.iters && (t + 1) * 16 < g.m;
         if (more) load_tile(t + 1, v);
         const int buf = it & 1;
+        // the previous tile's codes, written before the last barrier; buffer buf ^ 1 is written
+        // again only after the next barrier
+        if (it > 0) flush(t - 1, buf ^ 1);
         const int64_t tok = t * 16 + (lane & 15);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -514,19 +535,19 @@ __global__ __launch_bounds__(kThreads) void kron_mfma_lds_kernel(
             const float amax = max_xor16_xor32(absmax8(y));
             const uint32_t sbyte = e8m0_byte(amax);
             const uint32_t packed = cvt8_f32(y, cvt_scale(sbyte));
-            if (tok < g.m) {
-                if (DEBUG) {
-                    float4 *o = reinterpret_cast<float4 *>(ydbg + tok * g.d + (int64_t)jb * 32 + grp * 8);
-                    o[0] = make_float4(y[0], y[1], y[2], y[3]);
-                    o[1] = make_float4(y[4], y[5], y[6], y[7]);
-                }
-                *reinterpret_cast<uint32_t *>(codes + tok * (g.d / 2) + (int64_t)jb * 16 + grp * 4) = packed;
-                if (grp == 0) scales[tok * g.nblk + jb] = (uint8_t)sbyte;
+            if (DEBUG && tok < g.m) {
+                float4 *o = reinterpret_cast<float4 *>(ydbg + tok * g.d + (int64_t)jb * 32 + grp * 8);
+                o[0] = make_float4(y[0], y[1], y[2], y[3]);
+                o[1] = make_float4(y[4], y[5], y[6], y[7]);
             }
+            cs[buf][lane & 15][(wave * 4 + q) * 4 + grp] = packed;
+            if (grp == 0) ss[buf][lane & 15][wave * 4 + q] = (uint8_t)sbyte;
         }
         if (more) store_tile(buf ^ 1, v);
         __syncthreads();
     }
+    // it >= 1 here: tile tile0 exists (checked above) and the loop ran it
+    flush(tile0 + it - 1, (it - 1) & 1);
 }
 
 // fp32 input, quad layout: quantize (MODE kQuantOnly) or, with MODE kKron,
@@ -721,7 +742,7 @@ kq_status launch_mfma_lds(const uint16_t *A, int64_t m, int64_t d, int64_t lda, 
                           uint8_t *codes, uint8_t *scales, float *ydbg, kq_stream_t stream) {
     kq::LGeom g;
     unsigned nwg;
-    if (!make_lgeom(m, d, lda, 8, g, nwg)) return KQ_ERR_SHAPE;
+    if (!make_lgeom(m, d, lda, 6, g, nwg)) return KQ_ERR_SHAPE;
     hipLaunchKernelGGL((kq::kron_mfma_lds_kernel<DEBUG>), dim3(nwg), dim3(kq::kThreads), 0,
                        (hipStream_t)stream, A, g, factors, codes, scales, ydbg);
     return launched();
