@@ -31,11 +31,7 @@
 //  - tiles are numbered so that each XCD (workgroups are dealt to the eight XCDs
 //    round robin) gets a contiguous run, walked in bands of 4 row tiles, which
 //    keeps the operand rows a run shares in that XCD's L2; one launch covers
-//    whole tiles and half tiles in the order of kq_tileorder.hpp; the plain
-//    fp32-output product launches two workgroups per CU over the whole order,
-//    each looping over every (2 x CUs)-th item, so that a tile's output stores
-//    drain under the next tile's first loads (5-7% at 18432 x 3072 x 3072 and
-//    8192 x 4608 x 4608, bit-identical);
+//    whole tiles and half tiles in the order of kq_tileorder.hpp;
 //  - the output leaves through LDS: each store instruction writes 4 whole rows
 //    of 256 bytes (8 full cache lines) rather than 32 rows x 32 bytes, which
 //    the store path serves several times faster (the fp32 epilogue of a tile,
@@ -653,11 +649,8 @@ __device__ __forceinline__ void gemm256_tile(const uint8_t *__restrict__ ca, con
     }
 }
 
-// One workgroup per tile (or half tile) in the launch's work order; with PERSIST,
-// workgroup b takes items b, b + gridDim.x, ... of that order (gridDim.x a multiple
-// of 8, so every item stays on the XCD the order deals it to), and the output
-// stores of one item drain while the next item's first stages load.
-template <bool LR, bool B16, bool LRS = false, bool NS = false, bool PERSIST = false>
+// One workgroup per tile (or half tile) in the launch's work order.
+template <bool LR, bool B16, bool LRS = false, bool NS = false>
 __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__restrict__ ca,
                                                            const uint8_t *__restrict__ psa,
                                                            const uint8_t *__restrict__ cw,
@@ -667,21 +660,9 @@ __global__ __launch_bounds__(kThreads) void gemm256_kernel(const uint8_t *__rest
                                                            const void *__restrict__ lr2,
                                                            void *__restrict__ O) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Lay<256>::kStage + 1024];
-    auto run = [&](int i) {
-        const TileWork wk = tile_work(i, g.order);
-        if (wk.half < 0) gemm256_tile<LR, 256, B16, LRS, NS>(ca, psa, cw, psw, g, lr0, lr1, lr2, O, wk.tile, 0, smem);
-        else gemm256_tile<LR, 128, B16, LRS, NS>(ca, psa, cw, psw, g, lr0, lr1, lr2, O, wk.tile, wk.half, smem);
-    };
-    if constexpr (PERSIST) {
-        const int items = tile_order_groups(g.order);
-        for (int i = (int)blockIdx.x; i < items; i += (int)gridDim.x) {
-            // every wave has read its staged output rows before the next item's loads land in LDS
-            if (i != (int)blockIdx.x) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            run(i);
-        }
-    } else {
-        run((int)blockIdx.x);
-    }
+    const TileWork wk = tile_work((int)blockIdx.x, g.order);
+    if (wk.half < 0) gemm256_tile<LR, 256, B16, LRS, NS>(ca, psa, cw, psw, g, lr0, lr1, lr2, O, wk.tile, 0, smem);
+    else gemm256_tile<LR, 128, B16, LRS, NS>(ca, psa, cw, psw, g, lr0, lr1, lr2, O, wk.tile, wk.half, smem);
 }
 
 // Compute units of the current device (cached per device; 256 on MI355X).
@@ -778,24 +759,11 @@ kq_status gemm_packed(const uint8_t *codes_a, const uint8_t *packed_scales_a, co
     g.nwg = (int)(tiles_m * tiles_n);
     g.rows16 = aligned(O, 16) && (ldo * esz) % 16 == 0;
     g.r = 0;
-    const int ncu = kq::g256::cu_count();
-    g.order = kq::g256::make_tile_order(g.nwg, ncu);
-    const int items = kq::g256::tile_order_groups(g.order);
-    if constexpr (B16) {
-        // (the loop of the persistent form pushes the bf16 epilogue past 256 registers)
-        hipLaunchKernelGGL((kq::g256::gemm256_kernel<false, B16, false, NS>), dim3((unsigned)items),
-                           dim3(kq::g256::kThreads), 0, (hipStream_t)stream, codes_a, packed_scales_a, codes_w,
-                           packed_scales_w, g, nullptr, nullptr, nullptr, O);
-    } else {
-        // two workgroups per CU in flight over the launch (one resident at a time: 137 KB of LDS
-        // each), each running every (2 * CUs)-th item of the work order; a multiple of 8 for any
-        // CU count, since the work order's XCD runs assume it
-        const int cap = ((2 * ncu + 7) / 8) * 8;
-        hipLaunchKernelGGL((kq::g256::gemm256_kernel<false, B16, false, NS, true>),
-                           dim3((unsigned)(items < cap ? items : cap)), dim3(kq::g256::kThreads), 0,
-                           (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, nullptr,
-                           nullptr, nullptr, O);
-    }
+    g.order = kq::g256::make_tile_order(g.nwg, kq::g256::cu_count());
+    hipLaunchKernelGGL((kq::g256::gemm256_kernel<false, B16, false, NS>),
+                       dim3((unsigned)kq::g256::tile_order_groups(g.order)), dim3(kq::g256::kThreads), 0,
+                       (hipStream_t)stream, codes_a, packed_scales_a, codes_w, packed_scales_w, g, nullptr, nullptr,
+                       nullptr, O);
     return launched();
 }
 

@@ -120,16 +120,15 @@ def test_packed_gemm_exact_sums_bit_identical(torch_dev, kq, orc, m, n, k, seed)
 
 
 @pytest.mark.parametrize("m,n,k,seed", [(12000, 6000, 512, 41), (9000, 5000, 256, 42)])
-def test_packed_gemm_persistent_items_exact(torch_dev, kq, orc, m, n, k, seed):
-    """More work items than the fp32-output launch's 2 x 256 workgroups, so workgroups run
-    two or three tiles in turn through the same LDS: 12000 x 6000 is 1128 tiles (104 of
-    them as halves, the staggered order, 1232 items), 9000 x 5000 is 720 tiles in the plain
-    order with ragged rows and columns. Scales in 2^-1 .. 2^1 make every fp32 partial sum
-    exact (k <= 3072): two rows of every 256-row band (so every tile) equal the oracle's
-    fp64 sums rounded to fp32, every element rounds to what the bf16-output kernel (one
-    tile per workgroup) writes, and the MX-layout product is the same bit for bit."""
+def test_packed_gemm_multi_round_exact(torch_dev, kq, orc, m, n, k, seed):
+    """Launches of several rounds of workgroups on 256 CUs: 12000 x 6000 is 1128 tiles (104
+    of them as halves, the staggered order, 1232 workgroups), 9000 x 5000 is 720 tiles in
+    the plain order with ragged rows and columns. Scales in 2^-1 .. 2^1 make every fp32
+    partial sum exact (k <= 3072): two rows of every 256-row band (so every tile) equal the
+    oracle's fp64 sums rounded to fp32, every element rounds to what the bf16-output kernel
+    writes, and the MX-layout product is the same bit for bit."""
     torch = torch_dev
-    case("packed gemm persistent items %dx%dx%d" % (m, n, k))
+    case("packed gemm multi-round %dx%dx%d" % (m, n, k))
     rng = np.random.default_rng(seed)
     ca, sa, cw, sw = operands(rng, m, n, k, 126, 129)
     O, ops = run_packed(torch, kq, ca, sa, cw, sw)
