@@ -717,8 +717,48 @@ kq_status launch_mfma(const uint16_t *A, int64_t m, int64_t d, int64_t lda, cons
     return launched();
 }
 
+// Compute units of the current device (cached per device; 256 on MI355X).
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Tiles per workgroup of the LDS-staged MFMA form. Three workgroups fit a CU (168
+// registers per lane, 42.5 KB of LDS); a workgroup's factor setup costs about two
+// tiles. Among 4 .. 12 tiles that still give every resident slot a workgroup, the
+// fewest rounds x (tiles + 2), where a last round of under 1/16 of the slots counts
+// nothing (those few workgroups run at the bandwidth of an idle chip); small inputs
+// take the most workgroups. Measured against a fixed 6 (events, interleaved):
+// 18432 x 3072 9 tiles 31.3 against 33.7 us, 18432 x 12288 12 tiles 104.2 against
+// 105.2, 4096 x 12288 8 tiles 28.8 against 30.6; 8192 x 4608 lost 10% with 4 tiles
+// (1152 workgroups) against 6 (774: one round and 6 more).
+int64_t lds_form_iters(int64_t tiles, int64_t nstrip) {
+    const int64_t slots = 3 * (int64_t)device_cus(), tol = slots / 16;
+    int64_t best = 0, best_cost = 0;
+    for (int64_t it = 4; it <= 12; ++it) {
+        const int64_t wgs = (tiles + it - 1) / it * nstrip;
+        if (wgs < slots) break;  // fewer workgroups for every larger count
+        const int64_t rounds = (wgs - tol + slots - 1) / slots;
+        const int64_t cost = (rounds < 1 ? 1 : rounds) * (it + 2);
+        if (best == 0 || cost < best_cost) {
+            best = it;
+            best_cost = cost;
+        }
+    }
+    if (best) return best;
+    const int64_t it = tiles * nstrip / slots;  // largest count that still fills the slots, if any
+    return it < 1 ? 1 : (it > 4 ? 4 : it);
+}
+
 // LDS-staged MFMA form: strips of 16 blocks (nblk % 16 == 0), `iters` tiles of
-// 16 tokens per workgroup.
+// 16 tokens per workgroup (0: chosen by lds_form_iters).
 bool make_lgeom(int64_t m, int64_t d, int64_t lda, int64_t iters_per_wg, kq::LGeom &g, unsigned &nwg) {
     g.m = m;
     g.d = d;
@@ -727,6 +767,7 @@ bool make_lgeom(int64_t m, int64_t d, int64_t lda, int64_t iters_per_wg, kq::LGe
     if (g.nblk % 16 != 0) return false;
     g.nstrip = g.nblk / 16;
     const int64_t tiles = (m + 15) / 16;
+    if (iters_per_wg == 0 && tiles > 0) iters_per_wg = lds_form_iters(tiles, g.nstrip);
     int64_t iters = iters_per_wg < 1 ? 1 : iters_per_wg;
     if (iters > tiles) iters = tiles;
     const int64_t nslab = (tiles + iters - 1) / iters;
@@ -742,7 +783,7 @@ kq_status launch_mfma_lds(const uint16_t *A, int64_t m, int64_t d, int64_t lda, 
                           uint8_t *codes, uint8_t *scales, float *ydbg, kq_stream_t stream) {
     kq::LGeom g;
     unsigned nwg;
-    if (!make_lgeom(m, d, lda, 6, g, nwg)) return KQ_ERR_SHAPE;
+    if (!make_lgeom(m, d, lda, 0, g, nwg)) return KQ_ERR_SHAPE;
     hipLaunchKernelGGL((kq::kron_mfma_lds_kernel<DEBUG>), dim3(nwg), dim3(kq::kThreads), 0,
                        (hipStream_t)stream, A, g, factors, codes, scales, ydbg);
     return launched();
