@@ -258,6 +258,31 @@ def test_f32_quantizer_at_rounding_boundaries(torch_dev, kq, orc):
 # shapes, strides, streams, guard bytes, determinism
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("m,d", [(4096, 12288), (4099, 4096), (8192, 4608), (2000, 3072)])
+def test_mfma_lds_form_tile_counts(torch_dev, kq, orc, m, d):
+    """The LDS-staged MFMA form sizes its workgroups' runs of 16-token tiles from the launch
+    (8 tiles at 4096 x 12288, 6 at 8192 x 4608, 2 at 4099 x 4096 with a last run of one
+    ragged tile, 1 at 2000 x 3072): one row of every tile (so every tile of every run) and
+    the last row against the oracle, and the fast mode writes the same bytes."""
+    torch = torch_dev
+    case("mfma_lds tile counts m=%d d=%d" % (m, d))
+    A_host = synth.random_bf16_matrix(m, d, seed=m + d, scale=3.0)
+    A_host[:, 7] = synth.to_bf16_bits(np.full(m, 250.0))
+    fac = synth.lu_perturbed_factors(d // 32, seed=d + 3)
+    A = dev_bf16(torch, A_host)
+    y = torch.empty((m, d), dtype=torch.float32, device="cuda")
+    codes, scales = kq.transform_quantize_mxfp4(A, torch.from_numpy(fac).cuda(), y_debug=y, form="mfma_lds")
+    codes_fast, scales_fast = kq.transform_quantize_mxfp4(A, torch.from_numpy(fac).cuda(), form="mfma_lds")
+    torch.cuda.synchronize()
+    assert torch.equal(codes, codes_fast) and torch.equal(scales, scales_fast)
+    rng = np.random.default_rng(m)
+    rows = np.unique(np.concatenate([np.minimum(np.arange(0, m, 16) + rng.integers(0, 16, (m + 15) // 16), m - 1),
+                                     [m - 1]]))
+    rep = parity.fused_report(orc, A_host[rows], fac, gather(torch, codes, rows), gather(torch, scales, rows),
+                              gather(torch, y, rows))
+    print("[parity] mfma_lds m=%d d=%d %s" % (m, d, rep), flush=True)
+
+
 @pytest.mark.parametrize("m,d,pad", [(1, 32, 0), (3, 96, 8), (37, 160, 0), (4133, 1152, 64),
                                      (517, 4608, 0), (70, 512, 24), (1, 12288, 0)])
 def test_ragged_shapes_and_padded_rows(torch_dev, kq, orc, m, d, pad, form):
